@@ -1,0 +1,274 @@
+"""Seeded synthetic inputs for the decode step and the residual ranking.
+
+This module draws inputs only: it holds none of the method's arithmetic (no
+key rebuild, no predictor, no softmax, no error ranking, no quantiser). Both
+the HIP path and the float64 oracle consume what it produces; neither imports
+the other. Tensors are produced with torch on the requested device (CPU for
+small cases, the GPU for full-size workloads) from generators seeded by a hash
+of (config seed, tensor name, layer, step); bf16 and int8 tensors are drawn
+in their storage dtype, so the oracle reads the same values by exact upcast.
+
+Shapes follow the workloads: Mistral-7B and Llama-3.1-8B attention shapes
+(32 query / 8 KV heads, head_dim 128, 32 layers in groups of 4), block 64.
+No dataset items are used; the pages' benchmarks (LongBench, RULER) are stood
+in for by these draws.
+"""
+import dataclasses
+import hashlib
+import math
+
+import torch
+
+__all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "make_generator",
+           "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
+           "block_ptr_from_idx"]
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    ctx_len: int
+    n_layers: int
+    rank: int
+    mlp_hidden: int
+    res_frac: tuple            # (num, den): k = floor(T*num/den)
+    sel_den: int               # 1 = every block, else n_sel = nb / sel_den
+    act: str                   # 'f32' | 'bf16'  (q, factors, weights, window, out)
+    a_dtype: str               # 'f32' | 'bf16' | 'i8'
+    res_dtype: str             # 'f32' | 'bf16' | 'i8'
+    evict_half: bool = False
+    win_cap: int = 0
+    steps: int = 1
+    group: int = 4
+    n_q_heads: int = 32
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    block: int = 64
+    seed: int = 0
+
+    @property
+    def n_res(self):
+        num, den = self.res_frac
+        return (self.ctx_len * num) // den
+
+    @property
+    def nb(self):
+        return -(-self.ctx_len // self.block)
+
+    @property
+    def n_sel(self):
+        return self.nb // self.sel_den
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+CONFIGS = {
+    "c1_tiny_f32": DecodeConfig("c1_tiny_f32", 1, 4096, 4, 256, 64, (1, 5), 1, "f32", "f32", "f32", seed=1),
+    "c2_mistral_group": DecodeConfig("c2_mistral_group", 1, 32768, 4, 512, 256, (1, 5), 4, "bf16", "bf16",
+                                     "bf16", seed=2),
+    "c3_llama_131k": DecodeConfig("c3_llama_131k", 4, 131072, 32, 1024, 256, (1, 5), 8, "bf16", "bf16",
+                                  "bf16", seed=3),
+    "c4_llama_262k": DecodeConfig("c4_llama_262k", 8, 262144, 32, 1024, 256, (1, 5), 16, "bf16", "bf16",
+                                  "bf16", win_cap=1024, steps=128, seed=4),
+    "c5_composed": DecodeConfig("c5_composed", 12, 131072, 32, 512, 256, (1, 10), 1, "bf16", "i8", "i8",
+                                evict_half=True, seed=5),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class RankConfig:
+    n_slices: int
+    ctx_len: int
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    block: int = 64
+    res_frac: tuple = (1, 10)
+    in_dtype: str = "bf16"
+    res_dtype: str = "i8"
+    seed: int = 5
+
+    @property
+    def n_res(self):
+        num, den = self.res_frac
+        return (self.ctx_len * num) // den
+
+
+RANK_C5 = RankConfig(32, 131072)
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_SIGMA = 1.0 / math.sqrt(128.0)     # N(0, 1/sqrt(d)) draws, d = 128
+
+
+def n_blocks(ctx_len, block):
+    return -(-ctx_len // block)
+
+
+def make_generator(device, *key):
+    """A torch generator on ``device`` seeded by a hash of ``key``."""
+    h = hashlib.blake2b(repr(key).encode(), digest_size=8).digest()
+    g = torch.Generator(device=device)
+    g.manual_seed(int.from_bytes(h, "little") & ((1 << 63) - 1))
+    return g
+
+
+def _normal(shape, std, dtype, device, g):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return (x * std).to(dtype)
+
+
+def _int8_rows(shape, std, device, g):
+    """int8 codes with a float32 scale per row, drawn directly (codes from a
+    rounded normal of std 40, scales around std/40)."""
+    codes = torch.randn(shape, generator=g, device=device).mul_(40.0).round_().clamp_(-127, 127)
+    scale = torch.rand(shape[:-1], generator=g, device=device).add_(0.5).mul_(std / 40.0)
+    return codes.to(torch.int8), scale.to(torch.float32)
+
+
+def gen_group_factor(cfg, group, device, batch=None):
+    """The shared key factor A of one layer group: [B, T, r] in ``cfg.a_dtype``
+    (int8 codes plus a [B, T] float32 scale for 'i8')."""
+    bsz = cfg.batch if batch is None else batch
+    g = make_generator(device, cfg.seed, "A", group)
+    shape = (bsz, cfg.ctx_len, cfg.rank)
+    if cfg.a_dtype == "i8":
+        return _int8_rows(shape, _SIGMA, device, g)
+    return _normal(shape, _SIGMA, _DT[cfg.a_dtype], device, g), None
+
+
+def _selection(cfg, bsz, layer, step, device):
+    """Per sequence: blocks {0, 1, nb-2, nb-1} plus n_sel-4 drawn uniformly
+    without replacement from [2, nb-3], ascending (int32 [B, n_sel])."""
+    nb, n_sel = cfg.nb, cfg.n_sel
+    g = make_generator("cpu", cfg.seed, "sel", layer, step)
+    rows = []
+    for _ in range(bsz):
+        mid = torch.randperm(nb - 4, generator=g)[: n_sel - 4] + 2
+        rows.append(torch.sort(torch.cat([torch.tensor([0, 1, nb - 2, nb - 1]), mid])).values)
+    return torch.stack(rows).to(torch.int32).to(device)
+
+
+def _keep_mask(cfg, bsz, layer, step, device):
+    """Per sequence: exactly nb/2 blocks evicted, drawn from [2, nb-3] (uint8
+    [B, nb], 1 = kept)."""
+    nb = cfg.nb
+    g = make_generator("cpu", cfg.seed, "keep", layer, step)
+    keep = torch.ones(bsz, nb, dtype=torch.uint8)
+    for b in range(bsz):
+        ev = torch.randperm(nb - 4, generator=g)[: nb // 2] + 2
+        keep[b, ev] = 0
+    return keep.to(device)
+
+
+def block_ptr_from_idx(idx, ctx_len, block):
+    """Block CSR of ascending residual indices [..., k] -> [..., nb+1] int32
+    (format conversion: ptr[i] = number of indices below i*block)."""
+    nb = n_blocks(ctx_len, block)
+    bounds = torch.arange(nb + 1, device=idx.device, dtype=idx.dtype) * block
+    bounds[-1] = ctx_len
+    flat = idx.reshape(-1, idx.shape[-1]).contiguous()
+    ptr = torch.searchsorted(flat, bounds.expand(flat.shape[0], nb + 1).contiguous())
+    return ptr.reshape(*idx.shape[:-1], nb + 1).to(torch.int32)
+
+
+def gen_residual_positions(cfg, bsz, layer, device):
+    """Seeded uniform k-subsets of [0, T) per (b, KV head), ascending int32."""
+    g = make_generator(device, cfg.seed, "res_idx", layer)
+    k = cfg.n_res
+    keys = torch.rand(bsz * cfg.n_kv_heads, cfg.ctx_len, generator=g, device=device)
+    idx = torch.topk(keys, k, dim=1, sorted=False).indices
+    idx = torch.sort(idx, dim=1).values.to(torch.int32)
+    return idx.reshape(bsz, cfg.n_kv_heads, k)
+
+
+def gen_layer(cfg, layer, device, *, step=0, batch=None, biases=False, res_idx=None,
+              q_scale=1.0):
+    """Everything one layer's decode call reads except the group factor.
+
+    Returns a dict of tensors: q [B,Hq,d]; bl [B,Hkv*d,r] (B_l stored
+    output-major); w_lin [B,Hkv,d,d]; w1 [B,Hkv,h,d]; w2 [B,Hkv,d,h];
+    b1 [B,Hkv,h] and b2 [B,Hkv,d] when ``biases``; res_idx [B,Hkv,k] int32
+    ascending; res_val [B,Hkv,k,d] (+ res_scale [B,Hkv,k] for 'i8');
+    res_ptr [B,Hkv,nb+1] int32; sel [B,n_sel] int32 or None; keep [B,nb]
+    uint8 or None. ``res_idx`` may be given (e.g. from a ranking run).
+    ``q_scale`` rescales the query (the peaked-attention variant).
+    """
+    bsz = cfg.batch if batch is None else batch
+    act = _DT[cfg.act]
+    d, hkv, hq, r, h = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, cfg.rank, cfg.mlp_hidden
+    g = make_generator(device, cfg.seed, "layer", layer, step)
+    out = {
+        "q": (torch.randn(bsz, hq, d, generator=g, device=device) * (_SIGMA * q_scale)).to(act),
+        "bl": _normal((bsz, hkv * d, r), _SIGMA, act, device, g),
+        "w_lin": _normal((bsz, hkv, d, d), _SIGMA, act, device, g),
+        "w1": _normal((bsz, hkv, h, d), _SIGMA, act, device, g),
+        "w2": _normal((bsz, hkv, d, h), _SIGMA, act, device, g),
+        "b1": _normal((bsz, hkv, h), 0.05, act, device, g) if biases else None,
+        "b2": _normal((bsz, hkv, d), 0.05, act, device, g) if biases else None,
+    }
+    if res_idx is None:
+        res_idx = gen_residual_positions(cfg, bsz, layer, device)
+    k = res_idx.shape[-1]
+    gr = make_generator(device, cfg.seed, "res_val", layer)
+    if cfg.res_dtype == "i8":
+        out["res_val"], out["res_scale"] = _int8_rows((bsz, hkv, k, d), 0.05, device, gr)
+    else:
+        out["res_val"] = _normal((bsz, hkv, k, d), 0.05, _DT[cfg.res_dtype], device, gr)
+        out["res_scale"] = None
+    out["res_idx"] = res_idx.to(device)
+    out["res_ptr"] = block_ptr_from_idx(out["res_idx"], cfg.ctx_len, cfg.block)
+    out["sel"] = None if cfg.sel_den == 1 else _selection(cfg, bsz, layer, step, device)
+    out["keep"] = _keep_mask(cfg, bsz, layer, step, device) if cfg.evict_half else None
+    return out
+
+
+def gen_window(cfg, layer, device, *, batch=None):
+    """Recent-window buffers [B, cap, Hkv*d] in the activation dtype. The kernel
+    takes window tokens as given exact keys and values, so they are drawn
+    i.i.d. (keys with std 0.25, the spread of the rebuilt keys under the
+    factor draws; values with std 0.1)."""
+    bsz = cfg.batch if batch is None else batch
+    act = _DT[cfg.act]
+    g = make_generator(device, cfg.seed, "win", layer)
+    shape = (bsz, cfg.win_cap, cfg.n_kv_heads * cfg.head_dim)
+    return _normal(shape, 0.25, act, device, g), _normal(shape, 0.1, act, device, g)
+
+
+def gen_rank_inputs(rc, device, *, n_slices=None, plant_ties=True):
+    """Prefill-side ranking inputs V, V_hat [Lr, T, Hkv, d] in ``rc.in_dtype``.
+
+    V_hat ~ N(0, 0.125); V = V_hat + eps * s with eps ~ N(0, 0.05) per element
+    and s ~ LogNormal(0, 1) per (token, head), so a minority of tokens carry
+    most of the error. With ``plant_ties``, per (slice, head): 1% of tokens
+    copy another token's (V, V_hat) row exactly (equal errors at random
+    places), k-2 tokens get a deviation 1e4 times larger (a top tier) and a
+    group of 6 tokens share one identical row with a deviation 1e3 times
+    larger, so that group straddles the k-th place.
+    """
+    ns = rc.n_slices if n_slices is None else n_slices
+    dt = _DT[rc.in_dtype]
+    T, hkv, d = rc.ctx_len, rc.n_kv_heads, rc.head_dim
+    g = make_generator(device, rc.seed, "rank", ns, T)
+    v_hat = (torch.randn(ns, T, hkv, d, generator=g, device=device) * 0.125).to(dt)
+    s = torch.exp(torch.randn(ns, T, hkv, 1, generator=g, device=device))
+    v = (v_hat.float() + torch.randn(ns, T, hkv, d, generator=g, device=device) * 0.05 * s).to(dt)
+    if plant_ties:
+        k = rc.n_res
+        gc = make_generator("cpu", rc.seed, "rank-ties", ns, T)
+        for sl in range(ns):
+            for h in range(hkv):
+                perm = torch.randperm(T, generator=gc)
+                n_dup = max(1, T // 100)
+                src, dst = perm[:n_dup], perm[n_dup:2 * n_dup]
+                v[sl, dst, h] = v[sl, src, h]
+                v_hat[sl, dst, h] = v_hat[sl, src, h]
+                if k >= 2:
+                    top = perm[2 * n_dup:2 * n_dup + k - 2].to(device)
+                    v[sl, top, h] = (v_hat[sl, top, h].float() + 500.0 *
+                                     torch.randn(top.numel(), d, generator=g, device=device).abs().add(0.5)).to(dt)
+                grp = perm[2 * n_dup + max(k - 2, 0):2 * n_dup + max(k - 2, 0) + 6].to(device)
+                if grp.numel():
+                    v_hat[sl, grp, h] = v_hat[sl, grp[:1], h]
+                    v[sl, grp, h] = (v_hat[sl, grp[:1], h].float() + 50.0).to(dt)
+    return v.contiguous(), v_hat.contiguous()
