@@ -1,0 +1,174 @@
+/*
+ * lowram.h -- C ABI of liblowram, the MI355X (gfx950) decode-time path of
+ * LowRAM KV-cache compression.
+ *
+ * What the cache holds (project site, Figure 1; explainer, mechanism
+ * paragraph): low-rank keys, a per-head value predictor fitted to the
+ * context, and exact residuals for the tokens the predictor gets worst.
+ * Keys are K_l = A . B_l with A shared by a group of adjacent layers and B_l
+ * per layer (project site, Figure 3; explainer, keys paragraph).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *     and contiguous in the shapes written below, 16-byte aligned. The library
+ *     never allocates, frees or synchronises; work is enqueued on `stream`
+ *     (a hipStream_t passed as void*, NULL = the null stream) and runs
+ *     asynchronously.
+ *   - Every weight matrix is stored output-major, the layout of
+ *     torch.nn.Linear.weight: [out_features, in_features].
+ *   - Host-side argument checks run before any HIP call; on failure nothing is
+ *     launched and a negative status is returned. lowram_last_error() then
+ *     holds a message (thread-local).
+ *   - Device data that the host cannot check (block lists, residual indices,
+ *     block pointers) is bounds-guarded in the kernels: out-of-range entries
+ *     are skipped, never dereferenced.
+ *   - Offsets are computed in 64-bit.
+ */
+#ifndef LOWRAM_H
+#define LOWRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LOWRAM_OK               0
+#define LOWRAM_ERR_ARG         -1  /* null pointer, bad shape, misalignment      */
+#define LOWRAM_ERR_UNSUPPORTED -2  /* dtype combination or shape not built       */
+#define LOWRAM_ERR_WORKSPACE   -3  /* workspace missing or smaller than required */
+#define LOWRAM_ERR_WINDOW_FULL -4  /* win_len > win_cap                          */
+#define LOWRAM_ERR_EMPTY       -5  /* nothing to attend (no block and no window) */
+#define LOWRAM_ERR_HIP         -6  /* a HIP launch or runtime call failed        */
+
+/* Element types. */
+#define LOWRAM_F32  0
+#define LOWRAM_BF16 1
+#define LOWRAM_I8   2   /* symmetric codes with a float32 scale per row */
+
+/* Flags for lowram_decode_args.flags. */
+#define LOWRAM_FLAG_GENERIC 1  /* use the fp32 SIMT kernel even where the MFMA kernel applies */
+
+/*
+ * One layer's decode step for a batch (explainer, prefill/decode paragraph:
+ * only the chunks the current query selects are rebuilt; paper page,
+ * Abstract: a selected subset of KV pairs per step).
+ *
+ * For each sequence b the attended compressed tokens are the 64-token blocks
+ * listed in sel[b] (every block when sel is NULL) that keep[b] marks kept
+ * (every listed block when keep is NULL); block i covers tokens
+ * [64 i, min(64 i + 64, ctx_len)). For each attended token t and KV head h:
+ *   k_t      = a_t . B_l                      (a_t = q_t * a_scale[t] for int8)
+ *   k_{t,h}  = k_t[h d : h d + d]
+ *   v_{t,h}  = k_{t,h} W_lin + gelu(k_{t,h} W1 + b1) W2 + b2
+ *              + R[slot] when t is stored among h's residuals
+ * (explainer, mechanism and Slim Attention paragraphs), plus win_len exact
+ * recent tokens (win_k, win_v) per head. Query head j attends over KV head
+ * j / (n_q_heads / n_kv_heads) with scale 1/sqrt(head_dim):
+ *   out[b, j] = softmax(q_j . K^T / sqrt(d)) . V.
+ * gelu is the exact error-function form.
+ *
+ * Shapes (B = batch, T = ctx_len, r = rank, h = mlp_hidden, d = head_dim,
+ * Hq = n_q_heads, Hkv = n_kv_heads, k = n_res, nb = ceil(T / block_size)):
+ */
+typedef struct lowram_decode_args {
+    int32_t batch, ctx_len, n_q_heads, n_kv_heads, head_dim, rank, mlp_hidden, block_size;
+    int32_t n_res;        /* residual slots per (b, KV head), 0..T                   */
+    int32_t n_sel;        /* entries per sel row (ignored when sel is NULL)          */
+    int32_t win_len;      /* exact window tokens attended, 0..win_cap               */
+    int32_t win_cap;      /* rows allocated per sequence in win_k / win_v           */
+    int32_t act_dtype;    /* F32 | BF16: q, b_l, w_*, b*, win_*, out                */
+    int32_t a_dtype;      /* F32 | BF16 | I8                                        */
+    int32_t res_dtype;    /* F32 | BF16 | I8                                        */
+    int32_t flags;        /* LOWRAM_FLAG_*                                          */
+
+    const void    *q;           /* [B, Hq, d]                                       */
+    const void    *a;           /* [B, T, r]   this layer's group factor A          */
+    const float   *a_scale;     /* [B, T]      int8 A only, else NULL               */
+    const void    *b_l;         /* [B, Hkv*d, r]  B_l output-major (= B_l^T)        */
+    const void    *w_lin;       /* [B, Hkv, d, d]                                   */
+    const void    *w1;          /* [B, Hkv, h, d]                                   */
+    const void    *b1;          /* [B, Hkv, h]  or NULL (= 0)                       */
+    const void    *w2;          /* [B, Hkv, d, h]                                   */
+    const void    *b2;          /* [B, Hkv, d]  or NULL (= 0)                       */
+    const int32_t *res_idx;     /* [B, Hkv, k] strictly ascending token indices     */
+    const void    *res_val;     /* [B, Hkv, k, d]                                   */
+    const float   *res_scale;   /* [B, Hkv, k] int8 residuals only, else NULL       */
+    const int32_t *res_blk_ptr; /* [B, Hkv, nb+1] slots of block i: [p[i], p[i+1])  */
+    const int32_t *sel;         /* [B, n_sel] ascending block indices, or NULL      */
+    const uint8_t *keep;        /* [B, nb] 1 = kept, 0 = evicted, or NULL           */
+    const void    *win_k;       /* [B, win_cap, Hkv*d] or NULL when win_len == 0    */
+    const void    *win_v;       /* [B, win_cap, Hkv*d]                              */
+
+    void          *out;         /* [B, Hq, d] output, act_dtype                     */
+    int32_t       *stats;       /* [B, Hkv, 2] or NULL: (tokens attended incl.
+                                   window, residuals applied)                       */
+    void          *workspace;   /* device scratch, >= lowram_decode_workspace_size  */
+    size_t         workspace_bytes;
+
+    void          *ev_main_begin; /* optional hipEvent_t recorded right before and  */
+    void          *ev_main_end;   /* after the fused reconstruct+attend kernel       */
+} lowram_decode_args;
+
+/* Enqueue one layer's decode step. Returns LOWRAM_OK or a negative status.
+ * A sequence with nothing to attend (its blocks all evicted and no window)
+ * gets a zero output row and zero stats; LOWRAM_ERR_EMPTY is returned only
+ * when the host can see that every sequence is empty (ctx_len == 0 or
+ * n_sel == 0, and win_len == 0). */
+int lowram_decode_step(const lowram_decode_args *args, void *stream);
+
+/* Bytes of workspace lowram_decode_step needs for these shapes; 0 when the
+ * arguments are invalid (see lowram_last_error). */
+size_t lowram_decode_workspace_size(const lowram_decode_args *args);
+
+/*
+ * Prefill-side residual ranking (paper page, Abstract: residuals for the
+ * tokens the predictor reconstructs worst; explainer, three-details
+ * paragraph: ranking by error). For each slice s and KV head h of
+ * V, V_hat [Lr, T, Hkv, d]:
+ *   e_t  = sum_i (V[s,t,h,i] - V_hat[s,t,h,i])^2, accumulated in index order
+ *          in binary64, one rounding per multiply and per add;
+ *   I    = the n_res tokens with the largest e_t, ties to the lower index,
+ *          stored in ascending order;
+ *   R    = V - V_hat at those tokens, computed exactly in binary64 and stored
+ *          as res_dtype: F32 / BF16 rounded to nearest-even in one step, or
+ *          I8 with s = float32(max|R| / 127) and q = clamp(rint(R / s), +-127);
+ *   ptr  = block CSR: ptr[i] = #{t in I : t < i * block_size}, ptr[nb] = n_res.
+ */
+typedef struct lowram_rank_args {
+    int32_t n_slices, ctx_len, n_kv_heads, head_dim, block_size, n_res;
+    int32_t in_dtype;           /* F32 | BF16                                       */
+    int32_t res_dtype;          /* F32 | BF16 | I8                                  */
+
+    const void *v;              /* [Lr, T, Hkv, d]                                  */
+    const void *v_hat;          /* [Lr, T, Hkv, d]                                  */
+
+    int32_t    *res_idx;        /* [Lr, Hkv, k]                                     */
+    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype                       */
+    float      *res_scale;      /* [Lr, Hkv, k]  I8 only, else NULL                 */
+    int32_t    *res_blk_ptr;    /* [Lr, Hkv, nb+1]                                  */
+    double     *err;            /* [Lr, Hkv, T] or NULL (then kept in workspace)    */
+
+    void       *workspace;
+    size_t      workspace_bytes;
+
+    void       *ev_main_begin;  /* optional hipEvent_t around the error kernel      */
+    void       *ev_main_end;
+} lowram_rank_args;
+
+int    lowram_rank_residuals(const lowram_rank_args *args, void *stream);
+size_t lowram_rank_workspace_size(const lowram_rank_args *args);
+
+/* Static description of a status code. */
+const char *lowram_status_string(int status);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *lowram_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWRAM_H */

@@ -1,0 +1,217 @@
+"""ctypes binding over liblowram.so (argument marshalling only).
+
+Every step of the decode and ranking paths runs in the library's HIP kernels;
+torch provides device memory and the current stream. The library must be
+built (``python -m long_context_decode_lowram_amd.build``); a missing library
+is an error, there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowram.so")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_WINDOW_FULL, ERR_EMPTY, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16, I8 = 0, 1, 2
+FLAG_GENERIC = 1
+BLOCK = 64
+
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int32
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in (
+        "batch", "ctx_len", "n_q_heads", "n_kv_heads", "head_dim", "rank", "mlp_hidden", "block_size",
+        "n_res", "n_sel", "win_len", "win_cap", "act_dtype", "a_dtype", "res_dtype", "flags")] + [
+        (n, _p) for n in (
+        "q", "a", "a_scale", "b_l", "w_lin", "w1", "b1", "w2", "b2", "res_idx", "res_val", "res_scale",
+        "res_blk_ptr", "sel", "keep", "win_k", "win_v", "out", "stats", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+
+
+class RankArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in (
+        "n_slices", "ctx_len", "n_kv_heads", "head_dim", "block_size", "n_res", "in_dtype", "res_dtype")] + [
+        (n, _p) for n in ("v", "v_hat", "res_idx", "res_val", "res_scale", "res_blk_ptr", "err", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+
+
+class LowramError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"liblowram status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m long_context_decode_lowram_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.lowram_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _p]
+        L.lowram_decode_step.restype = ctypes.c_int
+        L.lowram_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
+        L.lowram_decode_workspace_size.restype = ctypes.c_size_t
+        L.lowram_rank_residuals.argtypes = [ctypes.POINTER(RankArgs), _p]
+        L.lowram_rank_residuals.restype = ctypes.c_int
+        L.lowram_rank_workspace_size.argtypes = [ctypes.POINTER(RankArgs)]
+        L.lowram_rank_workspace_size.restype = ctypes.c_size_t
+        L.lowram_status_string.argtypes = [ctypes.c_int]
+        L.lowram_status_string.restype = ctypes.c_char_p
+        L.lowram_last_error.argtypes = []
+        L.lowram_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().lowram_status_string(status).decode()
+
+
+def last_error():
+    return lib().lowram_last_error().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblowram must be contiguous")
+    return t.data_ptr()
+
+
+def _dt(t, name):
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}") from None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_decode_args(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, out, *, a_scale=None,
+                     b1=None, b2=None, res_scale=None, sel=None, keep=None, win_k=None, win_v=None,
+                     win_len=0, stats=None, workspace=None, generic=False, events=None):
+    """Fill a DecodeArgs from tensors (shapes as documented in lowram.h).
+    ``workspace`` may be None to size it first with ``decode_workspace_size``."""
+    B, Hq, d = q.shape
+    T, r = a.shape[1], a.shape[2]
+    args = DecodeArgs()
+    args.batch, args.ctx_len, args.n_q_heads = B, T, Hq
+    args.n_kv_heads = b_l.shape[1] // d
+    args.head_dim, args.rank, args.mlp_hidden, args.block_size = d, r, w1.shape[2], BLOCK
+    args.n_res = res_idx.shape[-1]
+    args.n_sel = 0 if sel is None else sel.shape[1]
+    args.win_len = win_len
+    args.win_cap = 0 if win_k is None else win_k.shape[1]
+    args.act_dtype = _dt(q, "q")
+    args.a_dtype = _dt(a, "a")
+    args.res_dtype = _dt(res_val, "res_val")
+    args.flags = FLAG_GENERIC if generic else 0
+    for name, t in (("q", q), ("a", a), ("a_scale", a_scale), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1),
+                    ("b1", b1), ("w2", w2), ("b2", b2), ("res_idx", res_idx), ("res_val", res_val),
+                    ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("sel", sel), ("keep", keep),
+                    ("win_k", win_k), ("win_v", win_v), ("out", out), ("stats", stats), ("workspace", workspace)):
+        setattr(args, name, _ptr(t))
+    args.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if events is not None:
+        args.ev_main_begin, args.ev_main_end = events
+    return args
+
+
+def decode_workspace_size(args):
+    n = lib().lowram_decode_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def decode_launch(args, stream=None):
+    rc = lib().lowram_decode_step(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def decode_step(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, *, out=None, workspace=None,
+                stream=None, **kw):
+    """One layer's decode step; returns ``out`` [B, Hq, d]. A workspace is
+    allocated with torch when none is given."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    args = make_decode_args(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, out, **kw)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(args), dtype=torch.uint8, device=q.device)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    decode_launch(args, stream)
+    return out
+
+
+def make_rank_args(v, v_hat, n_res, res_dtype, res_idx, res_val, res_scale, res_blk_ptr, *, err=None,
+                   workspace=None, events=None):
+    Lr, T, Hkv, d = v.shape
+    args = RankArgs()
+    args.n_slices, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, T, Hkv, d
+    args.block_size, args.n_res = BLOCK, n_res
+    args.in_dtype = _dt(v, "v")
+    args.res_dtype = {"f32": F32, "bf16": BF16, "i8": I8}[res_dtype]
+    for name, t in (("v", v), ("v_hat", v_hat), ("res_idx", res_idx), ("res_val", res_val),
+                    ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("err", err),
+                    ("workspace", workspace)):
+        setattr(args, name, _ptr(t))
+    args.workspace_bytes = 0 if workspace is None else workspace.numel()
+    if events is not None:
+        args.ev_main_begin, args.ev_main_end = events
+    return args
+
+
+def rank_workspace_size(args):
+    n = lib().lowram_rank_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def rank_launch(args, stream=None):
+    rc = lib().lowram_rank_residuals(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+_RES_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+def rank_residuals(v, v_hat, n_res, res_dtype, *, want_err=False, workspace=None, stream=None):
+    """Residual store for V, V_hat [Lr, T, Hkv, d]. Returns a dict with idx,
+    val, scale (int8 only), ptr and err (when ``want_err``)."""
+    Lr, T, Hkv, d = v.shape
+    dev = v.device
+    nb = -(-T // BLOCK)
+    out = {
+        "idx": torch.empty(Lr, Hkv, n_res, dtype=torch.int32, device=dev),
+        "val": torch.empty(Lr, Hkv, n_res, d, dtype=_RES_TORCH[res_dtype], device=dev),
+        "scale": torch.empty(Lr, Hkv, n_res, dtype=torch.float32, device=dev) if res_dtype == "i8" else None,
+        "ptr": torch.empty(Lr, Hkv, nb + 1, dtype=torch.int32, device=dev),
+        "err": torch.empty(Lr, Hkv, T, dtype=torch.float64, device=dev) if want_err else None,
+    }
+    args = make_rank_args(v, v_hat, n_res, res_dtype, out["idx"], out["val"], out["scale"], out["ptr"],
+                          err=out["err"])
+    if workspace is None:
+        workspace = torch.empty(rank_workspace_size(args), dtype=torch.uint8, device=dev)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    rank_launch(args, stream)
+    return out

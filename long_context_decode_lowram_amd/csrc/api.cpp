@@ -1,0 +1,238 @@
+// liblowram C ABI: argument checks, workspace carving and launch sequence.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "lowram.h"
+
+using namespace lowram;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct DecodePlan {
+    bool mfma;
+    int nb, n_cand, n_split, bps, part_stride;
+    size_t off_list, off_count, off_part, off_counts, total;
+};
+
+int plan_decode(const lowram_decode_args* a, DecodePlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->batch < 1 || a->ctx_len < 0 || a->n_q_heads < 1 || a->n_kv_heads < 1)
+        return fail(LOWRAM_ERR_ARG, "batch/heads must be >= 1 and ctx_len >= 0");
+    if (a->n_q_heads % a->n_kv_heads != 0)
+        return fail(LOWRAM_ERR_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", a->n_q_heads, a->n_kv_heads);
+    if (a->head_dim != kHeadDim) return fail(LOWRAM_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->block_size != kBlock) return fail(LOWRAM_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
+    if (a->rank < 32 || a->rank % 32 != 0) return fail(LOWRAM_ERR_UNSUPPORTED, "rank must be a positive multiple of 32 (got %d)", a->rank);
+    if (a->mlp_hidden < 16 || a->mlp_hidden % 16 != 0 || a->mlp_hidden > 1024)
+        return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 16 in [16, 1024] (got %d)", a->mlp_hidden);
+    if (a->act_dtype != LOWRAM_F32 && a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_ARG, "act_dtype must be F32 or BF16");
+    if (a->a_dtype < LOWRAM_F32 || a->a_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad a_dtype");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
+    if (a->win_len < 0 || a->win_cap < 0) return fail(LOWRAM_ERR_ARG, "win_len and win_cap must be >= 0");
+    if (a->win_len > a->win_cap) return fail(LOWRAM_ERR_WINDOW_FULL, "win_len (%d) > win_cap (%d)", a->win_len, a->win_cap);
+    if (a->win_len > 4096) return fail(LOWRAM_ERR_UNSUPPORTED, "win_len above 4096");
+    const int g = a->n_q_heads / a->n_kv_heads;
+    pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
+    if (a->sel != nullptr && (a->n_sel < 0 || a->n_sel > pl->nb))
+        return fail(LOWRAM_ERR_ARG, "n_sel (%d) must be in [0, nb=%d]", a->n_sel, pl->nb);
+    pl->n_cand = a->sel ? a->n_sel : pl->nb;
+    if (pl->n_cand == 0 && a->win_len == 0) return fail(LOWRAM_ERR_EMPTY, "no block and no window token to attend");
+
+    DecodeParams probe{};
+    probe.group = g; probe.hidden = a->mlp_hidden; probe.rank = a->rank;
+    pl->mfma = !(a->flags & LOWRAM_FLAG_GENERIC) && mfma_supported(probe, a->act_dtype, a->a_dtype, a->res_dtype);
+    if (!pl->mfma && g > 8) return fail(LOWRAM_ERR_UNSUPPORTED, "GQA group above 8 needs the MFMA kernel");
+    pl->bps = pl->mfma ? mfma_blocks_per_split() : 1;
+    pl->n_split = (pl->n_cand + pl->bps - 1) / pl->bps;
+    if (pl->n_split < 1) pl->n_split = 1;
+    pl->part_stride = (2 + a->mlp_hidden + kHeadDim + 3) & ~3;
+    const size_t smem = sizeof(float) * ((size_t)pl->n_split + a->win_len + a->mlp_hidden + 2 * kHeadDim + 8);
+    if (smem > 65536) return fail(LOWRAM_ERR_UNSUPPORTED, "too many splits plus window tokens for the combine");
+
+    const size_t B = a->batch;
+    pl->off_list = 0;
+    pl->off_count = up256(pl->off_list + B * pl->nb * sizeof(int32_t));
+    pl->off_part = up256(pl->off_count + B * sizeof(int32_t));
+    pl->off_counts = up256(pl->off_part + B * a->n_q_heads * (size_t)pl->n_split * pl->part_stride * sizeof(float));
+    pl->total = up256(pl->off_counts + B * a->n_kv_heads * (size_t)pl->n_split * 2 * sizeof(int32_t));
+    return LOWRAM_OK;
+}
+
+int check_decode_ptrs(const lowram_decode_args* a, const DecodePlan& pl) {
+    if (!a->q || !a->a || !a->b_l || !a->w_lin || !a->w1 || !a->w2 || !a->out || !a->res_blk_ptr)
+        return fail(LOWRAM_ERR_ARG, "q, a, b_l, w_lin, w1, w2, res_blk_ptr and out must be non-NULL");
+    if (a->n_res > 0 && (!a->res_idx || !a->res_val)) return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
+    if (a->a_dtype == LOWRAM_I8 && !a->a_scale) return fail(LOWRAM_ERR_ARG, "int8 A needs a_scale");
+    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale) return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    if (a->win_len > 0 && (!a->win_k || !a->win_v)) return fail(LOWRAM_ERR_ARG, "win_k and win_v must be non-NULL when win_len > 0");
+    const void* v16[] = {a->q, a->a, a->b_l, a->w_lin, a->w1, a->w2, a->res_val, a->win_k, a->win_v, a->out, a->workspace};
+    for (const void* p : v16)
+        if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
+    const void* v4[] = {a->a_scale, a->b1, a->b2, a->res_idx, a->res_scale, a->res_blk_ptr, a->sel, a->stats};
+    for (const void* p : v4)
+        if (misaligned(p, 4)) return fail(LOWRAM_ERR_ARG, "pointer %p is not 4-byte aligned", p);
+    if (pl.total > 0 && (!a->workspace || a->workspace_bytes < pl.total))
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+    return LOWRAM_OK;
+}
+
+struct RankPlan { size_t off_err, off_thr, off_neq, total; int nb; };
+
+int plan_rank(const lowram_rank_args* a, RankPlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_slices < 1 || a->ctx_len < 1 || a->n_kv_heads < 1)
+        return fail(LOWRAM_ERR_ARG, "n_slices, ctx_len and n_kv_heads must be >= 1");
+    if (a->head_dim != kHeadDim) return fail(LOWRAM_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->block_size != kBlock) return fail(LOWRAM_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
+    if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
+    if (a->in_dtype != LOWRAM_F32 && a->in_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_ARG, "in_dtype must be F32 or BF16");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
+    const size_t nseg = (size_t)a->n_slices * a->n_kv_heads;
+    pl->off_err = 0;
+    const size_t err_bytes = a->err ? 0 : nseg * a->ctx_len * sizeof(double);
+    pl->off_thr = up256(err_bytes);
+    pl->off_neq = up256(pl->off_thr + nseg * sizeof(unsigned long long));
+    pl->total = up256(pl->off_neq + nseg * sizeof(int32_t));
+    return LOWRAM_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(LOWRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lowram_status_string(int s) {
+    switch (s) {
+        case LOWRAM_OK: return "ok";
+        case LOWRAM_ERR_ARG: return "invalid argument";
+        case LOWRAM_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+        case LOWRAM_ERR_WORKSPACE: return "workspace missing or too small";
+        case LOWRAM_ERR_WINDOW_FULL: return "window length exceeds its capacity";
+        case LOWRAM_ERR_EMPTY: return "nothing to attend";
+        case LOWRAM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* lowram_last_error(void) { return g_err; }
+
+size_t lowram_decode_workspace_size(const lowram_decode_args* a) {
+    DecodePlan pl;
+    return plan_decode(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_decode_step(const lowram_decode_args* a, void* stream) {
+    g_err[0] = 0;
+    DecodePlan pl;
+    int rc = plan_decode(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    rc = check_decode_ptrs(a, pl);
+    if (rc != LOWRAM_OK) return rc;
+
+    DecodeParams p{};
+    p.batch = a->batch; p.ctx_len = a->ctx_len; p.n_q = a->n_q_heads; p.n_kv = a->n_kv_heads;
+    p.group = a->n_q_heads / a->n_kv_heads; p.rank = a->rank; p.hidden = a->mlp_hidden; p.n_res = a->n_res;
+    p.n_blocks = pl.nb; p.win_len = a->win_len; p.win_cap = a->win_cap; p.part_stride = pl.part_stride;
+    p.n_split = pl.n_split; p.blocks_per_split = pl.bps; p.scale = 0.08838834764831845f;  // 1/sqrt(128)
+    p.q = a->q; p.a = a->a; p.a_scale = a->a_scale; p.b_l = a->b_l; p.w_lin = a->w_lin; p.w1 = a->w1;
+    p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.res_idx = a->res_idx; p.res_val = a->res_val;
+    p.res_scale = a->res_scale; p.res_ptr = a->res_blk_ptr; p.sel = a->sel; p.keep = a->keep;
+    p.win_k = a->win_k; p.win_v = a->win_v; p.out = a->out; p.stats = a->stats; p.n_sel = a->n_sel;
+    char* ws = static_cast<char*>(a->workspace);
+    p.att_list = reinterpret_cast<int32_t*>(ws + pl.off_list);
+    p.att_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
+    p.partials = reinterpret_cast<float*>(ws + pl.off_part);
+    p.counts = reinterpret_cast<int32_t*>(ws + pl.off_counts);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_assemble(p, s);
+    if (e != hipSuccess) return hip_fail(e, "assemble launch");
+    if (a->ev_main_begin) {
+        e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_begin), s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+    e = pl.mfma ? launch_decode_mfma(p, a->a_dtype, a->res_dtype, s)
+                : launch_decode_generic(p, a->act_dtype, a->a_dtype, a->res_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    if (a->ev_main_end) {
+        e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_end), s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+    }
+    e = launch_combine(p, a->act_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return LOWRAM_OK;
+}
+
+size_t lowram_rank_workspace_size(const lowram_rank_args* a) {
+    RankPlan pl;
+    return plan_rank(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_rank_residuals(const lowram_rank_args* a, void* stream) {
+    g_err[0] = 0;
+    RankPlan pl;
+    int rc = plan_rank(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (!a->v || !a->v_hat || !a->res_idx || !a->res_blk_ptr)
+        return fail(LOWRAM_ERR_ARG, "v, v_hat, res_idx and res_blk_ptr must be non-NULL");
+    if (a->n_res > 0 && !a->res_val) return fail(LOWRAM_ERR_ARG, "res_val must be non-NULL when n_res > 0");
+    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale)
+        return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    const void* v16[] = {a->v, a->v_hat, a->res_val, a->workspace};
+    for (const void* p : v16)
+        if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
+    const void* v8[] = {a->err};
+    for (const void* p : v8)
+        if (misaligned(p, 8)) return fail(LOWRAM_ERR_ARG, "err pointer %p is not 8-byte aligned", p);
+    if (misaligned(a->res_idx, 4) || misaligned(a->res_blk_ptr, 4) || misaligned(a->res_scale, 4))
+        return fail(LOWRAM_ERR_ARG, "index/scale pointers must be 4-byte aligned");
+    if (!a->workspace || a->workspace_bytes < pl.total)
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+
+    char* ws = static_cast<char*>(a->workspace);
+    RankParams p{};
+    p.n_slices = a->n_slices; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads; p.n_res = a->n_res;
+    p.n_blocks = pl.nb; p.in_dtype = a->in_dtype; p.res_dtype = a->res_dtype;
+    p.v = a->v; p.v_hat = a->v_hat; p.res_idx = a->res_idx; p.res_val = a->res_val;
+    p.res_scale = a->res_scale; p.res_ptr = a->res_blk_ptr;
+    p.err = a->err ? a->err : reinterpret_cast<double*>(ws + pl.off_err);
+    p.thr = reinterpret_cast<unsigned long long*>(ws + pl.off_thr);
+    p.n_eq = reinterpret_cast<int32_t*>(ws + pl.off_neq);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a->ev_main_begin && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_begin), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    if ((e = launch_rank_error(p, s)) != hipSuccess) return hip_fail(e, "rank error launch");
+    if (a->ev_main_end && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_end), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    if ((e = launch_rank_select(p, s)) != hipSuccess) return hip_fail(e, "rank select launch");
+    if ((e = launch_rank_compact(p, s)) != hipSuccess) return hip_fail(e, "rank compact launch");
+    if ((e = launch_rank_gather(p, s)) != hipSuccess) return hip_fail(e, "rank gather launch");
+    return LOWRAM_OK;
+}
+
+}  // extern "C"

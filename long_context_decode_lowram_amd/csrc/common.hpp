@@ -1,0 +1,80 @@
+// Shared device helpers for the liblowram kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowram {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2 };
+
+constexpr int kHeadDim = 128;   // head_dim the kernels are built for
+constexpr int kBlock = 64;      // tokens per cache block
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Element load of a stored tensor as float (int8 returns the raw code).
+template <int DT> __device__ __forceinline__ float ld(const void* p, int64_t i);
+template <> __device__ __forceinline__ float ld<DT_F32>(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float ld<DT_BF16>(const void* p, int64_t i) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <> __device__ __forceinline__ float ld<DT_I8>(const void* p, int64_t i) {
+    return static_cast<float>(static_cast<const int8_t*>(p)[i]);
+}
+
+template <int DT> __device__ __forceinline__ void st(void* p, int64_t i, float v);
+template <> __device__ __forceinline__ void st<DT_F32>(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+}
+template <> __device__ __forceinline__ void st<DT_BF16>(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+}
+
+__device__ __forceinline__ float gelu_erf(float x) {
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Per-call constants shared by the decode kernels (passed by value).
+struct DecodeParams {
+    int batch, ctx_len, n_q, n_kv, group, rank, hidden, n_res, n_blocks, win_len, win_cap;
+    int part_stride;       // floats per partial record: 2 + hidden + head_dim, rounded up
+    int n_split;           // partial records per (b, query head)
+    int blocks_per_split;  // attended blocks folded into one partial record
+    float scale;           // 1/sqrt(head_dim)
+    const void* q; const void* a; const float* a_scale; const void* b_l;
+    const void* w_lin; const void* w1; const void* b1; const void* w2; const void* b2;
+    const int32_t* res_idx; const void* res_val; const float* res_scale; const int32_t* res_ptr;
+    const int32_t* sel; const uint8_t* keep; const void* win_k; const void* win_v;
+    void* out; int32_t* stats;
+    // workspace
+    int32_t* att_list;     // [B, n_blocks]
+    int32_t* att_count;    // [B]
+    float* partials;       // [B, Hq, n_split, part_stride]
+    int32_t* counts;       // [B, Hkv, n_split, 2]
+    int n_sel;
+};
+
+}  // namespace lowram

@@ -1,0 +1,39 @@
+// Host-side launchers of the liblowram kernels (one translation unit each).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace lowram {
+
+// Attended-set assembly: att_list/att_count from sel and keep. Grid (B).
+hipError_t launch_assemble(const DecodeParams& p, hipStream_t s);
+
+// Generic fp32 SIMT kernel: one workgroup per (attended block, KV head, b).
+hipError_t launch_decode_generic(const DecodeParams& p, int act, int adt, int rdt, hipStream_t s);
+
+// bf16 MFMA kernel. Returns hipErrorInvalidValue for unsupported combinations.
+bool mfma_supported(const DecodeParams& p, int act, int adt, int rdt);
+int mfma_blocks_per_split();
+hipError_t launch_decode_mfma(const DecodeParams& p, int adt, int rdt, hipStream_t s);
+
+// Split-K combine, window tokens, deferred W2 / b2, stats. Grid (Hq, B).
+size_t combine_smem_bytes(const DecodeParams& p);
+hipError_t launch_combine(const DecodeParams& p, int act, hipStream_t s);
+
+// Residual ranking.
+struct RankParams {
+    int n_slices, ctx_len, n_kv, n_res, n_blocks, in_dtype, res_dtype;
+    const void* v; const void* v_hat;
+    int32_t* res_idx; void* res_val; float* res_scale; int32_t* res_ptr;
+    double* err;                 // [Lr, Hkv, T]
+    unsigned long long* thr;     // [Lr*Hkv] threshold key
+    int32_t* n_eq;               // [Lr*Hkv] ties at the threshold to take
+};
+hipError_t launch_rank_error(const RankParams& p, hipStream_t s);
+hipError_t launch_rank_select(const RankParams& p, hipStream_t s);
+hipError_t launch_rank_compact(const RankParams& p, hipStream_t s);
+hipError_t launch_rank_gather(const RankParams& p, hipStream_t s);
+
+}  // namespace lowram

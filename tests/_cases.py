@@ -1,0 +1,85 @@
+"""Helpers shared by the GPU parity tests: build a seeded case, run it through
+the C ABI and through the float64 oracle, and compare."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def np64(t):
+    if t is None:
+        return None
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def make_case(cfg, layer=0, *, device="cpu", biases=True, q_scale=1.0, win_len=0, batch=None):
+    bsz = cfg.batch if batch is None else batch
+    a, a_scale = synth.gen_group_factor(cfg, layer // cfg.group, device, batch=bsz)
+    case = synth.gen_layer(cfg, layer, device, biases=biases, q_scale=q_scale, batch=bsz)
+    case.update(a=a, a_scale=a_scale, win_len=win_len, win_k=None, win_v=None)
+    if cfg.win_cap:
+        case["win_k"], case["win_v"] = synth.gen_window(cfg, layer, device, batch=bsz)
+    return case
+
+
+def set_residuals(case, cfg, idx):
+    """Replace the residual set with explicit ascending indices [B, Hkv, k]."""
+    bsz, hkv = idx.shape[:2]
+    k = idx.shape[-1]
+    g = synth.make_generator("cpu", cfg.seed, "set_res", k)
+    dev = case["q"].device
+    case["res_idx"] = idx.to(torch.int32).to(dev).contiguous()
+    if cfg.res_dtype == "i8":
+        case["res_val"] = torch.randint(-127, 128, (bsz, hkv, k, 128), generator=g).to(torch.int8).to(dev)
+        case["res_scale"] = (torch.rand(bsz, hkv, k, generator=g) * 1e-3 + 1e-4).to(dev)
+    else:
+        dt = torch.float32 if cfg.res_dtype == "f32" else torch.bfloat16
+        case["res_val"] = (torch.randn(bsz, hkv, k, 128, generator=g) * 0.05).to(dt).to(dev)
+        case["res_scale"] = None
+    case["res_ptr"] = synth.block_ptr_from_idx(case["res_idx"], cfg.ctx_len, cfg.block)
+    return case
+
+
+def to(case, device):
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in case.items()}
+
+
+def gpu_decode(case, *, generic=False, with_stats=True, out=None):
+    import long_context_decode_lowram_amd as L
+    c = to(case, "cuda")
+    q = c["q"]
+    stats = torch.full((q.shape[0], c["bl"].shape[1] // 128, 2), -7, dtype=torch.int32, device="cuda") \
+        if with_stats else None
+    out = L.decode_step(c["q"], c["a"], c["bl"], c["w_lin"], c["w1"], c["w2"], c["res_idx"], c["res_val"],
+                        c["res_ptr"], out=out, a_scale=c["a_scale"], b1=c["b1"], b2=c["b2"],
+                        res_scale=c["res_scale"], sel=c["sel"], keep=c["keep"], win_k=c["win_k"],
+                        win_v=c["win_v"], win_len=c["win_len"], stats=stats, generic=generic)
+    torch.cuda.synchronize()
+    return out, stats
+
+
+def oracle_decode(case, batch_index=None):
+    names = ["q", "a", "a_scale", "bl", "w_lin", "w1", "b1", "w2", "b2", "res_idx", "res_val", "res_scale",
+             "sel", "keep", "win_k", "win_v"]
+    sl = slice(None) if batch_index is None else slice(batch_index, batch_index + 1)
+    batch = {n: (None if case.get(n) is None else np64(case[n][sl])) for n in names}
+    batch["block"] = 64
+    batch["win_len"] = case["win_len"]
+    return oracle.decode_step(batch)
+
+
+def rel_err(got, ref):
+    """Max over rows of ||got - ref||_2 / ||ref||_2 (rows with a zero
+    reference must match exactly)."""
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    zero = den == 0
+    assert np.all(num[zero] == 0), "rows with a zero reference must be zero"
+    return float(np.max(num[~zero] / den[~zero])) if (~zero).any() else 0.0

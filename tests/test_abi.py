@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects bad arguments with the
+documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decode_lowram_amd as L
+from long_context_decode_lowram_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lowram.h")
+FAKE = 0x100000          # a 16-byte aligned non-NULL address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(lowram_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"lowram_decode_step", "lowram_decode_workspace_size", "lowram_rank_residuals",
+            "lowram_rank_workspace_size", "lowram_status_string", "lowram_last_error"} <= set(names)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_struct_layout_matches_binding():
+    # Field order and count of the ctypes mirrors against the header text.
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct lowram_decode_args"):text.index("} lowram_decode_args;")]
+    fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f[0] for f in B.DecodeArgs._fields_]
+    body = text[text.index("typedef struct lowram_rank_args"):text.index("} lowram_rank_args;")]
+    fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f[0] for f in B.RankArgs._fields_]
+
+
+def test_status_strings():
+    codes = [0, -1, -2, -3, -4, -5, -6]
+    strs = [L.status_string(c) for c in codes]
+    assert len(set(strs)) == len(codes)
+    assert L.status_string(-99) == "unknown status"
+
+
+def valid_decode():
+    a = B.DecodeArgs()
+    a.batch, a.ctx_len, a.n_q_heads, a.n_kv_heads, a.head_dim = 2, 1000, 32, 8, 128
+    a.rank, a.mlp_hidden, a.block_size, a.n_res, a.n_sel, a.win_len, a.win_cap = 256, 64, 64, 200, 4, 3, 16
+    a.act_dtype, a.a_dtype, a.res_dtype = B.BF16, B.BF16, B.BF16
+    for n in ("q", "a", "b_l", "w_lin", "w1", "w2", "res_idx", "res_val", "res_blk_ptr", "sel",
+              "win_k", "win_v", "out"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def call_decode(a):
+    return L.lib().lowram_decode_step(ctypes.byref(a), None)
+
+
+def test_decode_valid_args_stop_at_workspace():
+    a = valid_decode()
+    assert B.decode_workspace_size(a) > 0
+    assert call_decode(a) == B.ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE, B.decode_workspace_size(a) - 1
+    assert call_decode(a) == B.ERR_WORKSPACE
+    assert "workspace" in L.last_error()
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q", None, B.ERR_ARG),
+    ("out", None, B.ERR_ARG),
+    ("res_blk_ptr", None, B.ERR_ARG),
+    ("win_k", None, B.ERR_ARG),
+    ("q", FAKE + 4, B.ERR_ARG),                 # misaligned
+    ("head_dim", 64, B.ERR_UNSUPPORTED),
+    ("block_size", 32, B.ERR_UNSUPPORTED),
+    ("rank", 250, B.ERR_UNSUPPORTED),
+    ("mlp_hidden", 40, B.ERR_UNSUPPORTED),
+    ("n_q_heads", 30, B.ERR_ARG),
+    ("n_res", 1001, B.ERR_ARG),
+    ("n_res", -1, B.ERR_ARG),
+    ("n_sel", 17, B.ERR_ARG),                   # nb = 16
+    ("win_len", 17, B.ERR_WINDOW_FULL),
+    ("act_dtype", B.I8, B.ERR_ARG),
+    ("a_dtype", 7, B.ERR_ARG),
+    ("res_dtype", -1, B.ERR_ARG),
+    ("batch", 0, B.ERR_ARG),
+    ("a_dtype", B.I8, B.ERR_ARG),               # int8 A without a_scale
+    ("res_dtype", B.I8, B.ERR_ARG),             # int8 residuals without res_scale
+])
+def test_decode_rejects(field, value, status):
+    a = valid_decode()
+    setattr(a, field, value)
+    assert call_decode(a) == status
+    assert L.last_error() != ""
+
+
+def test_decode_empty_and_window_only():
+    a = valid_decode()
+    a.n_sel, a.win_len = 0, 0
+    assert call_decode(a) == B.ERR_EMPTY
+    a.win_len = 2                                # window only: valid, stops at workspace
+    assert call_decode(a) == B.ERR_WORKSPACE
+    a = valid_decode()
+    a.ctx_len, a.n_res, a.win_len, a.sel = 0, 0, 0, None
+    assert call_decode(a) == B.ERR_EMPTY
+
+
+def test_decode_workspace_grows_with_batch_and_is_zero_when_invalid():
+    a = valid_decode()
+    n2 = B.decode_workspace_size(a)
+    a.batch = 4
+    assert B.decode_workspace_size(a) > n2
+    a.head_dim = 64
+    assert L.lib().lowram_decode_workspace_size(ctypes.byref(a)) == 0
+
+
+def valid_rank():
+    a = B.RankArgs()
+    a.n_slices, a.ctx_len, a.n_kv_heads, a.head_dim, a.block_size, a.n_res = 2, 1000, 8, 128, 64, 100
+    a.in_dtype, a.res_dtype = B.BF16, B.BF16
+    for n in ("v", "v_hat", "res_idx", "res_val", "res_blk_ptr"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def call_rank(a):
+    return L.lib().lowram_rank_residuals(ctypes.byref(a), None)
+
+
+def test_rank_valid_args_stop_at_workspace():
+    a = valid_rank()
+    n = B.rank_workspace_size(a)
+    assert n >= 2 * 8 * 1000 * 8            # errors kept in the workspace
+    assert call_rank(a) == B.ERR_WORKSPACE
+    a.err = FAKE
+    assert B.rank_workspace_size(a) < n      # caller-provided err buffer
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("v", None, B.ERR_ARG), ("res_idx", None, B.ERR_ARG), ("res_val", None, B.ERR_ARG),
+    ("head_dim", 96, B.ERR_UNSUPPORTED), ("block_size", 128, B.ERR_UNSUPPORTED),
+    ("n_res", 1001, B.ERR_ARG), ("in_dtype", B.I8, B.ERR_ARG), ("res_dtype", B.I8, B.ERR_ARG),
+    ("n_slices", 0, B.ERR_ARG), ("v_hat", FAKE + 2, B.ERR_ARG),
+])
+def test_rank_rejects(field, value, status):
+    a = valid_rank()
+    setattr(a, field, value)
+    assert call_rank(a) == status

@@ -1,0 +1,114 @@
+"""GPU parity of lowram_decode_step against the float64 oracle, on seeded
+inputs at sizes the oracle finishes in seconds (several blocks and a ragged
+tail), with exact stats. Tolerances: relative output error per row 1e-4 for
+fp32 activations, 2e-2 for bf16."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _cases import TOL, gpu_decode, make_case, oracle_decode, rel_err, set_residuals
+
+pytestmark = pytest.mark.gpu
+
+C1 = synth.CONFIGS["c1_tiny_f32"]
+C2 = synth.CONFIGS["c2_mistral_group"]
+C4 = synth.CONFIGS["c4_llama_262k"]
+C5 = synth.CONFIGS["c5_composed"]
+
+SMALL = {
+    "f32_ragged": C1.replace(ctx_len=4096 + 37, batch=2),
+    "bf16_sel": C2.replace(ctx_len=64 * 40 + 9, batch=2),
+    "bf16_r1024_sel": C4.replace(ctx_len=64 * 96 + 50, batch=2, win_cap=64),
+    "i8_keep": C5.replace(ctx_len=64 * 48 + 5, batch=3),
+    "f32_a_bf16_res": C1.replace(ctx_len=1000, res_dtype="bf16", a_dtype="bf16"),
+}
+
+
+def check(case, cfg, *, generic, tol=None):
+    out, stats = gpu_decode(case, generic=generic)
+    ref, rstats = oracle_decode(case)
+    err = rel_err(out.float().cpu().numpy(), ref)
+    print(f"rel_err={err:.3e}", flush=True)
+    assert err <= (tol or TOL[cfg.act]), err
+    np.testing.assert_array_equal(stats.cpu().numpy(), rstats)
+    return out, stats
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs(name, generic):
+    cfg = SMALL[name]
+    case = make_case(cfg, layer=1, biases=True, win_len=40 if cfg.win_cap else 0)
+    check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_peaked_attention(generic):
+    """Query rescaled so logits have a spread of about 4: a score-path bug
+    cannot hide behind a near-uniform softmax."""
+    cfg = SMALL["bf16_sel"]
+    case = make_case(cfg, layer=2, q_scale=180.0)
+    check(case, cfg, generic=generic)
+    cfg = SMALL["f32_ragged"]
+    case = make_case(cfg, layer=2, q_scale=180.0)
+    check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_no_residuals_and_every_token_a_residual(generic):
+    for cfg in (SMALL["f32_ragged"], SMALL["bf16_sel"], SMALL["i8_keep"]):
+        case = make_case(cfg, layer=0)
+        bsz = case["q"].shape[0]
+        set_residuals(case, cfg, torch.zeros(bsz, 8, 0, dtype=torch.int32))
+        check(case, cfg, generic=generic)
+        set_residuals(case, cfg, torch.arange(cfg.ctx_len, dtype=torch.int32).expand(bsz, 8, -1))
+        check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_single_block_all_blocks_last_partial_block(generic):
+    cfg = SMALL["bf16_sel"]
+    nb = cfg.nb
+    case = make_case(cfg, layer=3)
+    for sel in ([[nb - 1], [0]], [[5], [nb - 1]], [list(range(nb))] * 2):
+        case["sel"] = torch.tensor(sel, dtype=torch.int32)
+        check(case, cfg, generic=generic)
+    case["sel"] = None
+    check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_window_lengths(generic):
+    cfg = SMALL["bf16_r1024_sel"]
+    case = make_case(cfg, layer=4)
+    for w in (0, 1, 63, 64):
+        case["win_len"] = w
+        check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_sequence_with_everything_evicted(generic):
+    cfg = SMALL["i8_keep"]
+    case = make_case(cfg, layer=5)
+    case["keep"][1] = 0
+    out, stats = check(case, cfg, generic=generic)
+    assert not out[1].float().abs().sum().item()
+    assert stats[1].abs().sum().item() == 0
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_bitwise_rerun(generic):
+    cfg = SMALL["bf16_sel"]
+    case = make_case(cfg, layer=6)
+    o1, s1 = gpu_decode(case, generic=generic)
+    o2, s2 = gpu_decode(case, generic=generic)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_c1_full_config_four_layers():
+    """The tiny fp32 workload as configured: batch 1, T=4096, one group of 4
+    layers, r=256, h=64, every block, k=819."""
+    for layer in range(C1.n_layers):
+        case = make_case(C1, layer=layer, biases=False)
+        check(case, C1, generic=False)
