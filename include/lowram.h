@@ -93,8 +93,8 @@ typedef struct lowram_decode_args {
     const void    *b1;          /* [B, Hkv, h]  or NULL (= 0)                       */
     const void    *w2;          /* [B, Hkv, d, h]                                   */
     const void    *b2;          /* [B, Hkv, d]  or NULL (= 0)                       */
-    const int32_t *res_idx;     /* [B, Hkv, k] strictly ascending token indices     */
-    const void    *res_val;     /* [B, Hkv, k, d]                                   */
+    const int32_t *res_idx;     /* [B, Hkv, k] strictly ascending (NULL if k == 0) */
+    const void    *res_val;     /* [B, Hkv, k, d]                  (NULL if k == 0) */
     const float   *res_scale;   /* [B, Hkv, k] int8 residuals only, else NULL       */
     const int32_t *res_blk_ptr; /* [B, Hkv, nb+1] slots of block i: [p[i], p[i+1])  */
     const int32_t *sel;         /* [B, n_sel] ascending block indices, or NULL      */
@@ -145,8 +145,8 @@ typedef struct lowram_rank_args {
     const void *v;              /* [Lr, T, Hkv, d]                                  */
     const void *v_hat;          /* [Lr, T, Hkv, d]                                  */
 
-    int32_t    *res_idx;        /* [Lr, Hkv, k]                                     */
-    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype                       */
+    int32_t    *res_idx;        /* [Lr, Hkv, k]      (may be NULL when k == 0)      */
+    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype (NULL when k == 0)    */
     float      *res_scale;      /* [Lr, Hkv, k]  I8 only, else NULL                 */
     int32_t    *res_blk_ptr;    /* [Lr, Hkv, nb+1]                                  */
     double     *err;            /* [Lr, Hkv, T] or NULL (then kept in workspace)    */

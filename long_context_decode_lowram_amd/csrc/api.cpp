@@ -196,9 +196,10 @@ int lowram_rank_residuals(const lowram_rank_args* a, void* stream) {
     RankPlan pl;
     int rc = plan_rank(a, &pl);
     if (rc != LOWRAM_OK) return rc;
-    if (!a->v || !a->v_hat || !a->res_idx || !a->res_blk_ptr)
-        return fail(LOWRAM_ERR_ARG, "v, v_hat, res_idx and res_blk_ptr must be non-NULL");
-    if (a->n_res > 0 && !a->res_val) return fail(LOWRAM_ERR_ARG, "res_val must be non-NULL when n_res > 0");
+    if (!a->v || !a->v_hat || !a->res_blk_ptr)
+        return fail(LOWRAM_ERR_ARG, "v, v_hat and res_blk_ptr must be non-NULL");
+    if (a->n_res > 0 && (!a->res_idx || !a->res_val))
+        return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
     if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale)
         return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
     const void* v16[] = {a->v, a->v_hat, a->res_val, a->workspace};

@@ -167,8 +167,9 @@ def block_ptr_from_idx(idx, ctx_len, block):
     nb = n_blocks(ctx_len, block)
     bounds = torch.arange(nb + 1, device=idx.device, dtype=idx.dtype) * block
     bounds[-1] = ctx_len
-    flat = idx.reshape(-1, idx.shape[-1]).contiguous()
-    ptr = torch.searchsorted(flat, bounds.expand(flat.shape[0], nb + 1).contiguous())
+    rows = math.prod(idx.shape[:-1])
+    flat = idx.reshape(rows, idx.shape[-1]).contiguous()
+    ptr = torch.searchsorted(flat, bounds.expand(rows, nb + 1).contiguous())
     return ptr.reshape(*idx.shape[:-1], nb + 1).to(torch.int32)
 
 
@@ -261,6 +262,7 @@ def gen_rank_inputs(rc, device, *, n_slices=None, plant_ties=True):
                 perm = torch.randperm(T, generator=gc)
                 n_dup = max(1, T // 100)
                 src, dst = perm[:n_dup], perm[n_dup:2 * n_dup]
+                src, dst = src.to(device), dst.to(device)
                 v[sl, dst, h] = v[sl, src, h]
                 v_hat[sl, dst, h] = v_hat[sl, src, h]
                 if k >= 2:
