@@ -1,0 +1,323 @@
+"""Decode-step benchmark: reconstructed-KV attention over the compressed cache.
+
+One step = one decode token for every sequence in the batch: the layer
+loop of lowram_decode_step calls over all layers of the workload (each call
+rebuilds the selected blocks' keys, predicts values, adds residuals and runs
+GQA attention), inputs resident in HBM. Prints one JSON line with the
+cached-tokens/s metric, the fused kernel's roofline and the float64 oracle's
+rate on a bounded sample of the same workload.
+
+python bench.py [--steps K] [--warmup W] [--workload c3_llama_131k] [--batch B]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c3_llama_131k")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--generic", action="store_true", help="force the fp32 SIMT kernel")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def attended_counts(inp, cfg):
+    """Per sequence: attended compressed tokens and residual rows that fall in
+    attended blocks (exact, from the selection and the block CSR)."""
+    import torch
+    B, nb = inp["res_ptr"].shape[0], cfg.nb
+    mask = torch.zeros(B, nb, dtype=torch.bool, device=inp["res_ptr"].device)
+    if inp["sel"] is None:
+        mask[:] = True
+    else:
+        mask.scatter_(1, inp["sel"].long(), True)
+    if inp["keep"] is not None:
+        mask &= inp["keep"].bool()
+    sizes = torch.full((nb,), cfg.block, device=mask.device)
+    sizes[-1] = cfg.ctx_len - (nb - 1) * cfg.block
+    n_att = (mask * sizes).sum(1)
+    per_blk = (inp["res_ptr"][..., 1:] - inp["res_ptr"][..., :-1]).long()        # [B, Hkv, nb]
+    n_res_att = (per_blk * mask[:, None, :]).sum((1, 2))
+    return n_att.tolist(), n_res_att.tolist()
+
+
+def work_per_call(cfg, n_att, n_res_att, win):
+    """Algorithmic bytes and FLOPs of one layer call (all sequences).
+
+    Bytes: every attended A row once (int8 rows add their scale), every
+    residual row applied (value, index, int8 scale), the layer factor, the
+    predictor, q and out, the window rows. FLOPs: key rebuild 2*r*Hkv*d,
+    predictor 2*Hkv*d*(d + h) per token (the W2 product is applied after the
+    attention-weighted sum, a linear rewrite), scores 2*Hq*d and weighted sums
+    2*Hq*(d + h) per token."""
+    d, hkv, hq, r, h = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, cfg.rank, cfg.mlp_hidden
+    ea = {"f32": 4, "bf16": 2, "i8": 1}[cfg.a_dtype]
+    er = {"f32": 4, "bf16": 2, "i8": 1}[cfg.res_dtype]
+    ew = {"f32": 4, "bf16": 2}[cfg.act]
+    byts = flops = flops_direct = 0
+    for na, nr in zip(n_att, n_res_att):
+        byts += na * (r * ea + (4 if cfg.a_dtype == "i8" else 0))
+        byts += nr * (d * er + 4 + (4 if cfg.res_dtype == "i8" else 0))
+        byts += (r * hkv * d + hkv * (d * d + 2 * d * h)) * ew + 2 * hq * d * ew + win * 2 * hkv * d * ew
+        flops += 2 * na * hkv * d * (r + d + h) + 2 * na * hq * d + 2 * na * hq * (d + h)
+        flops_direct += 2 * na * r * hkv * d + 2 * na * hkv * (d * d + 2 * d * h) + 4 * (na + win) * hq * d
+    return byts, flops, flops_direct
+
+
+def stored_bytes(cfg):
+    """Compressed cache bytes per sequence over all layers (factors, predictor,
+    residuals with indices and block pointers) and the dense bf16 K+V bytes."""
+    d, hkv, r, h, T = cfg.head_dim, cfg.n_kv_heads, cfg.rank, cfg.mlp_hidden, cfg.ctx_len
+    ea = {"f32": 4, "bf16": 2, "i8": 1}[cfg.a_dtype]
+    er = {"f32": 4, "bf16": 2, "i8": 1}[cfg.res_dtype]
+    ew = {"f32": 4, "bf16": 2}[cfg.act]
+    groups = -(-cfg.n_layers // cfg.group)
+    a = groups * T * (r * ea + (4 if cfg.a_dtype == "i8" else 0))
+    per_layer = r * hkv * d * ew + hkv * (d * d + 2 * d * h) * ew
+    per_layer += hkv * cfg.n_res * (d * er + 4 + (4 if cfg.res_dtype == "i8" else 0)) + hkv * (cfg.nb + 1) * 4
+    stored = a + cfg.n_layers * per_layer
+    dense = cfg.n_layers * 2 * hkv * d * 2 * T
+    return stored, dense
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                          "(the path shards by sequence, see the design notes)"}))
+        sys.exit(2)
+    import torch
+    import long_context_decode_lowram_amd as L
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    if args.batch:
+        cfg = cfg.replace(batch=args.batch)
+    dev = "cuda"
+    torch.cuda.init()
+    t0 = time.time()
+    groups = [synth.gen_group_factor(cfg, g, dev) for g in range(-(-cfg.n_layers // cfg.group))]
+    layers = [synth.gen_layer(cfg, l, dev) for l in range(cfg.n_layers)]
+    win = min(cfg.win_cap, 128) if cfg.win_cap else 0
+    wins = [synth.gen_window(cfg, l, dev) if cfg.win_cap else (None, None) for l in range(cfg.n_layers)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    print(f"# generated {args.workload} B={cfg.batch} in {gen_s:.1f}s, "
+          f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident", file=sys.stderr, flush=True)
+
+    outs = [torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=layers[0]["q"].dtype, device=dev)
+            for _ in range(cfg.n_layers)]
+    calls = []
+    for l, x in enumerate(layers):
+        a, a_scale = groups[l // cfg.group]
+        wk, wv = wins[l]
+        calls.append(L.make_decode_args(x["q"], a, x["bl"], x["w_lin"], x["w1"], x["w2"], x["res_idx"],
+                                        x["res_val"], x["res_ptr"], outs[l], a_scale=a_scale, b1=x["b1"],
+                                        b2=x["b2"], res_scale=x["res_scale"], sel=x["sel"], keep=x["keep"],
+                                        win_k=wk, win_v=wv, win_len=win, generic=args.generic))
+    ws_bytes = max(L.decode_workspace_size(c) for c in calls)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for c in calls:
+        c.workspace, c.workspace_bytes = ws.data_ptr(), ws_bytes
+
+    counts = [attended_counts(x, cfg) for x in layers]
+    step_bytes = step_flops = step_flops_direct = 0
+    for n_att, n_res_att in counts:
+        b_, f_, fd_ = work_per_call(cfg, n_att, n_res_att, win)
+        step_bytes, step_flops, step_flops_direct = step_bytes + b_, step_flops + f_, step_flops_direct + fd_
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream()
+    n_ev = args.steps * cfg.n_layers
+    evs = [(ev.create(), ev.create()) for _ in range(n_ev)]
+
+    def step(timed_index=None):
+        for l, c in enumerate(calls):
+            if timed_index is not None:
+                c.ev_main_begin, c.ev_main_end = evs[timed_index * cfg.n_layers + l]
+            else:
+                c.ev_main_begin = c.ev_main_end = None
+            L.decode_launch(c, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    kernel_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    kern_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    generic = args.generic or not (cfg.act == "bf16" and cfg.a_dtype in ("bf16", "i8")
+                                   and cfg.mlp_hidden % 64 == 0 and cfg.rank % 64 == 0)
+    launch_flops = step_flops / cfg.n_layers
+    launch_bytes = step_bytes / cfg.n_layers
+    achieved = launch_flops / (kern_avg_ms * 1e-3) / 1e12
+    peak = PEAK_F32_VALU_TFLOPS if generic else PEAK_BF16_TFLOPS
+    cached = cfg.batch * (cfg.ctx_len + win)
+    hbm_gbs = step_bytes / (ms * 1e-3) / 1e9
+    stored, dense = stored_bytes(cfg)
+    result = {
+        "metric": "decode-step reconstructed-KV attention: cached tokens/s and % of HBM roofline",
+        "value": cached / (ms * 1e-3),
+        "unit": "cached tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if cfg.act == "f32" else ("bf16+i8" if cfg.a_dtype == "i8" else "bf16"),
+        "data": "synthetic (seeded draws at Llama-3.1-8B / Mistral-7B attention shapes)",
+        "config": {"workload": args.workload, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
+                   "layers": cfg.n_layers, "rank": cfg.rank, "mlp_hidden": cfg.mlp_hidden,
+                   "blocks_attended_per_layer": int(sum(c[0][0] for c in counts) / cfg.n_layers // cfg.block),
+                   "n_res": cfg.n_res, "window": win, "kernel": "generic-f32" if generic else "mfma-bf16"},
+        "hbm": {"algorithmic_bytes_per_step": step_bytes, "achieved_GBs": hbm_gbs,
+                "frac_of_8TBs": hbm_gbs / PEAK_HBM_GBS},
+        "roofline": {"bound": "alu" if generic else "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel": "decode_generic_kernel" if generic else "decode_mfma_kernel",
+                     "kernel_avg_ms": kern_avg_ms, "flops_per_launch": launch_flops,
+                     "bytes_per_launch": launch_bytes,
+                     "direct_method_flops_per_launch": step_flops_direct / cfg.n_layers},
+        "attention_only_decode_tokens_per_s": cfg.batch / (ms * 1e-3),
+        "compression_ratio": dense / stored,
+        "input_generation_s": gen_s,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_baseline(cfg, groups, layers, wins, outs, win,
+                                                                args.cpu_seconds)
+    if args.rank:
+        result["rank_residuals"] = bench_rank(args.steps, args.warmup, ev)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, groups, layers, wins, outs, win, budget_s):
+    """The float64 oracle on sequence 0 of successive layers (until the time
+    budget is spent), timed on this host's cores, and the relative error of
+    the GPU outputs of those same (sequence, layer) pairs against it."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    import oracle
+
+    def host(t):
+        if t is None:
+            return None
+        t = t[0:1]
+        return (t.float() if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+    layer_s, errs, used = [], [], 0
+    with threadpoolctl.threadpool_limits(limits=len(os.sched_getaffinity(0))):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        for l in range(cfg.n_layers):
+            a, a_scale = groups[l // cfg.group]
+            x = layers[l]
+            batch = {k: host(x[k]) for k in ("q", "bl", "w_lin", "w1", "w2", "b1", "b2", "res_idx", "res_val",
+                                             "res_scale", "sel", "keep")}
+            batch.update(a=host(a), a_scale=host(a_scale), block=cfg.block, win_len=win,
+                         win_k=host(wins[l][0]), win_v=host(wins[l][1]))
+            t0 = time.time()
+            ref, _ = oracle.decode_step(batch)
+            layer_s.append(time.time() - t0)
+            got = outs[l][0:1].float().cpu().numpy()
+            errs.append(float(np.max(np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1))))
+            used += 1
+            if sum(layer_s) >= budget_s:
+                break
+    t_layer = sum(layer_s) / len(layer_s)
+    rate = (cfg.ctx_len + win) / (cfg.n_layers * t_layer)
+    return ({"value": rate, "unit": "cached tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"sequence 0 of layers 0..{used - 1} ({used} of {cfg.n_layers} layer calls, "
+                       f"{sum(layer_s):.1f} s); step rate extrapolated as one sequence x all layers",
+             "seconds_per_layer_call": t_layer},
+            {"oracle_layers_checked": used, "max_rel_err": max(errs), "tolerance": 2e-2 if cfg.act == "bf16" else 1e-4})
+
+
+def bench_rank(steps, warmup, ev):
+    import torch
+    import long_context_decode_lowram_amd as L
+    import synth
+
+    rc = synth.RANK_C5
+    v, vh = synth.gen_rank_inputs(rc, "cuda", plant_ties=False)
+    Lr, T, hkv, d = v.shape
+    k, nb = rc.n_res, -(-T // 64)
+    o = {"idx": torch.empty(Lr, hkv, k, dtype=torch.int32, device="cuda"),
+         "val": torch.empty(Lr, hkv, k, d, dtype=torch.int8, device="cuda"),
+         "scale": torch.empty(Lr, hkv, k, dtype=torch.float32, device="cuda"),
+         "ptr": torch.empty(Lr, hkv, nb + 1, dtype=torch.int32, device="cuda")}
+    args = L.make_rank_args(v, vh, k, "i8", o["idx"], o["val"], o["scale"], o["ptr"])
+    ws = torch.empty(L.rank_workspace_size(args), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    for _ in range(warmup):
+        L.rank_launch(args)
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(steps):
+        args.ev_main_begin, args.ev_main_end = evs[i]
+        L.rank_launch(args)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    err_ms = sum(ev.elapsed_ms(a, b) for a, b in evs) / steps
+    in_bytes = 2 * v.numel() * v.element_size()
+    err_bytes = in_bytes + Lr * hkv * T * 8
+    return {"shape": [Lr, T, hkv, d], "n_res": k, "ms_per_call": ms,
+            "error_kernel_ms": err_ms, "error_kernel_GBs": err_bytes / (err_ms * 1e-3) / 1e9,
+            "error_kernel_frac_of_8TBs": err_bytes / (err_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "whole_call_input_GBs": in_bytes / (ms * 1e-3) / 1e9}
+
+
+if __name__ == "__main__":
+    main()

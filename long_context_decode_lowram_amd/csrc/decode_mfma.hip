@@ -1,10 +1,424 @@
-// bf16 MFMA decode kernel (placeholder until the fused kernel lands).
+// Fused bf16 MFMA decode kernel for gfx950 (wave64, v_mfma_f32_16x16x32_bf16).
+//
+// Work split: one wave per attended 64-token block, four blocks of one KV head
+// per workgroup, so the head's B_l chunks and predictor weights are staged in
+// LDS once and shared by the four waves. Workgroup ids are remapped so that
+// the KV heads of one block group land on the same XCD (its L2 then serves the
+// eight reads of the same A rows).
+//
+// Per wave, all on MFMA with fp32 accumulation:
+//   1. K^T[n][t] = B_l[:, head]^T . A_blk^T  over the rank (A rows straight
+//      from HBM into VGPRs, B_l chunks from LDS). int8 A rows are exact in
+//      bf16; their per-row scale multiplies the accumulator column.
+//   2. The accumulators, rounded to bf16, are used in place as the A operand
+//      of the next products (the k-slot order of an MFMA is free as long as
+//      both operands agree, which removes any transpose):
+//      S^T = K . Q^T  (query heads of this KV head padded to 16 columns),
+//      Z   = K . [W1 | W_lin]^T  in chunks of 64 features.
+//   3. Softmax weights against the workgroup-wide max; gelu(Z_W1 + b1) in
+//      fp32; O = P . [gelu | K W_lin]  (P in registers as the A operand).
+//   4. Residual rows of the block add P[t] * R to the K W_lin part.
+//   5. The four waves' O are summed in fixed order into one partial record
+//      (m, l, O_G[h], O_V[d]); the combine kernel applies W2 and b2 after the
+//      split merge: sum_t p_t (g_t W2 + b2) = (sum_t p_t g_t) W2 + l b2.
+#include <math.h>
+
 #include "kernels.hpp"
 
 namespace lowram {
 
-bool mfma_supported(const DecodeParams&, int, int, int) { return false; }
-int mfma_blocks_per_split() { return 1; }
-hipError_t launch_decode_mfma(const DecodeParams&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;                 // blocks per workgroup
+constexpr int kThreads = kWaves * kWave;
+constexpr int kKc = 64;                   // rank columns per staged B_l chunk
+constexpr int kBlRow = kKc + 8;           // padded LDS row of a B_l chunk (elements)
+constexpr int kFc = 64;                   // features per staged weight chunk
+constexpr int kWRow = kHeadDim + 8;       // padded LDS row of a weight chunk
+constexpr int kStage = 128 * kBlRow;      // elements per stage buffer (>= kFc * kWRow)
+constexpr int kQRow = kHeadDim + 8;
+constexpr int kMaxG = 8;
+constexpr int kXcd = 8;                   // XCDs on MI355X; workgroups go round-robin over them
+static_assert(kFc * kWRow <= kStage, "stage buffer too small for a weight chunk");
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
+    bf16x8 r;
+    r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+    r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+    return r;
+}
+
+// Two 4-element halves (n .. n+3 and n+16 .. n+19) of a bf16 LDS row.
+__device__ __forceinline__ bf16x8 lds_pair(const __bf16* row, int n) {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(row + n);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(row + n + 16);
+    u32x4 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+    return as_bf16x8(v);
+}
+
+// 8 int8 codes -> 8 bf16 (exact: |q| <= 127 needs 7 bits).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = static_cast<int8_t>((v[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        r[i] = (__bf16)static_cast<float>(q);
+    }
+    return r;
+}
+
+template <int ADT>
+__device__ __forceinline__ bf16x8 load_a_frag(const void* a, int64_t row_elem, bool valid) {
+    if (ADT == DT_BF16) {
+        if (!valid) return as_bf16x8(u32x4{0, 0, 0, 0});
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a) + row_elem));
+    } else {
+        if (!valid) return as_bf16x8(u32x4{0, 0, 0, 0});
+        return i8x8_to_bf16(*reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(a) + row_elem));
+    }
+}
+
+}  // namespace
+
+template <int ADT, int RDT>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p, int n_split_pad) {
+    // ---- workgroup -> (b, KV head, split), heads of one split on one XCD
+    const int per_b = n_split_pad * p.n_kv;
+    const int b = blockIdx.x / per_b;
+    const int rem = blockIdx.x % per_b;
+    const int xcd = rem % kXcd, slot = rem / kXcd;
+    const int h = slot % p.n_kv;
+    const int split = (slot / p.n_kv) * kXcd + xcd;
+    if (split >= p.n_split) return;
+    const int n_att = p.att_count[b];
+    if (split * kWaves >= n_att) return;         // beyond this sequence's attended blocks
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int G = p.group, H = p.hidden, R = p.rank;
+
+    __shared__ __attribute__((aligned(16))) __bf16 stage[2][kStage];
+    __shared__ __attribute__((aligned(16))) __bf16 qs[16 * kQRow];
+    __shared__ float pl[kWaves][kMaxG][kBlock];        // softmax weights for the residual rows
+    __shared__ float oslot[kWaves][kMaxG][kFc];        // per-wave O of the current feature chunk
+    __shared__ float mw[kWaves][kMaxG], lw[kWaves][kMaxG];
+
+    const int bi = split * kWaves + w;                 // this wave's attended-block index
+    const bool active = bi < n_att;
+    const int blk = active ? p.att_list[(int64_t)b * p.n_blocks + bi] : 0;
+    const int t0 = blk * kBlock;
+    const int nt = active ? min(kBlock, p.ctx_len - t0) : 0;
+
+    // ---- stage the query rows of this head (rows >= G zero)
+    for (int e = tid; e < 16 * kHeadDim; e += kThreads) {
+        const int j = e / kHeadDim, n = e % kHeadDim;
+        __bf16 v = (__bf16)0.0f;
+        if (j < G) v = static_cast<const __bf16*>(p.q)[((int64_t)b * p.n_q + h * G + j) * kHeadDim + n];
+        qs[j * kQRow + n] = v;
+    }
+
+    // ---- 1. K^T = B_l(head)^T . A_blk^T
+    const __bf16* bl = static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R;
+    const int64_t a_row0 = (int64_t)b * p.ctx_len + t0;
+    const int n_chunks = R / kKc;
+
+    auto stage_bl = [&](int c, u32x4 (&reg)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, row = e >> 3, col = (e & 7) * 8;
+            reg[q] = *reinterpret_cast<const u32x4*>(bl + (int64_t)row * R + c * kKc + col);
+        }
+    };
+    auto store_bl = [&](int buf, const u32x4 (&reg)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, row = e >> 3, col = (e & 7) * 8;
+            *reinterpret_cast<u32x4*>(&stage[buf][row * kBlRow + col]) = reg[q];
+        }
+    };
+    auto load_a = [&](int c, bf16x8 (&af)[2][4]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int tl = tt * 16 + l16;
+                af[kk][tt] = load_a_frag<ADT>(p.a, (a_row0 + tl) * R + c * kKc + kk * 32 + g4 * 8, tl < nt);
+            }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int nt_ = 0; nt_ < 8; ++nt_)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    {
+        u32x4 pre[4];
+        stage_bl(0, pre);
+        store_bl(0, pre);
+    }
+    bf16x8 af[2][4];
+    load_a(0, af);
+    __syncthreads();
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const bool more = c + 1 < n_chunks;
+        u32x4 pre[4];
+        bf16x8 an[2][4];
+        if (more) {
+            stage_bl(c + 1, pre);
+            load_a(c + 1, an);
+        }
+        const __bf16* sb = stage[c & 1];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int nt_ = 0; nt_ < 8; ++nt_) {
+                const bf16x8 bf = as_bf16x8(
+                    *reinterpret_cast<const u32x4*>(sb + (nt_ * 16 + l16) * kBlRow + kk * 32 + g4 * 8));
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bf, af[kk][tt], acc[nt_][tt]);
+            }
+        }
+        if (more) store_bl((c + 1) & 1, pre);
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) af[kk][tt] = an[kk][tt];
+        }
+    }
+
+    if (ADT == DT_I8) {           // per-row scale of the int8 factor, applied to column t
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int tl = tt * 16 + l16;
+            const float s = tl < nt ? p.a_scale[a_row0 + tl] : 0.f;
+#pragma unroll
+            for (int nt_ = 0; nt_ < 8; ++nt_) acc[nt_][tt] *= s;
+        }
+    }
+
+    // K as the A operand: kf[tt][s] holds n = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[tt][s] = pack8(acc[2 * s][tt], acc[2 * s + 1][tt]);
+
+    // ---- 2. scores S^T = K . Q^T ; lane holds S[j = l16][t = 16 tt + 4 g4 + i]
+    f32x4 sc[4];
+    {
+        bf16x8 qf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = lds_pair(qs + l16 * kQRow, 32 * s + 4 * g4);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sc[tt] = mfma(kf[tt][s], qf[s], sc[tt]);
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tl = tt * 16 + 4 * g4 + i;
+            const float v = tl < nt ? sc[tt][i] * p.scale : -INFINITY;
+            sc[tt][i] = v;
+            mloc = fmaxf(mloc, v);
+        }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    if (lane < G) mw[w][lane] = mloc;
+    __syncthreads();
+    float M = -INFINITY;
+    if (l16 < G)
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw[ww][l16]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = (l16 < G && M != -INFINITY && sc[tt][i] != -INFINITY) ? __expf(sc[tt][i] - M) : 0.f;
+            sc[tt][i] = e;
+            lsum += e;
+            if (l16 < G) pl[w][l16][tt * 16 + 4 * g4 + i] = e;
+        }
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    if (lane < G) lw[w][lane] = lsum;
+    // P as the A operand over tokens: pf[u] holds t = 32u + 4g + (0..3) and 32u + 16 + 4g + (0..3).
+    bf16x8 pf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) pf[u] = pack8(sc[2 * u], sc[2 * u + 1]);
+
+    // Residual slots of this wave's block.
+    int lo = 0, hi = 0;
+    const int64_t res_row = ((int64_t)b * p.n_kv + h) * p.n_res;
+    if (active) {
+        const int64_t pr = ((int64_t)b * p.n_kv + h) * (p.n_blocks + 1) + blk;
+        lo = max(0, min(p.res_ptr[pr], p.n_res));
+        hi = max(lo, min(p.res_ptr[pr + 1], p.n_res));
+    }
+
+    // ---- 3/4. feature chunks of [W1 | W_lin]: Z = K W^T, gelu on the W1 part, O = P Z
+    const int n_fchunks = (H + kHeadDim) / kFc;
+    const __bf16* w1 = static_cast<const __bf16*>(p.w1) + ((int64_t)b * p.n_kv + h) * H * (int64_t)kHeadDim;
+    const __bf16* wl = static_cast<const __bf16*>(p.w_lin) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)kHeadDim;
+    const __bf16* b1 = p.b1 ? static_cast<const __bf16*>(p.b1) + ((int64_t)b * p.n_kv + h) * H : nullptr;
+    float* rec0 = p.partials + (((int64_t)b * p.n_q + h * G) * p.n_split + split) * (int64_t)p.part_stride;
+    const int64_t rec_step = (int64_t)p.n_split * p.part_stride;
+
+    auto stage_w = [&](int fc, u32x4 (&reg)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, row = e >> 4, col = (e & 15) * 8;
+            const int f = fc * kFc + row;
+            const __bf16* src = f < H ? w1 + (int64_t)f * kHeadDim : wl + (int64_t)(f - H) * kHeadDim;
+            reg[q] = *reinterpret_cast<const u32x4*>(src + col);
+        }
+    };
+    auto store_w = [&](int buf, const u32x4 (&reg)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + kThreads * q, row = e >> 4, col = (e & 15) * 8;
+            *reinterpret_cast<u32x4*>(&stage[buf][row * kWRow + col]) = reg[q];
+        }
+    };
+
+    {
+        u32x4 pre[4];
+        stage_w(0, pre);
+        store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
+    }
+    __syncthreads();
+    int applied = 0;
+    for (int fc = 0; fc < n_fchunks; ++fc) {
+        const bool more = fc + 1 < n_fchunks;
+        u32x4 pre[4];
+        if (more) stage_w(fc + 1, pre);
+        const __bf16* sw = stage[fc & 1];
+        const int f0 = fc * kFc;
+        const bool gpart = f0 < H;
+        f32x4 o[4];
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft) {
+            bf16x8 wf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wf[s] = lds_pair(sw + (ft * 16 + l16) * kWRow, 32 * s + 4 * g4);
+            f32x4 z[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                z[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) z[tt] = mfma(kf[tt][s], wf[s], z[tt]);
+            }
+            if (gpart) {
+                const float bb = b1 ? (float)b1[f0 + ft * 16 + l16] : 0.f;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[tt][i] = gelu_erf(z[tt][i] + bb);
+            }
+            o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(z[2 * u], z[2 * u + 1]), o[ft]);
+        }
+        if (!gpart && active) {
+            // Residual rows of this block: O[j][f] += P[j][t] * R[f - H].
+            for (int q = lo; q < hi; ++q) {
+                const int tl = p.res_idx[res_row + q] - t0;
+                if (tl < 0 || tl >= nt) continue;
+                applied += (fc == n_fchunks - 1) ? 1 : 0;
+                float rs = 1.f;
+                if (RDT == DT_I8) rs = p.res_scale[res_row + q];
+#pragma unroll
+                for (int ft = 0; ft < 4; ++ft) {
+                    const int64_t ri = (res_row + q) * kHeadDim + (f0 - H) + ft * 16 + l16;
+                    const float rv = ld<RDT>(p.res_val, ri) * rs;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 4 * g4 + i;
+                        if (j < G) o[ft][i] += pl[w][j][tl] * rv;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * g4 + i;
+                if (j < G) oslot[w][j][ft * 16 + l16] = active ? o[ft][i] : 0.f;
+            }
+        if (more) store_w((fc + 1) & 1, pre);
+        __syncthreads();
+        for (int e = tid; e < G * kFc; e += kThreads) {
+            const int j = e / kFc, fl = e % kFc;
+            const float v = oslot[0][j][fl] + oslot[1][j][fl] + oslot[2][j][fl] + oslot[3][j][fl];
+            rec0[j * rec_step + 2 + f0 + fl] = v;
+        }
+        __syncthreads();
+    }
+
+    // ---- 5. record header and counts
+    if (tid < G) {
+        float m = -INFINITY, l = 0.f;
+        for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, mw[ww][tid]);
+        for (int ww = 0; ww < kWaves; ++ww) l += lw[ww][tid];
+        rec0[tid * rec_step + 0] = m;
+        rec0[tid * rec_step + 1] = l;
+    }
+    __shared__ int cnt_tok[kWaves], cnt_res[kWaves];
+    if (lane == 0) {
+        cnt_tok[w] = nt;
+        cnt_res[w] = applied;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t* c = p.counts + (((int64_t)b * p.n_kv + h) * p.n_split + split) * 2;
+        c[0] = cnt_tok[0] + cnt_tok[1] + cnt_tok[2] + cnt_tok[3];
+        c[1] = cnt_res[0] + cnt_res[1] + cnt_res[2] + cnt_res[3];
+    }
+}
+
+bool mfma_supported(const DecodeParams& p, int act, int adt, int rdt) {
+    (void)rdt;
+    return act == DT_BF16 && (adt == DT_BF16 || adt == DT_I8) && p.group >= 1 && p.group <= kMaxG &&
+           p.hidden % kFc == 0 && p.rank % kKc == 0;
+}
+
+int mfma_blocks_per_split() { return kWaves; }
+
+template <int ADT>
+static hipError_t launch_r(const DecodeParams& p, int rdt, hipStream_t s) {
+    const int n_split_pad = (p.n_split + kXcd - 1) / kXcd * kXcd;
+    const dim3 grid((unsigned)((int64_t)n_split_pad * p.n_kv * p.batch));
+    switch (rdt) {
+        case DT_F32: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_F32>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
+        case DT_BF16: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_BF16>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
+        default: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_I8>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int adt, int rdt, hipStream_t s) {
+    return adt == DT_I8 ? launch_r<DT_I8>(p, rdt, s) : launch_r<DT_BF16>(p, rdt, s);
+}
 
 }  // namespace lowram
