@@ -79,15 +79,50 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v) {
     return r;
 }
 
-template <int ADT>
-__device__ __forceinline__ bf16x8 load_a_frag(const void* a, int64_t row_elem, bool valid) {
-    if (ADT == DT_BF16) {
-        if (!valid) return as_bf16x8(u32x4{0, 0, 0, 0});
-        return as_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a) + row_elem));
-    } else {
-        if (!valid) return as_bf16x8(u32x4{0, 0, 0, 0});
-        return i8x8_to_bf16(*reinterpret_cast<const u32x2*>(static_cast<const int8_t*>(a) + row_elem));
+// A buffer descriptor over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One A-row fragment (8 rank columns of one token) at byte offset `off` of
+// the wave's block, kept raw until the MFMA uses it (bf16 as is, int8 codes
+// widened then); rows past the block's end read as zero.
+template <int ADT> struct AFrag;
+template <> struct AFrag<DT_BF16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     }
+    __device__ __forceinline__ bf16x8 get() const { return as_bf16x8(v); }
+};
+template <> struct AFrag<DT_I8> {
+    u32x2 v;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+    __device__ __forceinline__ bf16x8 get() const { return i8x8_to_bf16(v); }
+};
+
+// GELU(x) = x Phi(x) through the normal tail Q(a) = 1 - Phi(a), a = |x|:
+// log2 Q on [0, 6] is a degree-7 polynomial in (a - 3) fitted on Chebyshev
+// nodes (gelu_tail_fit.py derives the constants and bounds the float32
+// evaluation: |error| < 7e-7 over the real line, far below the bf16 rounding
+// the result goes through next). One exp2, no divide, no branch.
+__device__ __forceinline__ float gelu_tail(float x) {
+    constexpr float c0 = -9.53293514251709f, c1 = -4.7365193367004395f, c2 = -0.6704442501068115f,
+                    c3 = -0.007554398849606514f, c4 = 0.0011327347019687295f,
+                    c5 = -0.00016774206596892327f, c6 = 2.2999249267741106e-05f,
+                    c7 = -1.8896262190537527e-06f;
+    const float a = fminf(fabsf(x), 6.0f) - 3.0f;
+    float p = fmaf(c7, a, c6);
+    p = fmaf(p, a, c5);
+    p = fmaf(p, a, c4);
+    p = fmaf(p, a, c3);
+    p = fmaf(p, a, c2);
+    p = fmaf(p, a, c1);
+    p = fmaf(p, a, c0);
+    const float t = x * __builtin_amdgcn_exp2f(p);
+    return x >= 0.0f ? x - t : t;
 }
 
 }  // namespace
@@ -105,7 +140,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int n_att = p.att_count[b];
     if (split * kWaves >= n_att) return;         // beyond this sequence's attended blocks
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, provably uniform
     const int l16 = lane & 15, g4 = lane >> 4;
     const int G = p.group, H = p.hidden, R = p.rank;
 
@@ -130,16 +166,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     }
 
     // ---- 1. K^T = B_l(head)^T . A_blk^T
-    const __bf16* bl = static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R;
+    constexpr int EA = ADT == DT_BF16 ? 2 : 1;   // bytes per A element
     const int64_t a_row0 = (int64_t)b * p.ctx_len + t0;
+    const __amdgpu_buffer_rsrc_t ra =
+        rsrc(static_cast<const char*>(p.a) + a_row0 * R * EA, (uint32_t)(nt * R * EA));
+    const __amdgpu_buffer_rsrc_t rb =
+        rsrc(static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R,
+             (uint32_t)(kHeadDim * R * 2));
     const int n_chunks = R / kKc;
+    uint32_t a_off[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) a_off[tt] = (uint32_t)(((tt * 16 + l16) * R + g4 * 8) * EA);
+    uint32_t b_off[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = tid + kThreads * q;
+        b_off[q] = (uint32_t)(((e >> 3) * R + (e & 7) * 8) * 2);
+    }
 
     auto stage_bl = [&](int c, u32x4 (&reg)[4]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + kThreads * q, row = e >> 3, col = (e & 7) * 8;
-            reg[q] = *reinterpret_cast<const u32x4*>(bl + (int64_t)row * R + c * kKc + col);
-        }
+        for (int q = 0; q < 4; ++q) reg[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[q] + c * kKc * 2, 0, 0);
     };
     auto store_bl = [&](int buf, const u32x4 (&reg)[4]) {
 #pragma unroll
@@ -148,14 +195,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             *reinterpret_cast<u32x4*>(&stage[buf][row * kBlRow + col]) = reg[q];
         }
     };
-    auto load_a = [&](int c, bf16x8 (&af)[2][4]) {
+    using Frag = AFrag<ADT>;
+    auto load_a = [&](int c, Frag (&af)[2][4]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int tl = tt * 16 + l16;
-                af[kk][tt] = load_a_frag<ADT>(p.a, (a_row0 + tl) * R + c * kKc + kk * 32 + g4 * 8, tl < nt);
-            }
+            for (int tt = 0; tt < 4; ++tt) af[kk][tt].load(ra, a_off[tt] + (c * kKc + kk * 32) * EA);
     };
 
     f32x4 acc[8][4];
@@ -169,37 +214,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         stage_bl(0, pre);
         store_bl(0, pre);
     }
-    bf16x8 af[2][4];
-    load_a(0, af);
+    Frag afA[2][4], afB[2][4];
+    load_a(0, afA);
     __syncthreads();
 
-    for (int c = 0; c < n_chunks; ++c) {
+    // One chunk: prefetch chunk c+1 (B_l to registers, A fragments into `nxt`),
+    // multiply chunk c from LDS and `cur`, then publish the prefetched B_l.
+    auto chunk = [&](int c, const Frag (&cur)[2][4], Frag (&nxt)[2][4]) {
         const bool more = c + 1 < n_chunks;
         u32x4 pre[4];
-        bf16x8 an[2][4];
         if (more) {
             stage_bl(c + 1, pre);
-            load_a(c + 1, an);
+            load_a(c + 1, nxt);
         }
         const __bf16* sb = stage[c & 1];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 a8[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) a8[tt] = cur[kk][tt].get();
 #pragma unroll
             for (int nt_ = 0; nt_ < 8; ++nt_) {
                 const bf16x8 bf = as_bf16x8(
                     *reinterpret_cast<const u32x4*>(sb + (nt_ * 16 + l16) * kBlRow + kk * 32 + g4 * 8));
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bf, af[kk][tt], acc[nt_][tt]);
+                for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bf, a8[tt], acc[nt_][tt]);
             }
         }
         if (more) store_bl((c + 1) & 1, pre);
         __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) af[kk][tt] = an[kk][tt];
-        }
+    };
+    for (int c = 0; c < n_chunks; c += 2) {     // unrolled by two: the A registers ping-pong
+        chunk(c, afA, afB);
+        if (c + 1 < n_chunks) chunk(c + 1, afB, afA);
     }
 
     if (ADT == DT_I8) {           // per-row scale of the int8 factor, applied to column t
@@ -307,7 +354,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
     }
     __syncthreads();
+
+    // Residual rows of this block, weighted by P, for all d value features at
+    // once: rv[ft][i] holds feature 16 ft + l16 of query head 4 g4 + i. Rows are
+    // read eight at a time so their loads overlap.
+    f32x4 rv[8];
+#pragma unroll
+    for (int ft = 0; ft < 8; ++ft) rv[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     int applied = 0;
+    for (int q0 = lo; q0 < hi; q0 += 8) {
+        int tl[8];
+        float wgt[8];
+        float v[8][8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int q = min(q0 + r, hi - 1);
+            const int t = p.res_idx[res_row + q] - t0;
+            tl[r] = (q0 + r < hi && t >= 0 && t < nt) ? t : -1;
+            wgt[r] = RDT == DT_I8 ? p.res_scale[res_row + q] : 1.f;
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) v[r][ft] = ld<RDT>(p.res_val, (res_row + q) * kHeadDim + ft * 16 + l16);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (tl[r] < 0) continue;
+            ++applied;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * g4 + i;
+                const float pw = j < G ? pl[w][j][tl[r]] * wgt[r] : 0.f;
+#pragma unroll
+                for (int ft = 0; ft < 8; ++ft) rv[ft][i] += pw * v[r][ft];
+            }
+        }
+    }
     for (int fc = 0; fc < n_fchunks; ++fc) {
         const bool more = fc + 1 < n_fchunks;
         u32x4 pre[4];
@@ -333,31 +413,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) z[tt][i] = gelu_erf(z[tt][i] + bb);
+                    for (int i = 0; i < 4; ++i) z[tt][i] = gelu_tail(z[tt][i] + bb);
             }
             o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(z[2 * u], z[2 * u + 1]), o[ft]);
         }
-        if (!gpart && active) {
-            // Residual rows of this block: O[j][f] += P[j][t] * R[f - H].
-            for (int q = lo; q < hi; ++q) {
-                const int tl = p.res_idx[res_row + q] - t0;
-                if (tl < 0 || tl >= nt) continue;
-                applied += (fc == n_fchunks - 1) ? 1 : 0;
-                float rs = 1.f;
-                if (RDT == DT_I8) rs = p.res_scale[res_row + q];
+        if (!gpart) {            // add the residual rows to the k W_lin features
+            const bool second = f0 - H >= kFc;
 #pragma unroll
-                for (int ft = 0; ft < 4; ++ft) {
-                    const int64_t ri = (res_row + q) * kHeadDim + (f0 - H) + ft * 16 + l16;
-                    const float rv = ld<RDT>(p.res_val, ri) * rs;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = 4 * g4 + i;
-                        if (j < G) o[ft][i] += pl[w][j][tl] * rv;
-                    }
-                }
-            }
+            for (int ft = 0; ft < 4; ++ft) o[ft] += second ? rv[4 + ft] : rv[ft];
         }
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft)

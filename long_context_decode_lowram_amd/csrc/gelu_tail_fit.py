@@ -1,0 +1,47 @@
+"""Derive the constants of the device GELU used by the bf16 MFMA kernel.
+
+GELU(x) = x * Phi(x). With Q(a) = 1 - Phi(a) = erfc(a / sqrt 2) / 2 for a >= 0,
+GELU(x) = x - x Q(x) for x >= 0 and x Q(-x) for x < 0. The kernel evaluates
+log2 Q(a) on [0, 6] by a degree-7 polynomial in (a - 3) (least-squares fit on
+Chebyshev nodes of the interval), clamps a to 6 (Q(6) < 1e-9), and takes one
+exp2. This script prints the coefficients and the worst absolute GELU error
+of the float32 evaluation against scipy's erfc over [-12, 12].
+
+python long_context_decode_lowram_amd/csrc/gelu_tail_fit.py
+"""
+import numpy as np
+from scipy.special import erfc
+
+X, DEG, SHIFT = 6.0, 7, 3.0
+
+
+def fit():
+    n = 4000
+    a = np.cos(np.pi * (np.arange(n) + 0.5) / n) * X / 2 + X / 2
+    y = np.log2(0.5 * erfc(a / np.sqrt(2.0)))
+    c = np.polynomial.polynomial.polyfit(a - SHIFT, y, DEG)
+    return c.astype(np.float32)
+
+
+def gelu_f32(x, c):
+    x = np.asarray(x, np.float32)
+    a = np.minimum(np.abs(x), np.float32(X)) - np.float32(SHIFT)
+    p = np.float32(c[-1])
+    for k in range(len(c) - 2, -1, -1):
+        p = (p * a + c[k]).astype(np.float32)
+    q = np.exp2(p).astype(np.float32)
+    t = (x * q).astype(np.float32)
+    return np.where(x >= 0, (x - t).astype(np.float32), t)
+
+
+def max_error(c):
+    x = np.linspace(-12, 12, 2_000_001)
+    ref = x * (1.0 - 0.5 * erfc(x / np.sqrt(2.0)))
+    return float(np.max(np.abs(gelu_f32(x, c).astype(np.float64) - ref)))
+
+
+if __name__ == "__main__":
+    c = fit()
+    for k, v in enumerate(c):
+        print(f"    constexpr float kGeluTail{k} = {float(v)!r}f;")
+    print("max |gelu error| =", max_error(c))
