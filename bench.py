@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -103,6 +105,25 @@ def work_per_call(cfg, n_att, n_res_att, win):
         flops += 2 * na * hkv * d * (r + d + h) + 2 * na * hq * d + 2 * na * hq * (d + h)
         flops_direct += 2 * na * r * hkv * d + 2 * na * hkv * (d * d + 2 * d * h) + 4 * (na + win) * hq * d
     return byts, flops, flops_direct
+
+
+def recorded_traffic(workload, kernel_src):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes scaled by a calibration copy),
+    or None when there is none for this workload or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_kernel_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    text = open(path).read()
+    if f"sha256 (decode_mfma.hip): {sha}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch="):
+            return float(line.split("=", 1)[1])
+    return None
 
 
 def stored_bytes(cfg):
@@ -221,7 +242,9 @@ def main():
         "hbm": {"algorithmic_bytes_per_step": step_bytes, "achieved_GBs": hbm_gbs,
                 "frac_of_8TBs": hbm_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "alu" if generic else "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None if generic else recorded_traffic(
+                         args.workload, os.path.join(ROOT, "long_context_decode_lowram_amd", "csrc", "decode_mfma.hip")),
                      "kernel": "decode_generic_kernel" if generic else "decode_mfma_kernel",
                      "kernel_avg_ms": kern_avg_ms, "flops_per_launch": launch_flops,
                      "bytes_per_launch": launch_bytes,
@@ -236,6 +259,12 @@ def main():
                                                                 args.cpu_seconds)
     if args.rank:
         result["rank_residuals"] = bench_rank(args.steps, args.warmup, ev)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 1 << 30
     print(json.dumps(result), flush=True)
 
 
