@@ -103,17 +103,17 @@ template <> struct AFrag<DT_I8> {
     __device__ __forceinline__ bf16x8 get() const { return i8x8_to_bf16(v); }
 };
 
-// GELU(x) = x Phi(x) through the normal tail Q(a) = 1 - Phi(a), a = |x|:
-// log2 Q on [0, 6] is a degree-7 polynomial in (a - 3) fitted on Chebyshev
-// nodes (gelu_tail_fit.py derives the constants and bounds the float32
-// evaluation: |error| < 7e-7 over the real line, far below the bf16 rounding
-// the result goes through next). One exp2, no divide, no branch.
+// GELU(x) = x Phi(x) = max(x, 0) - |x| Q(|x|) with the normal tail
+// Q(a) = 1 - Phi(a). log2 Q on [0, 6] is a degree-7 polynomial in a fitted on
+// Chebyshev nodes; gelu_tail_fit.py derives the constants and bounds the
+// float32 evaluation: |error| < 7e-7 over the real line, far below the bf16
+// rounding the result goes through next. One exp2, no divide, no branch.
 __device__ __forceinline__ float gelu_tail(float x) {
-    constexpr float c0 = -9.53293514251709f, c1 = -4.7365193367004395f, c2 = -0.6704442501068115f,
-                    c3 = -0.007554398849606514f, c4 = 0.0011327347019687295f,
-                    c5 = -0.00016774206596892327f, c6 = 2.2999249267741106e-05f,
+    constexpr float c0 = -0.9999943375587463f, c1 = -1.1512691974639893f, c2 = -0.45840978622436523f,
+                    c3 = -0.05402068793773651f, c4 = 0.00853946153074503f,
+                    c5 = -0.0009388679172843695f, c6 = 6.268139986786991e-05f,
                     c7 = -1.8896262190537527e-06f;
-    const float a = fminf(fabsf(x), 6.0f) - 3.0f;
+    const float a = fminf(fabsf(x), 6.0f);
     float p = fmaf(c7, a, c6);
     p = fmaf(p, a, c5);
     p = fmaf(p, a, c4);
@@ -121,8 +121,7 @@ __device__ __forceinline__ float gelu_tail(float x) {
     p = fmaf(p, a, c2);
     p = fmaf(p, a, c1);
     p = fmaf(p, a, c0);
-    const float t = x * __builtin_amdgcn_exp2f(p);
-    return x >= 0.0f ? x - t : t;
+    return fmaxf(x, 0.0f) - a * __builtin_amdgcn_exp2f(p);
 }
 
 }  // namespace
@@ -221,12 +220,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // One chunk: prefetch chunk c+1 (B_l to registers, A fragments into `nxt`),
     // multiply chunk c from LDS and `cur`, then publish the prefetched B_l.
     auto chunk = [&](int c, const Frag (&cur)[2][4], Frag (&nxt)[2][4]) {
-        const bool more = c + 1 < n_chunks;
+        const int cn = min(c + 1, n_chunks - 1);     // unconditional prefetch; the last chunk reloads itself
         u32x4 pre[4];
-        if (more) {
-            stage_bl(c + 1, pre);
-            load_a(c + 1, nxt);
-        }
+        stage_bl(cn, pre);
+        load_a(cn, nxt);
         const __bf16* sb = stage[c & 1];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -241,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bf, a8[tt], acc[nt_][tt]);
             }
         }
-        if (more) store_bl((c + 1) & 1, pre);
+        store_bl((c + 1) & 1, pre);   // the other buffer: nobody reads it in this chunk
         __syncthreads();
     };
     for (int c = 0; c < n_chunks; c += 2) {     // unrolled by two: the A registers ping-pong
@@ -348,6 +345,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         }
     };
 
+    __shared__ float b1s[1024];          // hidden bias, zero when absent
+    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
     {
         u32x4 pre[4];
         stage_w(0, pre);
@@ -389,35 +388,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         }
     }
     for (int fc = 0; fc < n_fchunks; ++fc) {
-        const bool more = fc + 1 < n_fchunks;
         u32x4 pre[4];
-        if (more) stage_w(fc + 1, pre);
+        stage_w(min(fc + 1, n_fchunks - 1), pre);   // unconditional; the last chunk reloads itself
         const __bf16* sw = stage[fc & 1];
         const int f0 = fc * kFc;
         const bool gpart = f0 < H;
-        f32x4 o[4];
-#pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
+        // Z for one 16-feature tile; on the W1 part the accumulator starts at the bias.
+        auto ztile = [&](int ft, f32x4 (&z)[4]) {
             bf16x8 wf[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) wf[s] = lds_pair(sw + (ft * 16 + l16) * kWRow, 32 * s + 4 * g4);
-            f32x4 z[4];
+            const float bb = gpart ? b1s[f0 + ft * 16 + l16] : 0.f;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                z[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                z[tt] = f32x4{bb, bb, bb, bb};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) z[tt] = mfma(kf[tt][s], wf[s], z[tt]);
             }
+        };
+        f32x4 o[4], zc[4], zn[4];
+        ztile(0, zc);
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft) {
+            if (ft + 1 < 4) ztile(ft + 1, zn);        // the next tile's MFMAs overlap this tile's GELU
             if (gpart) {
-                const float bb = b1 ? (float)b1[f0 + ft * 16 + l16] : 0.f;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) z[tt][i] = gelu_tail(z[tt][i] + bb);
+                    for (int i = 0; i < 4; ++i) zc[tt][i] = gelu_tail(zc[tt][i]);
             }
             o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(z[2 * u], z[2 * u + 1]), o[ft]);
+            for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(zc[2 * u], zc[2 * u + 1]), o[ft]);
+            if (ft + 1 < 4) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) zc[tt] = zn[tt];
+            }
         }
         if (!gpart) {            // add the residual rows to the k W_lin features
             const bool second = f0 - H >= kFc;
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 const int j = 4 * g4 + i;
                 if (j < G) oslot[w][j][ft * 16 + l16] = active ? o[ft][i] : 0.f;
             }
-        if (more) store_w((fc + 1) & 1, pre);
+        store_w((fc + 1) & 1, pre);     // the other buffer: nobody reads it in this chunk
         __syncthreads();
         for (int e = tid; e < G * kFc; e += kThreads) {
             const int j = e / kFc, fl = e % kFc;

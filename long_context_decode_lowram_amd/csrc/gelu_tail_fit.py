@@ -1,18 +1,20 @@
 """Derive the constants of the device GELU used by the bf16 MFMA kernel.
 
 GELU(x) = x * Phi(x). With Q(a) = 1 - Phi(a) = erfc(a / sqrt 2) / 2 for a >= 0,
-GELU(x) = x - x Q(x) for x >= 0 and x Q(-x) for x < 0. The kernel evaluates
-log2 Q(a) on [0, 6] by a degree-7 polynomial in (a - 3) (least-squares fit on
-Chebyshev nodes of the interval), clamps a to 6 (Q(6) < 1e-9), and takes one
-exp2. This script prints the coefficients and the worst absolute GELU error
-of the float32 evaluation against scipy's erfc over [-12, 12].
+GELU(x) = x - x Q(x) for x >= 0 and x Q(-x) for x < 0, i.e.
+GELU(x) = max(x, 0) - |x| Q(|x|). The kernel evaluates log2 Q(a) on [0, 6] by
+a degree-7 polynomial in a (least-squares fit on Chebyshev nodes of the
+interval), clamps a to 6 (6 Q(6) < 1e-8, so beyond 6 the product
+min(|x|, 6) Q is below that bound), and takes one exp2. This script
+prints the coefficients and the worst absolute GELU error of the float32
+evaluation against scipy's erfc over [-12, 12].
 
 python long_context_decode_lowram_amd/csrc/gelu_tail_fit.py
 """
 import numpy as np
 from scipy.special import erfc
 
-X, DEG, SHIFT = 6.0, 7, 3.0
+X, DEG, SHIFT = 6.0, 7, 0.0
 
 
 def fit():
@@ -30,8 +32,8 @@ def gelu_f32(x, c):
     for k in range(len(c) - 2, -1, -1):
         p = (p * a + c[k]).astype(np.float32)
     q = np.exp2(p).astype(np.float32)
-    t = (x * q).astype(np.float32)
-    return np.where(x >= 0, (x - t).astype(np.float32), t)
+    t = (np.minimum(np.abs(x), np.float32(X)) * q).astype(np.float32)
+    return (np.maximum(x, np.float32(0)) - t).astype(np.float32)
 
 
 def max_error(c):
