@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
     float* sw = es + p.n_split;           // [win_len]
     float* oc = sw + nw;                  // [H + 128]
     float* qs = oc + H + kHeadDim;        // [128]
-    float* red = qs + kHeadDim;           // [8]
+    float* red = qs + kHeadDim;           // [8 + 128]: block reductions, then the second half-sums
 
     for (int f = tid; f < kHeadDim; f += blockDim.x)
         qs[f] = ld<ACT>(p.q, ((int64_t)b * p.n_q + j) * kHeadDim + f);
@@ -115,17 +115,36 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
             oc[f] = acc;
         }
         __syncthreads();
+        // out[f] = (sum_i O_G[i] W2[f][i] + O_V[f] + L b2[f] + window) / (L + L_w):
+        // two threads per output feature, each half of the W2 row in 16-byte loads.
         const float inv = 1.0f / (Lt + Lw);
-        for (int f = tid; f < kHeadDim; f += blockDim.x) {
-            const int64_t w2row = (((int64_t)b * p.n_kv + h) * kHeadDim + f) * H;
-            float y = 0.f;
-            for (int i = 0; i < H; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
+        const int f = tid & (kHeadDim - 1), half = tid >> 7;      // blockDim.x == 256
+        const int64_t w2row = (((int64_t)b * p.n_kv + h) * kHeadDim + f) * H;
+        const int i0 = half * (H / 2), i1 = i0 + H / 2;
+        float y = 0.f;
+        if (ACT == DT_BF16) {
+            const uint4* wv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.w2) + w2row + i0);
+            for (int c = 0; c < (i1 - i0) / 8; ++c) {
+                const uint4 u = wv[c];
+                const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int i = i0 + 8 * c + 2 * k;
+                    y += oc[i] * __uint_as_float(wd[k] << 16) + oc[i + 1] * __uint_as_float(wd[k] & 0xffff0000u);
+                }
+            }
+        } else {
+            for (int i = i0; i < i1; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
+        }
+        if (half == 1) {
             y += oc[H + f];
             if (p.b2) y += Lt * ld<ACT>(p.b2, ((int64_t)b * p.n_kv + h) * kHeadDim + f);
             for (int u = 0; u < nw; ++u)
                 y += sw[u] * ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f);
-            st<ACT>(p.out, out_row + f, y * inv);
+            red[8 + f] = y;
         }
+        __syncthreads();
+        if (half == 0) st<ACT>(p.out, out_row + f, (y + red[8 + f]) * inv);
     }
     if (p.stats != nullptr && j % p.group == 0 && tid == 0) {
         int tok = 0, res = 0;
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 }
 
 size_t combine_smem_bytes(const DecodeParams& p) {
-    return sizeof(float) * ((size_t)p.n_split + p.win_len + p.hidden + 2 * kHeadDim + 8);
+    return sizeof(float) * ((size_t)p.n_split + p.win_len + p.hidden + 3 * kHeadDim + 8);
 }
 
 hipError_t launch_combine(const DecodeParams& p, int act, hipStream_t s) {

@@ -7,9 +7,13 @@
 // eight reads of the same A rows).
 //
 // Per wave, all on MFMA with fp32 accumulation:
-//   1. K^T[n][t] = B_l[:, head]^T . A_blk^T  over the rank (A rows straight
-//      from HBM into VGPRs, B_l chunks from LDS). int8 A rows are exact in
-//      bf16; their per-row scale multiplies the accumulator column.
+//   1. K^T[n][t] = B_l[:, head]^T . A_blk^T  over the rank, 64 rank columns
+//      per chunk. Each chunk of B_l (shared) and of the wave's own A rows
+//      (bf16 factor) is copied global -> LDS by direct loads one chunk ahead,
+//      into unpadded rows with an XOR swizzle; no registers hold data in
+//      flight, so the next chunk's loads are issued before this chunk's
+//      MFMAs. int8 A rows come straight into registers (exact in bf16) and
+//      their per-row scale multiplies the accumulator column.
 //   2. The accumulators, rounded to bf16, are used in place as the A operand
 //      of the next products (the k-slot order of an MFMA is free as long as
 //      both operands agree, which removes any transpose):
@@ -37,14 +41,15 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;                 // blocks per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kKc = 64;                   // rank columns per staged B_l chunk
-constexpr int kBlRow = kKc + 8;           // padded LDS row of a B_l chunk (elements)
 constexpr int kFc = 64;                   // features per staged weight chunk
 constexpr int kWRow = kHeadDim + 8;       // padded LDS row of a weight chunk
-constexpr int kStage = 128 * kBlRow;      // elements per stage buffer (>= kFc * kWRow)
+constexpr int kRowBytes = kKc * 2;        // one bf16 row of a rank chunk: 128 bytes, eight 16-byte pieces
+constexpr int kStage = kFc * kWRow;       // elements per stage buffer: a padded weight chunk
 constexpr int kQRow = kHeadDim + 8;
 constexpr int kMaxG = 8;
 constexpr int kXcd = 8;                   // XCDs on MI355X; workgroups go round-robin over them
-static_assert(kFc * kWRow <= kStage, "stage buffer too small for a weight chunk");
+constexpr int kABytes = kBlock * kRowBytes;   // one wave's A rows of a rank chunk: 8 KB
+static_assert(128 * kRowBytes <= kStage * 2, "stage buffer too small for a B_l chunk");
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -83,6 +88,43 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier for the main loop. __syncthreads() would also wait for
+// every direct-to-LDS load still in flight (they count as LDS stores), which
+// includes the next chunk's A rows; here the caller has already waited for
+// the loads the other waves need, so only this wave's LDS operations are
+// drained. The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds + 16 i (in lane order), read from byte voff + soff of the buffer;
+// reads past the buffer's end produce zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+// Rank-chunk tiles in LDS are unpadded 128-byte rows of eight 16-byte
+// pieces; piece p of row r sits in slot p ^ swz(r). Sixteen consecutive rows
+// read at one logical piece then hit sixteen distinct 16-byte bank groups
+// (also eight distinct ones for any eight consecutive rows).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // One A-row fragment (8 rank columns of one token) at byte offset `off` of
 // the wave's block, kept raw until the MFMA uses it (bf16 as is, int8 codes
@@ -144,25 +186,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int l16 = lane & 15, g4 = lane >> 4;
     const int G = p.group, H = p.hidden, R = p.rank;
 
-    __shared__ __attribute__((aligned(16))) __bf16 stage[2][kStage];
-    __shared__ __attribute__((aligned(16))) __bf16 qs[16 * kQRow];
-    __shared__ float pl[kWaves][kMaxG][kBlock];        // softmax weights for the residual rows
-    __shared__ float oslot[kWaves][kMaxG][kFc];        // per-wave O of the current feature chunk
+    // LDS: two stage buffers (B_l rank chunks in the main loop, weight chunks
+    // after it) and one region that holds each wave's A rows in the main loop
+    // and the epilogue's small arrays after it. Separate objects, so the
+    // compiler's waits for direct-to-LDS loads stay per buffer.
+    __shared__ __attribute__((aligned(16))) __bf16 stg0[kStage], stg1[kStage];
+    __shared__ __attribute__((aligned(16))) unsigned char sa[kWaves * kABytes];
     __shared__ float mw[kWaves][kMaxG], lw[kWaves][kMaxG];
+    __bf16* const qs = reinterpret_cast<__bf16*>(sa);                                  // [16][kQRow]
+    float (*const pl)[kMaxG][kBlock] = reinterpret_cast<float (*)[kMaxG][kBlock]>(sa + 4352);   // softmax weights
+    float (*const oslot)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa + 12544);     // per-wave O chunk
+    float* const b1s = reinterpret_cast<float*>(sa + 20736);                           // [1024] hidden bias
+    static_assert(20736 + 4096 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352, "epilogue arrays overflow sa");
 
     const int bi = split * kWaves + w;                 // this wave's attended-block index
     const bool active = bi < n_att;
     const int blk = active ? p.att_list[(int64_t)b * p.n_blocks + bi] : 0;
     const int t0 = blk * kBlock;
     const int nt = active ? min(kBlock, p.ctx_len - t0) : 0;
-
-    // ---- stage the query rows of this head (rows >= G zero)
-    for (int e = tid; e < 16 * kHeadDim; e += kThreads) {
-        const int j = e / kHeadDim, n = e % kHeadDim;
-        __bf16 v = (__bf16)0.0f;
-        if (j < G) v = static_cast<const __bf16*>(p.q)[((int64_t)b * p.n_q + h * G + j) * kHeadDim + n];
-        qs[j * kQRow + n] = v;
-    }
 
     // ---- 1. K^T = B_l(head)^T . A_blk^T
     constexpr int EA = ADT == DT_BF16 ? 2 : 1;   // bytes per A element
@@ -173,28 +214,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         rsrc(static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R,
              (uint32_t)(kHeadDim * R * 2));
     const int n_chunks = R / kKc;
-    uint32_t a_off[4];
+
+    // Direct loads of a rank chunk: instruction q of a wave fills 8 rows
+    // (1 KB); lane i takes row 8q + i/8 and the piece that the swizzle puts
+    // in slot i%8 (rows start at multiples of 8, so swz = i/8 ^ (q & 1)).
+    const int dma_row = lane >> 3;
+    auto dma_piece = [&](int q) { return (uint32_t)((((lane & 7) ^ dma_row ^ (q & 1))) * 16); };
+    uint32_t bl_off[4];         // B_l: this wave fills rows 32w .. 32w+31 of the head's 128
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bl_off[q] = (uint32_t)((w * 32 + q * 8 + dma_row) * R * 2) + dma_piece(q);
+    auto dma_bl = [&](int c, __bf16* buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dma16(rb, reinterpret_cast<unsigned char*>(buf) + (w * 32 + q * 8) * kRowBytes, bl_off[q], (uint32_t)(c * kRowBytes));
+    };
+    unsigned char* const sa_w = sa + w * kABytes;     // this wave's A rows (bf16 factor)
+    auto dma_a = [&](int c) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            dma16(ra, sa_w + q * 8 * kRowBytes, (uint32_t)((q * 8 + dma_row) * R * 2) + dma_piece(q), (uint32_t)(c * kRowBytes));
+    };
+
+    // MFMA operand reads: lane (l16, g4) takes row l16 of a 16-row tile at
+    // logical piece 4 kk + g4, i.e. slot (4 kk + g4) ^ swz(l16).
+    const int xs = g4 ^ swz(l16);
+    const uint32_t rd_off[2] = {(uint32_t)(l16 * kRowBytes + xs * 16), (uint32_t)(l16 * kRowBytes + (xs ^ 4) * 16)};
+    auto lds16 = [&](const void* base, uint32_t off) {
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(base) + off));
+    };
+
+    using Frag = AFrag<ADT>;
+    uint32_t a_off[4];          // int8 factor: A fragments straight into registers
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) a_off[tt] = (uint32_t)(((tt * 16 + l16) * R + g4 * 8) * EA);
-    uint32_t b_off[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = tid + kThreads * q;
-        b_off[q] = (uint32_t)(((e >> 3) * R + (e & 7) * 8) * 2);
-    }
-
-    auto stage_bl = [&](int c, u32x4 (&reg)[4]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) reg[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[q] + c * kKc * 2, 0, 0);
-    };
-    auto store_bl = [&](int buf, const u32x4 (&reg)[4]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + kThreads * q, row = e >> 3, col = (e & 7) * 8;
-            *reinterpret_cast<u32x4*>(&stage[buf][row * kBlRow + col]) = reg[q];
-        }
-    };
-    using Frag = AFrag<ADT>;
     auto load_a = [&](int c, Frag (&af)[2][4]) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -208,53 +260,107 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    {
-        u32x4 pre[4];
-        stage_bl(0, pre);
-        store_bl(0, pre);
-    }
-    Frag afA[2][4], afB[2][4];
-    load_a(0, afA);
-    __syncthreads();
-
-    // One chunk: prefetch chunk c+1 (B_l to registers, A fragments into `nxt`),
-    // multiply chunk c from LDS and `cur`, then publish the prefetched B_l.
-    auto chunk = [&](int c, const Frag (&cur)[2][4], Frag (&nxt)[2][4]) {
-        const int cn = min(c + 1, n_chunks - 1);     // unconditional prefetch; the last chunk reloads itself
-        u32x4 pre[4];
-        stage_bl(cn, pre);
-        load_a(cn, nxt);
-        const __bf16* sb = stage[c & 1];
+    // 64 MFMAs of one rank chunk: B_l tiles from `sb`, the 4 token tiles in
+    // a8. Step s covers kk = s / 8, B_l tile s % 8; its fragment is read two
+    // steps ahead.
+    auto mma_chunk = [&](const __bf16* sb, const bf16x8 (&a8)[2][4]) {
+        auto rd = [&](int st) { return lds16(sb, rd_off[st >> 3] + (st & 7) * 16 * kRowBytes); };
+        bf16x8 bq[3];
+        bq[0] = rd(0);
+        bq[1] = rd(1);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 a8[4];
+        for (int st = 0; st < 16; ++st) {
+            if (st + 2 < 16) bq[(st + 2) % 3] = rd(st + 2);
+            const int kk = st >> 3, nt_ = st & 7;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) a8[tt] = cur[kk][tt].get();
-#pragma unroll
-            for (int nt_ = 0; nt_ < 8; ++nt_) {
-                const bf16x8 bf = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(sb + (nt_ * 16 + l16) * kBlRow + kk * 32 + g4 * 8));
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bf, a8[tt], acc[nt_][tt]);
-            }
+            for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bq[st % 3], a8[kk][tt], acc[nt_][tt]);
         }
-        store_bl((c + 1) & 1, pre);   // the other buffer: nobody reads it in this chunk
-        __syncthreads();
+        // Keep that order through scheduling: two reads, then (read, 4 MFMAs)
+        // fourteen times, then the last 8 MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int st = 0; st < 14; ++st) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
-    for (int c = 0; c < n_chunks; c += 2) {     // unrolled by two: the A registers ping-pong
-        chunk(c, afA, afB);
-        if (c + 1 < n_chunks) chunk(c + 1, afB, afA);
-    }
 
-    if (ADT == DT_I8) {           // per-row scale of the int8 factor, applied to column t
+    if constexpr (ADT == DT_BF16) {
+        // Per chunk c: read this wave's A fragments of c (copied during the
+        // previous chunk), start the copies of chunk c+1 (B_l into the other
+        // stage buffer, A into the now consumed region), run the MFMAs, then
+        // wait for the B_l copy only (the A copy stays in flight) and meet at
+        // the barrier.
+        dma_bl(0, stg0);
+        dma_a(0);
+        wait_vmcnt<8>();
+        barrier_lds();
+        auto chunk = [&](int c, const __bf16* cur, __bf16* nxt) {
+            bf16x8 a8[2][4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int tl = tt * 16 + l16;
-            const float s = tl < nt ? p.a_scale[a_row0 + tl] : 0.f;
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int nt_ = 0; nt_ < 8; ++nt_) acc[nt_][tt] *= s;
+                for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = lds16(sa_w, rd_off[kk] + tt * 16 * kRowBytes);
+            wait_lgkmcnt0();
+            if (c + 1 < n_chunks) {
+                dma_bl(c + 1, nxt);
+                dma_a(c + 1);
+            }
+            mma_chunk(cur, a8);
+            wait_vmcnt<8>();
+            barrier_lds();
+        };
+        for (int c = 0; c < n_chunks; c += 2) {     // static buffers: even chunks in stg0
+            chunk(c, stg0, stg1);
+            if (c + 1 < n_chunks) chunk(c + 1, stg1, stg0);
+        }
+    } else {
+        // int8 factor: A fragments ping-pong in registers, one chunk ahead.
+        dma_bl(0, stg0);
+        Frag afA[2][4], afB[2][4];
+        load_a(0, afA);
+        wait_vmcnt<8>();
+        barrier_lds();
+        auto chunk = [&](int c, const __bf16* cur, __bf16* nxt, const Frag (&fc)[2][4], Frag (&fn)[2][4]) {
+            const int cn = min(c + 1, n_chunks - 1);   // unconditional; the last chunk reloads itself
+            dma_bl(cn, nxt);
+            load_a(cn, fn);
+            bf16x8 a8[2][4];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = fc[kk][tt].get();
+            mma_chunk(cur, a8);
+            wait_vmcnt<8>();
+            barrier_lds();
+        };
+        for (int c = 0; c < n_chunks; c += 2) {
+            chunk(c, stg0, stg1, afA, afB);
+            if (c + 1 < n_chunks) chunk(c + 1, stg1, stg0, afB, afA);
         }
     }
+
+    // Tokens past the block's end contribute nothing: their K columns are set
+    // to zero whatever the factor rows there held.
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tl = tt * 16 + l16;
+        const float s = tl < nt ? (ADT == DT_I8 ? p.a_scale[a_row0 + tl] : 1.f) : 0.f;
+#pragma unroll
+        for (int nt_ = 0; nt_ < 8; ++nt_)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[nt_][tt][i] = tl < nt ? acc[nt_][tt][i] * s : 0.f;
+    }
+
+    // ---- stage the query rows of this head (rows >= G zero); sa is free now
+    for (int e = tid; e < 16 * kHeadDim; e += kThreads) {
+        const int j = e / kHeadDim, n = e % kHeadDim;
+        __bf16 v = (__bf16)0.0f;
+        if (j < G) v = static_cast<const __bf16*>(p.q)[((int64_t)b * p.n_q + h * G + j) * kHeadDim + n];
+        qs[j * kQRow + n] = v;
+    }
+    __syncthreads();
 
     // K as the A operand: kf[tt][s] holds n = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
     bf16x8 kf[4][4];
@@ -341,11 +447,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = tid + kThreads * q, row = e >> 4, col = (e & 15) * 8;
-            *reinterpret_cast<u32x4*>(&stage[buf][row * kWRow + col]) = reg[q];
+            *reinterpret_cast<u32x4*>((buf ? stg1 : stg0) + row * kWRow + col) = reg[q];
         }
     };
 
-    __shared__ float b1s[1024];          // hidden bias, zero when absent
     for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
     {
         u32x4 pre[4];
@@ -390,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     for (int fc = 0; fc < n_fchunks; ++fc) {
         u32x4 pre[4];
         stage_w(min(fc + 1, n_fchunks - 1), pre);   // unconditional; the last chunk reloads itself
-        const __bf16* sw = stage[fc & 1];
+        const __bf16* sw = (fc & 1) ? stg1 : stg0;
         const int f0 = fc * kFc;
         const bool gpart = f0 < H;
         // Z for one 16-feature tile; on the W1 part the accumulator starts at the bias.
