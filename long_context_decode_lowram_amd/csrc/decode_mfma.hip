@@ -146,24 +146,32 @@ template <> struct AFrag<DT_I8> {
 };
 
 // GELU(x) = x Phi(x) = max(x, 0) - |x| Q(|x|) with the normal tail
-// Q(a) = 1 - Phi(a). log2 Q on [0, 6] is a degree-7 polynomial in a fitted on
-// Chebyshev nodes; gelu_tail_fit.py derives the constants and bounds the
-// float32 evaluation: |error| < 7e-7 over the real line, far below the bf16
-// rounding the result goes through next. One exp2, no divide, no branch.
-__device__ __forceinline__ float gelu_tail(float x) {
-    constexpr float c0 = -0.9999943375587463f, c1 = -1.1512691974639893f, c2 = -0.45840978622436523f,
-                    c3 = -0.05402068793773651f, c4 = 0.00853946153074503f,
-                    c5 = -0.0009388679172843695f, c6 = 6.268139986786991e-05f,
-                    c7 = -1.8896262190537527e-06f;
-    const float a = fminf(fabsf(x), 6.0f);
-    float p = fmaf(c7, a, c6);
-    p = fmaf(p, a, c5);
-    p = fmaf(p, a, c4);
-    p = fmaf(p, a, c3);
-    p = fmaf(p, a, c2);
-    p = fmaf(p, a, c1);
-    p = fmaf(p, a, c0);
-    return fmaxf(x, 0.0f) - a * __builtin_amdgcn_exp2f(p);
+// Q(a) = 1 - Phi(a). log2 Q on [0, 6] is a degree-4 polynomial in a (a
+// weighted near-minimax fit; gelu_tail_fit.py derives the constants and
+// bounds the float32 evaluation: |error| < 7e-6 over the real line, far below
+// the bf16 rounding the result goes through next). One exp2, no divide, no
+// branch; the clamps are v_med3 (finite inputs), which needs none of the
+// quieting steps an IEEE min/max would add.
+__device__ __forceinline__ void gelu_tail16(f32x4 (&z)[4]) {
+    constexpr float c0 = -1.0004796981811523f, c1 = -1.1473716497421265f, c2 = -0.4680161774158478f,
+                    c3 = -0.04407823458313942f, c4 = 0.003866035956889391f;
+    // Sixteen independent chains, evaluated step by step so their latencies overlap.
+    float a[16], p[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] = __builtin_amdgcn_fmed3f(fabsf(z[k >> 2][k & 3]), 0.0f, 6.0f);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = fmaf(c4, a[k], c3);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = fmaf(p[k], a[k], c2);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = fmaf(p[k], a[k], c1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = fmaf(p[k], a[k], c0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = __builtin_amdgcn_exp2f(p[k]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        z[k >> 2][k & 3] = fmaf(-a[k], p[k], __builtin_amdgcn_fmed3f(z[k >> 2][k & 3], 0.0f, 3.0e38f));
 }
 
 }  // namespace
@@ -195,9 +203,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     __shared__ float mw[kWaves][kMaxG], lw[kWaves][kMaxG];
     __bf16* const qs = reinterpret_cast<__bf16*>(sa);                                  // [16][kQRow]
     float (*const pl)[kMaxG][kBlock] = reinterpret_cast<float (*)[kMaxG][kBlock]>(sa + 4352);   // softmax weights
-    float (*const oslot)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa + 12544);     // per-wave O chunk
+    // per-wave O of a feature chunk, two buffers; they reuse the space of qs
+    // and pl, which are dead by the feature loop
+    float (*const oslot0)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa);
+    float (*const oslot1)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa + 8192);
     float* const b1s = reinterpret_cast<float*>(sa + 20736);                           // [1024] hidden bias
-    static_assert(20736 + 4096 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352, "epilogue arrays overflow sa");
+    static_assert(20736 + 4096 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736,
+                  "epilogue arrays overflow sa");
 
     const int bi = split * kWaves + w;                 // this wave's attended-block index
     const bool active = bi < n_att;
@@ -451,14 +463,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         }
     };
 
-    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
-    {
-        u32x4 pre[4];
-        stage_w(0, pre);
-        store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
-    }
-    __syncthreads();
-
     // Residual rows of this block, weighted by P, for all d value features at
     // once: rv[ft][i] holds feature 16 ft + l16 of query head 4 g4 + i. Rows are
     // read eight at a time so their loads overlap.
@@ -492,6 +496,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             }
         }
     }
+    // The pre-pass above read only this wave's own softmax weights; after this
+    // barrier the query rows and the weights are dead, and their space holds
+    // the two per-wave O buffers of the feature loop.
+    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
+    {
+        u32x4 pre[4];
+        stage_w(0, pre);
+        store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
+    }
+    __syncthreads();
     for (int fc = 0; fc < n_fchunks; ++fc) {
         u32x4 pre[4];
         stage_w(min(fc + 1, n_fchunks - 1), pre);   // unconditional; the last chunk reloads itself
@@ -516,12 +530,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft) {
             if (ft + 1 < 4) ztile(ft + 1, zn);        // the next tile's MFMAs overlap this tile's GELU
-            if (gpart) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) zc[tt][i] = gelu_tail(zc[tt][i]);
-            }
+            if (gpart) gelu_tail16(zc);
             o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(zc[2 * u], zc[2 * u + 1]), o[ft]);
@@ -535,21 +544,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
             for (int ft = 0; ft < 4; ++ft) o[ft] += second ? rv[4 + ft] : rv[ft];
         }
+        float (*const os)[kMaxG][kFc] = (fc & 1) ? oslot1 : oslot0;
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * g4 + i;
-                if (j < G) oslot[w][j][ft * 16 + l16] = active ? o[ft][i] : 0.f;
+                if (j < G) os[w][j][ft * 16 + l16] = active ? o[ft][i] : 0.f;
             }
         store_w((fc + 1) & 1, pre);     // the other buffer: nobody reads it in this chunk
         __syncthreads();
+        // Sum the four waves' O in fixed order. The next write of this buffer
+        // comes two chunks later, after every wave has passed the next barrier.
         for (int e = tid; e < G * kFc; e += kThreads) {
             const int j = e / kFc, fl = e % kFc;
-            const float v = oslot[0][j][fl] + oslot[1][j][fl] + oslot[2][j][fl] + oslot[3][j][fl];
+            const float v = os[0][j][fl] + os[1][j][fl] + os[2][j][fl] + os[3][j][fl];
             rec0[j * rec_step + 2 + f0 + fl] = v;
         }
-        __syncthreads();
     }
 
     // ---- 5. record header and counts
