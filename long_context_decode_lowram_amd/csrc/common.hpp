@@ -44,6 +44,12 @@ template <> __device__ __forceinline__ void st<DT_BF16>(void* p, int64_t i, floa
     static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
 }
 
+// A raw buffer descriptor over [base, base + bytes): loads at offsets past
+// the end return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float gelu_erf(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }

@@ -84,10 +84,6 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v) {
     return r;
 }
 
-// A buffer descriptor over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima mean "no wait").
@@ -221,9 +217,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     constexpr int EA = ADT == DT_BF16 ? 2 : 1;   // bytes per A element
     const int64_t a_row0 = (int64_t)b * p.ctx_len + t0;
     const __amdgpu_buffer_rsrc_t ra =
-        rsrc(static_cast<const char*>(p.a) + a_row0 * R * EA, (uint32_t)(nt * R * EA));
+        buffer_rsrc(static_cast<const char*>(p.a) + a_row0 * R * EA, (uint32_t)(nt * R * EA));
     const __amdgpu_buffer_rsrc_t rb =
-        rsrc(static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R,
+        buffer_rsrc(static_cast<const __bf16*>(p.b_l) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)R,
              (uint32_t)(kHeadDim * R * 2));
     const int n_chunks = R / kKc;
 

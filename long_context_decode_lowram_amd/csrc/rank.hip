@@ -17,70 +17,113 @@ template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
 
-template <int DT> __device__ __forceinline__ double ld64(const void* base, int64_t i);
-template <> __device__ __forceinline__ double ld64<DT_F32>(const void* base, int64_t i) {
-    return static_cast<double>(static_cast<const float*>(base)[i]);
-}
-template <> __device__ __forceinline__ double ld64<DT_BF16>(const void* base, int64_t i) {
-    return static_cast<double>(bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]));
-}
 }  // namespace
 
-// One wave per workgroup; each iteration stages 64 consecutive rows of V and
-// V_hat through LDS with 16-byte coalesced loads, then lane l sums row l in
-// index order. Rows are (slice, token, head) in storage order; the error
-// goes to err[slice, head, token].
+// Element k of a staged 16-byte piece as binary64 (exact widening).
+template <int DT> __device__ __forceinline__ double piece_elem(const uint4& u, int k);
+template <> __device__ __forceinline__ double piece_elem<DT_F32>(const uint4& u, int k) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    return static_cast<double>(__uint_as_float(w[k]));
+}
+template <> __device__ __forceinline__ double piece_elem<DT_BF16>(const uint4& u, int k) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t x = w[k >> 1];
+    return static_cast<double>(__uint_as_float((k & 1) ? (x & 0xffff0000u) : (x << 16)));
+}
+
+// One wave per workgroup. A batch is 64 consecutive rows of V and V_hat;
+// lane l sums row l in index order. Rows go through LDS one 128-byte segment
+// at a time (64 rows x 128 bytes per tensor, coalesced 16-byte loads), which
+// keeps the LDS footprint at 18 KB so two waves share each SIMD and hide the
+// latency of the sequential binary64 chain. Two segments are in flight in
+// registers (buffer loads: pieces past the last row read as zero) while one
+// is summed. Rows are (slice, token, head) in storage order; the error goes to
+// err[slice, head, token].
 template <int DT>
-__global__ __launch_bounds__(64) void rank_error_kernel(RankParams p, int64_t n_rows) {
+__global__ __launch_bounds__(64, 2) void rank_error_kernel(RankParams p, int64_t n_rows) {
     constexpr int RB = kHeadDim * Elem<DT>::bytes;   // bytes per row
-    constexpr int LS = RB + 16;                      // padded LDS row stride
-    constexpr int PER_LANE = RB / 16;                // 16-byte pieces per lane per tensor
+    constexpr int SEG = 128;                         // bytes per row segment
+    constexpr int NSEG = RB / SEG;                   // 2 (bf16) or 4 (f32)
+    constexpr int LS = SEG + 16;                     // padded LDS row stride
+    constexpr int PIECES = kRows * SEG / (kWave * 16);   // 16-byte pieces per lane per tensor: 8
+    constexpr int EPP = 16 / Elem<DT>::bytes;        // elements per piece
     __shared__ __attribute__((aligned(16))) unsigned char sv[kRows * LS];
     __shared__ __attribute__((aligned(16))) unsigned char sh[kRows * LS];
     const int lane = threadIdx.x;
     const int64_t n_batches = (n_rows + kRows - 1) / kRows;
+    const int64_t g = gridDim.x;
+    const int64_t my_batches = blockIdx.x < n_batches ? (n_batches - 1 - blockIdx.x) / g + 1 : 0;
+    const int64_t n_items = my_batches * NSEG;       // (batch, segment) pairs of this wave
     const unsigned char* gv = static_cast<const unsigned char*>(p.v);
     const unsigned char* gh = static_cast<const unsigned char*>(p.v_hat);
-    for (int64_t bt = blockIdx.x; bt < n_batches; bt += gridDim.x) {
-        const int64_t row0 = bt * kRows;
-        const int64_t byte0 = row0 * RB;
-        const int64_t bytes_left = (n_rows - row0) * RB;
-        uint4 rv[PER_LANE], rh[PER_LANE];
+    // Piece c of this lane: row (c*64 + lane) / 8, 16-byte column (c*64 + lane) % 8.
+    auto load = [&](int64_t it, uint4 (&rv)[PIECES], uint4 (&rh)[PIECES]) {
+        const int64_t bt = blockIdx.x + (it / NSEG) * g;
+        const int sg = (int)(it % NSEG);
+        const int64_t byte0 = bt * kRows * RB;
+        const int64_t left = (n_rows - bt * kRows) * RB;
+        const uint32_t nbytes = (uint32_t)(left < kRows * RB ? left : kRows * RB);
+        const __amdgpu_buffer_rsrc_t bv = buffer_rsrc(gv + byte0, nbytes);
+        const __amdgpu_buffer_rsrc_t bh = buffer_rsrc(gh + byte0, nbytes);
 #pragma unroll
-        for (int c = 0; c < PER_LANE; ++c) {
-            const int64_t off = (int64_t)(c * kWave + lane) * 16;
-            if (off < bytes_left) {
-                rv[c] = *reinterpret_cast<const uint4*>(gv + byte0 + off);
-                rh[c] = *reinterpret_cast<const uint4*>(gh + byte0 + off);
-            } else {
-                rv[c] = make_uint4(0, 0, 0, 0);
-                rh[c] = make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < PIECES; ++c) {
+            const int q = c * kWave + lane;
+            const uint32_t off = (uint32_t)((q >> 3) * RB + sg * SEG + (q & 7) * 16);
+            rv[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bv, off, 0, 0));
+            rh[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bh, off, 0, 0));
+        }
+    };
+    auto stage = [&](const uint4 (&rv)[PIECES], const uint4 (&rh)[PIECES]) {
+#pragma unroll
+        for (int c = 0; c < PIECES; ++c) {
+            const int q = c * kWave + lane;
+            *reinterpret_cast<uint4*>(sv + (q >> 3) * LS + (q & 7) * 16) = rv[c];
+            *reinterpret_cast<uint4*>(sh + (q >> 3) * LS + (q & 7) * 16) = rh[c];
+        }
+    };
+    double e = 0.0;
+    // Continue row `lane`'s sum over the staged segment; after the last
+    // segment of a batch, store it.
+    auto consume = [&](int64_t it) {
+        const int sg = (int)(it % NSEG);
+        if (sg == 0) e = 0.0;
+#pragma unroll 2
+        for (int c = 0; c < SEG / 16; ++c) {
+            const uint4 uv = *reinterpret_cast<const uint4*>(sv + lane * LS + c * 16);
+            const uint4 uh = *reinterpret_cast<const uint4*>(sh + lane * LS + c * 16);
+            double sq[EPP];
+#pragma unroll
+            for (int k = 0; k < EPP; ++k) {
+                const double dlt = piece_elem<DT>(uv, k) - piece_elem<DT>(uh, k);
+                sq[k] = dlt * dlt;
+            }
+#pragma unroll
+            for (int k = 0; k < EPP; ++k) e = e + sq[k];
+        }
+        if (sg == NSEG - 1) {
+            const int64_t row = (blockIdx.x + (it / NSEG) * g) * kRows + lane;
+            if (row < n_rows) {
+                const int64_t per_slice = (int64_t)p.ctx_len * p.n_kv;
+                const int64_t sl = row / per_slice, rem = row % per_slice;
+                const int64_t t = rem / p.n_kv, h = rem % p.n_kv;
+                p.err[(sl * p.n_kv + h) * p.ctx_len + t] = e;
             }
         }
-#pragma unroll
-        for (int c = 0; c < PER_LANE; ++c) {
-            const int off = (c * kWave + lane) * 16;
-            const int r = off / RB, col = off % RB;
-            *reinterpret_cast<uint4*>(sv + r * LS + col) = rv[c];
-            *reinterpret_cast<uint4*>(sh + r * LS + col) = rh[c];
-        }
+    };
+    uint4 av[PIECES], ah[PIECES], bv[PIECES], bh[PIECES];
+    if (n_items > 0) load(0, av, ah);
+    if (n_items > 1) load(1, bv, bh);
+    for (int64_t it = 0; it < n_items; it += 2) {     // two register sets with fixed roles
+        stage(av, ah);
         __syncthreads();
-        const int64_t row = row0 + lane;
-        if (row < n_rows) {
-            double e = 0.0;
-            const void* pv = sv + lane * LS;
-            const void* ph = sh + lane * LS;
-#pragma unroll 8
-            for (int i = 0; i < kHeadDim; ++i) {
-                const double dlt = ld64<DT>(pv, i) - ld64<DT>(ph, i);
-                const double sq = dlt * dlt;
-                e = e + sq;
-            }
-            const int64_t per_slice = (int64_t)p.ctx_len * p.n_kv;
-            const int64_t sl = row / per_slice, rem = row % per_slice;
-            const int64_t t = rem / p.n_kv, h = rem % p.n_kv;
-            p.err[(sl * p.n_kv + h) * p.ctx_len + t] = e;
-        }
+        if (it + 2 < n_items) load(it + 2, av, ah);
+        consume(it);
+        __syncthreads();
+        if (it + 1 >= n_items) break;
+        stage(bv, bh);
+        __syncthreads();
+        if (it + 3 < n_items) load(it + 3, bv, bh);
+        consume(it + 1);
         __syncthreads();
     }
 }
@@ -88,7 +131,7 @@ __global__ __launch_bounds__(64) void rank_error_kernel(RankParams p, int64_t n_
 hipError_t launch_rank_error(const RankParams& p, hipStream_t s) {
     const int64_t n_rows = (int64_t)p.n_slices * p.ctx_len * p.n_kv;
     const int64_t n_batches = (n_rows + kRows - 1) / kRows;
-    const int grid = (int)(n_batches < 256 * 16 ? n_batches : 256 * 16);
+    const int grid = (int)(n_batches < 256 * 8 ? n_batches : 256 * 8);   // one resident wave per slot: 8 per CU
     if (p.in_dtype == DT_F32)
         hipLaunchKernelGGL(rank_error_kernel<DT_F32>, dim3(grid), dim3(64), 0, s, p, n_rows);
     else
@@ -218,57 +261,101 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
     return f32_to_bf16_bits(f);
 }
 
-// One wave per stored residual: R = V - V_hat at the chosen token, exact in
-// binary64, then encoded. Lane l owns elements 2l and 2l+1.
-template <int IDT, int RDT>
-__global__ __launch_bounds__(256) void rank_gather_kernel(RankParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t n_slots = (int64_t)p.n_slices * p.n_kv * p.n_res;
-    if (gid >= n_slots) return;
-    const int64_t seg = gid / p.n_res;
-    const int64_t sl = seg / p.n_kv, h = seg % p.n_kv;
-    int t = p.res_idx[gid];
-    t = t < 0 ? 0 : (t >= p.ctx_len ? p.ctx_len - 1 : t);
-    const int64_t row = ((sl * p.ctx_len + t) * p.n_kv + h) * kHeadDim;
-    const double d0 = ld64<IDT>(p.v, row + 2 * lane) - ld64<IDT>(p.v_hat, row + 2 * lane);
-    const double d1 = ld64<IDT>(p.v, row + 2 * lane + 1) - ld64<IDT>(p.v_hat, row + 2 * lane + 1);
-    const int64_t o = gid * kHeadDim + 2 * lane;
-    if (RDT == DT_F32) {
-        static_cast<float*>(p.res_val)[o] = static_cast<float>(d0);
-        static_cast<float*>(p.res_val)[o + 1] = static_cast<float>(d1);
-    } else if (RDT == DT_BF16) {
-        static_cast<uint16_t*>(p.res_val)[o] = f64_to_bf16_bits(d0);
-        static_cast<uint16_t*>(p.res_val)[o + 1] = f64_to_bf16_bits(d1);
+// Sixteen lanes per stored residual: lane j of a group owns elements
+// 8j .. 8j+7 of the row (16-byte loads of bf16, 32 of f32). R = V - V_hat at
+// the chosen token, exact in binary64, then encoded. A wave holds four
+// groups and takes two slots per group per iteration (eight rows' loads in
+// flight), walking the slots with a grid stride.
+template <int IDT>
+__device__ __forceinline__ void load_row8(const void* base, int64_t e0, double (&d)[8], const void* base_h) {
+    if (IDT == DT_BF16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base_h) + e0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = piece_elem<DT_BF16>(u, k) - piece_elem<DT_BF16>(w, k);
     } else {
-        double amax = fmax(fabs(d0), fabs(d1));
-        for (int off = 32; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off, kWave));
+        const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e0);
+        const uint4* ph = reinterpret_cast<const uint4*>(static_cast<const float*>(base_h) + e0);
+        const uint4 u0 = pv[0], u1 = pv[1], w0 = ph[0], w1 = ph[1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            d[k] = piece_elem<DT_F32>(u0, k) - piece_elem<DT_F32>(w0, k);
+            d[4 + k] = piece_elem<DT_F32>(u1, k) - piece_elem<DT_F32>(w1, k);
+        }
+    }
+}
+
+template <int RDT>
+__device__ __forceinline__ void store_res8(const RankParams& p, int64_t gid, int j, const double (&d)[8]) {
+    const int64_t o = gid * kHeadDim + 8 * j;
+    if (RDT == DT_F32) {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.res_val) + o);
+        dst[0] = make_float4((float)d[0], (float)d[1], (float)d[2], (float)d[3]);
+        dst[1] = make_float4((float)d[4], (float)d[5], (float)d[6], (float)d[7]);
+    } else if (RDT == DT_BF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)f64_to_bf16_bits(d[2 * k]) | ((uint32_t)f64_to_bf16_bits(d[2 * k + 1]) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.res_val) + o) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        double amax = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmax(amax, fabs(d[k]));
+        for (int off = 8; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off, kWave));
         const float s = static_cast<float>(amax / 127.0);
         const double s64 = static_cast<double>(s);
-        auto code = [&](double dv) -> int8_t {
-            if (!(s64 > 0.0)) return 0;
-            double q = rint(dv / s64);
-            q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
-            return static_cast<int8_t>(q);
-        };
-        static_cast<int8_t*>(p.res_val)[o] = code(d0);
-        static_cast<int8_t*>(p.res_val)[o + 1] = code(d1);
-        if (lane == 0) p.res_scale[gid] = s;
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            int8_t c = 0;
+            if (s64 > 0.0) {
+                double q = rint(d[k] / s64);
+                q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+                c = static_cast<int8_t>(q);
+            }
+            w[k >> 2] |= (uint32_t)(uint8_t)c << (8 * (k & 3));
+        }
+        *reinterpret_cast<uint2*>(static_cast<int8_t*>(p.res_val) + o) = make_uint2(w[0], w[1]);
+        if (j == 0) p.res_scale[gid] = s;
+    }
+}
+
+template <int IDT, int RDT>
+__global__ __launch_bounds__(256) void rank_gather_kernel(RankParams p, int64_t n_slots) {
+    const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
+    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t stride = (int64_t)gridDim.x * 4 * 8;     // slots per grid step
+    auto row_of = [&](int64_t gid) {
+        const int64_t seg = gid / p.n_res;
+        const int64_t sl = seg / p.n_kv, h = seg % p.n_kv;
+        int t = p.res_idx[gid];
+        t = t < 0 ? 0 : (t >= p.ctx_len ? p.ctx_len - 1 : t);
+        return ((sl * p.ctx_len + t) * p.n_kv + h) * kHeadDim + 8 * j;
+    };
+    for (int64_t base = wave * 8; base < n_slots; base += stride) {
+        const int64_t g0 = base + grp, g1 = base + 4 + grp;    // a group's two slots (uniform per group)
+        double d0[8], d1[8];
+        if (g0 < n_slots) load_row8<IDT>(p.v, row_of(g0), d0, p.v_hat);
+        if (g1 < n_slots) load_row8<IDT>(p.v, row_of(g1), d1, p.v_hat);
+        if (g0 < n_slots) store_res8<RDT>(p, g0, j, d0);
+        if (g1 < n_slots) store_res8<RDT>(p, g1, j, d1);
     }
 }
 
 hipError_t launch_rank_gather(const RankParams& p, hipStream_t s) {
     const int64_t n_slots = (int64_t)p.n_slices * p.n_kv * p.n_res;
     if (n_slots == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n_slots + 3) / 4));
+    const int64_t want = (n_slots + 31) / 32;                 // one step per workgroup covers 32 slots
+    const dim3 grid((unsigned)(want < 8192 ? want : 8192));
     if (p.in_dtype == DT_F32) {
-        if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_F32>), grid, dim3(256), 0, s, p);
-        else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_BF16>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_I8>), grid, dim3(256), 0, s, p);
+        if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_F32>), grid, dim3(256), 0, s, p, n_slots);
+        else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_BF16>), grid, dim3(256), 0, s, p, n_slots);
+        else hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
     } else {
-        if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_F32>), grid, dim3(256), 0, s, p);
-        else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_BF16>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_I8>), grid, dim3(256), 0, s, p);
+        if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_F32>), grid, dim3(256), 0, s, p, n_slots);
+        else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_BF16>), grid, dim3(256), 0, s, p, n_slots);
+        else hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
     }
     return hipGetLastError();
 }
