@@ -139,57 +139,118 @@ hipError_t launch_rank_error(const RankParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Exact k-th largest key per (slice, head) by an 8-pass radix select on the
-// binary64 bit patterns (non-negative doubles order like their bits). It
-// leaves the threshold key and how many tokens equal to it are taken
-// (lowest indices first).
+// Exact k-th largest key per (slice, head) by radix select on the binary64
+// bit patterns (non-negative doubles order like their bits). It leaves the
+// threshold key and how many tokens equal to it are taken (lowest indices
+// first).
+//   1. One pass finds the smallest and largest key; the bits they share are
+//      shared by every key, so the digits start below them (errors span a few
+//      dozen binades: the top exponent bits carry no information and would
+//      pile every key into one bin).
+//   2. Passes over 11-bit digits with a private histogram per wave, a block
+//      scan from the top bin, and the bin holding the k-th key.
+//   3. Once that bin holds at most kCand keys, they are copied to LDS and the
+//      remaining digits are resolved there.
+namespace {
+constexpr int kDigit = 11, kBins = 1 << kDigit, kSelWaves = 16, kCand = 2048;
+}
+
 __global__ __launch_bounds__(1024) void rank_select_kernel(RankParams p) {
-    const int seg = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
+    const int seg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long* keys =
         reinterpret_cast<const unsigned long long*>(p.err) + (int64_t)seg * p.ctx_len;
-    __shared__ unsigned int hist[16][256];
-    __shared__ unsigned long long s_prefix;
-    __shared__ int s_krem;
+    __shared__ unsigned int hist[kSelWaves][kBins];           // 128 KB
+    __shared__ unsigned long long cand[kCand];                // 16 KB
+    __shared__ unsigned long long red_lo[kSelWaves], red_hi[kSelWaves];
+    __shared__ unsigned int wtot[kSelWaves];
+    __shared__ unsigned int s_bin, s_above, s_cnt, s_ncand;
     if (p.n_res == 0) {
         if (tid == 0) { p.thr[seg] = ~0ull; p.n_eq[seg] = 0; }
         return;
     }
-    unsigned long long prefix = 0, mask = 0;
-    int krem = p.n_res;
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
-        for (int e = tid; e < 16 * 256; e += 1024) (&hist[0][0])[e] = 0;
-        __syncthreads();
-        for (int t = tid; t < p.ctx_len; t += 1024) {
-            const unsigned long long key = keys[t];
-            if ((key & mask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid < 256) {
-            unsigned int c = 0;
-            for (int i = 0; i < 16; ++i) c += hist[i][tid];
-            hist[0][tid] = c;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int cum = 0;
-            for (int d = 255; d >= 0; --d) {
-                const int c = (int)hist[0][d];
-                if (cum + c >= krem) {
-                    s_prefix = prefix | ((unsigned long long)d << shift);
-                    s_krem = krem - cum;
-                    break;
-                }
-                cum += c;
+    // f(key) for every key of src[0, n); eight loads per thread in flight.
+    auto for_keys = [&](const unsigned long long* src, int n, auto&& f) {
+        for (int t0 = 0; t0 < n; t0 += 8 * 1024) {
+            unsigned long long kk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + j * 1024 + tid;
+                kk[j] = t < n ? src[t] : 0ull;
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + j * 1024 + tid < n) f(kk[j]);
         }
+    };
+    // 1. common leading bits of all keys
+    unsigned long long lo = ~0ull, hi = 0ull;
+    for_keys(keys, p.ctx_len, [&](unsigned long long k) {
+        lo = k < lo ? k : lo;
+        hi = k > hi ? k : hi;
+    });
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long l2 = __shfl_xor(lo, o, kWave), h2 = __shfl_xor(hi, o, kWave);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+    }
+    if (lane == 0) { red_lo[w] = lo; red_hi[w] = hi; }
+    __syncthreads();
+    lo = red_lo[0]; hi = red_hi[0];
+    for (int i = 1; i < kSelWaves; ++i) {
+        lo = red_lo[i] < lo ? red_lo[i] : lo;
+        hi = red_hi[i] > hi ? red_hi[i] : hi;
+    }
+    int shift = lo == hi ? 0 : 64 - __clzll(lo ^ hi);        // bits still undecided
+    unsigned long long mask = shift == 64 ? 0ull : (~0ull << shift);
+    unsigned long long prefix = lo & mask;
+    unsigned int krem = (unsigned int)p.n_res;
+
+    // 2./3. digit passes over the global keys, then over the LDS candidates
+    const unsigned long long* src = keys;
+    int n_src = p.ctx_len;
+    while (shift > 0) {
+        const int d = shift < kDigit ? shift : kDigit;
+        shift -= d;
+        for (int e = tid; e < kSelWaves * kBins; e += 1024) (&hist[0][0])[e] = 0u;
         __syncthreads();
-        prefix = s_prefix;
-        krem = s_krem;
-        mask |= 0xffull << shift;
+        for_keys(src, n_src, [&](unsigned long long k) {
+            if ((k & mask) == prefix) atomicAdd(&hist[w][(unsigned)(k >> shift) & (kBins - 1)], 1u);
+        });
+        __syncthreads();
+        // Thread t owns bins 2047-2t and 2046-2t (descending order); sum the
+        // wave copies, then an exclusive scan gives the count above each bin.
+        const int b0 = kBins - 1 - 2 * tid, b1 = b0 - 1;
+        unsigned int c0 = 0, c1 = 0;
+        for (int i = 0; i < kSelWaves; ++i) { c0 += hist[i][b0]; c1 += hist[i][b1]; }
+        unsigned int incl = c0 + c1;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const unsigned int v = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += v;
+        }
+        if (lane == kWave - 1) wtot[w] = incl;
+        __syncthreads();
+        unsigned int above = incl - (c0 + c1);
+        for (int i = 0; i < w; ++i) above += wtot[i];
+        if (above < krem && krem <= above + c0) { s_bin = b0; s_above = above; s_cnt = c0; }
+        else if (above + c0 < krem && krem <= above + c0 + c1) { s_bin = b1; s_above = above + c0; s_cnt = c1; }
+        __syncthreads();
+        const unsigned int bin = s_bin, cnt = s_cnt;
+        krem -= s_above;
+        prefix |= (unsigned long long)bin << shift;
+        mask |= (unsigned long long)(kBins - 1 >> (kDigit - d)) << shift;
+        if (shift > 0 && src == keys && cnt <= (unsigned)kCand) {
+            if (tid == 0) s_ncand = 0;
+            __syncthreads();
+            for_keys(keys, n_src, [&](unsigned long long k) {
+                if ((k & mask) == prefix) cand[atomicAdd(&s_ncand, 1u)] = k;
+            });
+            __syncthreads();
+            src = cand;
+            n_src = (int)s_ncand;
+        }
         __syncthreads();
     }
-    if (tid == 0) { p.thr[seg] = prefix; p.n_eq[seg] = krem; }
+    if (tid == 0) { p.thr[seg] = prefix; p.n_eq[seg] = (int)krem; }
 }
 
 hipError_t launch_rank_select(const RankParams& p, hipStream_t s) {
@@ -199,44 +260,79 @@ hipError_t launch_rank_select(const RankParams& p, hipStream_t s) {
 
 // Ordered compaction per (slice, head): token t is taken when its key is above
 // the threshold, or equal to it and among the first n_eq such tokens. Slots
-// follow ascending t; ptr[i] counts taken tokens below 64*i.
+// follow ascending t; ptr[i] counts taken tokens below 64*i. Each thread
+// takes 8 consecutive tokens per step (8192 per workgroup step); a block
+// scan of the per-thread counts orders them.
+__device__ __forceinline__ unsigned int block_excl_scan_1024(unsigned int v, unsigned int* wtot, unsigned int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    unsigned int incl = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned int u = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += u;
+    }
+    if (lane == kWave - 1) wtot[w] = incl;
+    __syncthreads();
+    unsigned int before = incl - v;
+    total = 0;
+    for (int i = 0; i < 16; ++i) {
+        if (i < w) before += wtot[i];
+        total += wtot[i];
+    }
+    __syncthreads();
+    return before;
+}
+
 __global__ __launch_bounds__(1024) void rank_compact_kernel(RankParams p) {
-    const int seg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int seg = blockIdx.x, tid = threadIdx.x;
     const unsigned long long* keys =
         reinterpret_cast<const unsigned long long*>(p.err) + (int64_t)seg * p.ctx_len;
     const unsigned long long thr = p.thr[seg];
-    const int neq = p.n_eq[seg];
-    __shared__ int wsel[16], weq[16];
-    int run_sel = 0, run_eq = 0;
+    const unsigned int neq = (unsigned int)p.n_eq[seg];
+    __shared__ unsigned int wtot[16];
+    unsigned int run_sel = 0, run_eq = 0;
     int32_t* idx = p.res_idx + (int64_t)seg * p.n_res;
     int32_t* ptr = p.res_ptr + (int64_t)seg * (p.n_blocks + 1);
-    const unsigned long long lt_mask = (1ull << lane) - 1ull;
-    for (int c0 = 0; c0 < p.ctx_len; c0 += 1024) {
-        const int t = c0 + tid;
-        const bool valid = t < p.ctx_len;
-        const unsigned long long key = valid ? keys[t] : 0ull;
-        const bool gt = valid && key > thr;
-        const bool eq = valid && key == thr && p.n_res > 0;
-        const unsigned long long meq = __ballot(eq);
-        if (lane == 0) weq[w] = __popcll(meq);
-        __syncthreads();
-        int off_eq = 0, tot_eq = 0;
-        for (int i = 0; i < 16; ++i) { tot_eq += weq[i]; if (i < w) off_eq += weq[i]; }
-        const bool take = eq && (run_eq + off_eq + __popcll(meq & lt_mask) < neq);
-        const bool sel = gt || take;
-        const unsigned long long msel = __ballot(sel);
-        if (lane == 0) wsel[w] = __popcll(msel);
-        __syncthreads();
-        int off_sel = 0, tot_sel = 0;
-        for (int i = 0; i < 16; ++i) { tot_sel += wsel[i]; if (i < w) off_sel += wsel[i]; }
-        const int before = run_sel + off_sel + __popcll(msel & lt_mask);
-        if (sel && before < p.n_res) idx[before] = t;
-        if (valid && (t % kBlock) == 0) ptr[t / kBlock] = before;
+    for (int t0 = 0; t0 < p.ctx_len; t0 += 8 * 1024) {
+        const int tb = t0 + 8 * tid;
+        unsigned long long kk[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kk[j] = tb + j < p.ctx_len ? keys[tb + j] : 0ull;
+        unsigned int n_gt = 0, n_eq = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool valid = tb + j < p.ctx_len;
+            n_gt += valid && kk[j] > thr;
+            n_eq += valid && kk[j] == thr && p.n_res > 0;
+        }
+        unsigned int tot_eq;
+        unsigned int eq_before = run_eq + block_excl_scan_1024(n_eq, wtot, tot_eq);
+        // taken tokens of this thread: all above, and the equal ones still within n_eq
+        unsigned int n_take = n_gt;
+        {
+            unsigned int e = eq_before;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (tb + j < p.ctx_len && kk[j] == thr && p.n_res > 0) { n_take += e < neq; ++e; }
+        }
+        unsigned int tot_sel;
+        unsigned int before = run_sel + block_excl_scan_1024(n_take, wtot, tot_sel);
+        unsigned int e = eq_before;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = tb + j;
+            if (t >= p.ctx_len) break;
+            if (t % kBlock == 0) ptr[t / kBlock] = (int32_t)before;
+            bool take = kk[j] > thr;
+            if (kk[j] == thr && p.n_res > 0) { take = e < neq; ++e; }
+            if (take) {
+                if (before < (unsigned int)p.n_res) idx[before] = t;
+                ++before;
+            }
+        }
         run_sel += tot_sel;
         run_eq += tot_eq;
-        __syncthreads();
     }
-    if (tid == 0) ptr[p.n_blocks] = run_sel < p.n_res ? run_sel : p.n_res;
+    if (tid == 0) ptr[p.n_blocks] = run_sel < (unsigned int)p.n_res ? (int32_t)run_sel : p.n_res;
 }
 
 hipError_t launch_rank_compact(const RankParams& p, hipStream_t s) {
