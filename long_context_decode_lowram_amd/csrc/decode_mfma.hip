@@ -42,14 +42,13 @@ constexpr int kWaves = 4;                 // blocks per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kKc = 64;                   // rank columns per staged B_l chunk
 constexpr int kFc = 64;                   // features per staged weight chunk
-constexpr int kWRow = kHeadDim + 8;       // padded LDS row of a weight chunk
 constexpr int kRowBytes = kKc * 2;        // one bf16 row of a rank chunk: 128 bytes, eight 16-byte pieces
-constexpr int kStage = kFc * kWRow;       // elements per stage buffer: a padded weight chunk
+constexpr int kStage = kFc * kHeadDim;    // elements per stage buffer: a weight chunk (= a B_l chunk)
 constexpr int kQRow = kHeadDim + 8;
 constexpr int kMaxG = 8;
 constexpr int kXcd = 8;                   // XCDs on MI355X; workgroups go round-robin over them
 constexpr int kABytes = kBlock * kRowBytes;   // one wave's A rows of a rank chunk: 8 KB
-static_assert(128 * kRowBytes <= kStage * 2, "stage buffer too small for a B_l chunk");
+static_assert(128 * kRowBytes == kStage * 2, "a stage buffer holds one B_l chunk or one weight chunk");
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -452,11 +451,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             reg[q] = *reinterpret_cast<const u32x4*>(src + col);
         }
     };
+    // Weight chunks in LDS: 256-byte rows (one feature) of sixteen 16-byte
+    // pieces. Piece 4s + g holds the elements the MFMA lane group g needs for
+    // k-group s: 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3), matching the
+    // k-slots of kf. Piece P of row f sits in slot P ^ (f & 15), so a wave's
+    // reads of one piece from 16 consecutive rows are conflict-free. A 16-byte
+    // global chunk c (elements 8c .. 8c+7) fills the half (c / 2) & 1 of two
+    // pieces.
     auto store_w = [&](int buf, const u32x4 (&reg)[4]) {
+        unsigned char* base = reinterpret_cast<unsigned char*>(buf ? stg1 : stg0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = tid + kThreads * q, row = e >> 4, col = (e & 15) * 8;
-            *reinterpret_cast<u32x4*>((buf ? stg1 : stg0) + row * kWRow + col) = reg[q];
+            const int e = tid + kThreads * q, row = e >> 4, c = e & 15;
+            const int sg = c >> 2, j = c & 3, g0 = (j & 1) * 2, half = j >> 1;
+            unsigned char* r0 = base + row * 256 + half * 8;
+            *reinterpret_cast<u32x2*>(r0 + (((4 * sg + g0) ^ (row & 15)) * 16)) = u32x2{reg[q][0], reg[q][1]};
+            *reinterpret_cast<u32x2*>(r0 + (((4 * sg + g0 + 1) ^ (row & 15)) * 16)) = u32x2{reg[q][2], reg[q][3]};
         }
     };
 
@@ -513,7 +523,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         auto ztile = [&](int ft, f32x4 (&z)[4]) {
             bf16x8 wf[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wf[s] = lds_pair(sw + (ft * 16 + l16) * kWRow, 32 * s + 4 * g4);
+            for (int s = 0; s < 4; ++s)
+                wf[s] = lds16(sw, (uint32_t)((ft * 16 + l16) * 256 + (((4 * s + g4) ^ l16) * 16)));
             const float bb = gpart ? b1s[f0 + ft * 16 + l16] : 0.f;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
