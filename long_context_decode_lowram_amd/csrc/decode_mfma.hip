@@ -191,12 +191,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int G = p.group, H = p.hidden, R = p.rank;
 
     // LDS: two stage buffers (B_l rank chunks in the main loop, weight chunks
-    // after it) and one region that holds each wave's A rows in the main loop
-    // and the epilogue's small arrays after it. Separate objects, so the
-    // compiler's waits for direct-to-LDS loads stay per buffer.
+    // after it), one region that holds each wave's A rows in the main loop
+    // and the epilogue's small arrays after it, and each wave's 4 KB of
+    // residual rows. Separate objects, so the compiler's waits for
+    // direct-to-LDS loads can stay per buffer. 80 KB: two workgroups per CU.
     __shared__ __attribute__((aligned(16))) __bf16 stg0[kStage], stg1[kStage];
     __shared__ __attribute__((aligned(16))) unsigned char sa[kWaves * kABytes];
-    __shared__ float mw[kWaves][kMaxG], lw[kWaves][kMaxG];
+    __shared__ __attribute__((aligned(16))) unsigned char sres[kWaves * 4096];
     __bf16* const qs = reinterpret_cast<__bf16*>(sa);                                  // [16][kQRow]
     float (*const pl)[kMaxG][kBlock] = reinterpret_cast<float (*)[kMaxG][kBlock]>(sa + 4352);   // softmax weights
     // per-wave O of a feature chunk, two buffers; they reuse the space of qs
@@ -204,7 +205,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     float (*const oslot0)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa);
     float (*const oslot1)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa + 8192);
     float* const b1s = reinterpret_cast<float*>(sa + 20736);                           // [1024] hidden bias
-    static_assert(20736 + 4096 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736,
+    float (*const mw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(sa + 24832);         // per-wave score max
+    float (*const lw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(sa + 24960);         // per-wave weight sum
+    int* const cnt_tok = reinterpret_cast<int*>(sa + 25088);
+    int* const cnt_res = reinterpret_cast<int*>(sa + 25104);
+    static_assert(25120 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736,
                   "epilogue arrays overflow sa");
 
     const int bi = split * kWaves + w;                 // this wave's attended-block index
@@ -212,6 +217,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int blk = active ? p.att_list[(int64_t)b * p.n_blocks + bi] : 0;
     const int t0 = blk * kBlock;
     const int nt = active ? min(kBlock, p.ctx_len - t0) : 0;
+
+    // Residual slots lo .. hi-1 of this wave's block (wave-uniform).
+    const int64_t res_row = ((int64_t)b * p.n_kv + h) * p.n_res;
+    int lo = 0, hi = 0;
+    if (active) {
+        const int64_t pr = ((int64_t)b * p.n_kv + h) * (p.n_blocks + 1) + blk;
+        lo = max(0, min(p.res_ptr[pr], p.n_res));
+        hi = max(lo, min(p.res_ptr[pr + 1], p.n_res));
+    }
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    // The block's residual rows are consecutive rows of res_val. Each wave
+    // copies up to kResRows of them at a time into its 4 KB of sres; the first
+    // batch starts here, so it lands while the keys are rebuilt.
+    constexpr int kResRowB = kHeadDim * (RDT == DT_F32 ? 4 : (RDT == DT_BF16 ? 2 : 1));
+    constexpr int kResRows = 4096 / kResRowB;            // 8 (f32), 16 (bf16), 32 (int8)
+    unsigned char* const rs_w = sres + w * 4096;
+    auto dma_res = [&](int q0) {
+        const int n = min(kResRows, hi - q0);
+        const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(
+            static_cast<const unsigned char*>(p.res_val) + (res_row + q0) * (int64_t)kResRowB, (uint32_t)(n * kResRowB));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma16(rr, rs_w + q * 1024, (uint32_t)(q * 1024 + lane * 16), 0u);
+    };
+    // Token (relative to the block) and int8 scale of residual row q0 + lane.
+    auto res_meta = [&](int q0, int& tok, float& scl) {
+        const int n = min(kResRows, hi - q0);
+        tok = lane < n ? p.res_idx[res_row + q0 + lane] - t0 : -1;
+        scl = (RDT == DT_I8 && lane < n) ? p.res_scale[res_row + q0 + lane] : 1.f;
+    };
+    int tok0 = -1;
+    float scl0 = 1.f;
+    if (lo < hi) {
+        dma_res(lo);
+        res_meta(lo, tok0, scl0);
+    }
 
     // ---- 1. K^T = B_l(head)^T . A_blk^T
     constexpr int EA = ADT == DT_BF16 ? 2 : 1;   // bytes per A element
@@ -349,12 +390,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         }
     }
 
+    // Nothing is in flight here (the last chunk starts no copy, and the memory
+    // counter is in order, so the residual copy started before the loop has
+    // landed); saying so lets the compiler drop its conservative waits on the
+    // A region and the stage buffers, which the epilogue reuses.
+    wait_vmcnt<0>();
+
+    // This thread's 8 query elements and, for int8 A, the row scales.
+    const int qj = tid >> 4, qc = (tid & 15) * 8;
+    u32x4 qv = {0u, 0u, 0u, 0u};
+    if (qj < G) qv = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) +
+                                                     ((int64_t)b * p.n_q + h * G + qj) * kHeadDim + qc);
+    float ascl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tl = tt * 16 + l16;
+        ascl[tt] = ADT == DT_I8 && tl < nt ? p.a_scale[a_row0 + tl] : 1.f;
+    }
+
     // Tokens past the block's end contribute nothing: their K columns are set
     // to zero whatever the factor rows there held.
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int tl = tt * 16 + l16;
-        const float s = tl < nt ? (ADT == DT_I8 ? p.a_scale[a_row0 + tl] : 1.f) : 0.f;
+        const float s = tl < nt ? ascl[tt] : 0.f;
 #pragma unroll
         for (int nt_ = 0; nt_ < 8; ++nt_)
 #pragma unroll
@@ -362,13 +421,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     }
 
     // ---- stage the query rows of this head (rows >= G zero); sa is free now
-    for (int e = tid; e < 16 * kHeadDim; e += kThreads) {
-        const int j = e / kHeadDim, n = e % kHeadDim;
-        __bf16 v = (__bf16)0.0f;
-        if (j < G) v = static_cast<const __bf16*>(p.q)[((int64_t)b * p.n_q + h * G + j) * kHeadDim + n];
-        qs[j * kQRow + n] = v;
-    }
-    __syncthreads();
+    *reinterpret_cast<u32x4*>(qs + qj * kQRow + qc) = qv;
+    barrier_lds();           // not __syncthreads: the residual copy stays in flight
 
     // K as the A operand: kf[tt][s] holds n = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
     bf16x8 kf[4][4];
@@ -403,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     if (lane < G) mw[w][lane] = mloc;
-    __syncthreads();
+    barrier_lds();
     float M = -INFINITY;
     if (l16 < G)
         for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mw[ww][l16]);
@@ -424,15 +478,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     bf16x8 pf[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) pf[u] = pack8(sc[2 * u], sc[2 * u + 1]);
-
-    // Residual slots of this wave's block.
-    int lo = 0, hi = 0;
-    const int64_t res_row = ((int64_t)b * p.n_kv + h) * p.n_res;
-    if (active) {
-        const int64_t pr = ((int64_t)b * p.n_kv + h) * (p.n_blocks + 1) + blk;
-        lo = max(0, min(p.res_ptr[pr], p.n_res));
-        hi = max(lo, min(p.res_ptr[pr + 1], p.n_res));
-    }
 
     // ---- 3/4. feature chunks of [W1 | W_lin]: Z = K W^T, gelu on the W1 part, O = P Z
     const int n_fchunks = (H + kHeadDim) / kFc;
@@ -471,36 +516,67 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     };
 
     // Residual rows of this block, weighted by P, for all d value features at
-    // once: rv[ft][i] holds feature 16 ft + l16 of query head 4 g4 + i. Rows are
-    // read eight at a time so their loads overlap.
+    // once: rv[ft][i] holds feature 16 ft + l16 of query head 4 g4 + i. The
+    // rows come from the LDS copies; row r's token comes from lane r.
     f32x4 rv[8];
 #pragma unroll
     for (int ft = 0; ft < 8; ++ft) rv[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     int applied = 0;
-    for (int q0 = lo; q0 < hi; q0 += 8) {
-        int tl[8];
-        float wgt[8];
-        float v[8][8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int q = min(q0 + r, hi - 1);
-            const int t = p.res_idx[res_row + q] - t0;
-            tl[r] = (q0 + r < hi && t >= 0 && t < nt) ? t : -1;
-            wgt[r] = RDT == DT_I8 ? p.res_scale[res_row + q] : 1.f;
-#pragma unroll
-            for (int ft = 0; ft < 8; ++ft) v[r][ft] = ld<RDT>(p.res_val, (res_row + q) * kHeadDim + ft * 16 + l16);
+    for (int q0 = lo; q0 < hi; q0 += kResRows) {
+        if (q0 != lo) {
+            wait_lgkmcnt0();               // this wave's reads of the previous rows are done
+            dma_res(q0);
         }
+        const int n = min(kResRows, hi - q0);
+        int tok = tok0;
+        float scl = scl0;
+        if (q0 != lo) res_meta(q0, tok, scl);
+        wait_vmcnt<0>();
+        // Four rows per step, all their LDS reads first. Rows past n read the
+        // zeros the copy left there; rows outside the block get weight zero.
+        for (int r0 = 0; r0 < n; r0 += 4) {
+            float pw[4][4], v[4][8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (tl[r] < 0) continue;
-            ++applied;
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + u;
+                const int t = __builtin_amdgcn_readlane(tok, r);
+                const bool ok = r < n && t >= 0 && t < nt;
+                applied += ok ? 1 : 0;
+                const int tc = ok ? t : 0;
+                const float wr = RDT == DT_I8 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), r)) : 1.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * g4 + i;
-                const float pw = j < G ? pl[w][j][tl[r]] * wgt[r] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 4 * g4 + i;
+                    pw[u][i] = (ok && j < G) ? pl[w][j][tc] * wr : 0.f;
+                }
 #pragma unroll
-                for (int ft = 0; ft < 8; ++ft) rv[ft][i] += pw * v[r][ft];
+                for (int ft = 0; ft < 8; ++ft) {
+                    const int f = ft * 16 + l16;
+                    if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
+                    else if (RDT == DT_BF16) v[u][ft] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rs_w + r * kResRowB + f * 2));
+                    else v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
+                }
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int ft = 0; ft < 8; ++ft) rv[ft][i] += pw[u][i] * v[u][ft];
+        }
+    }
+    // Park the residual sums in this wave's quarter of sres (its rows are
+    // consumed): resS[w][j][f] for f in 0..127, added in the cross-wave sum of
+    // the K W_lin chunks, so no registers hold them through the feature loop.
+    float (*const resS)[kMaxG][kHeadDim] = reinterpret_cast<float (*)[kMaxG][kHeadDim]>(sres);
+    static_assert(kWaves * kMaxG * kHeadDim * 4 <= kWaves * 4096, "residual sums overflow sres");
+    wait_lgkmcnt0();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * g4 + i;
+        if (j < G) {
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) resS[w][j][ft * 16 + l16] = rv[ft][i];
         }
     }
     // The pre-pass above read only this wave's own softmax weights; after this
@@ -547,11 +623,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 for (int tt = 0; tt < 4; ++tt) zc[tt] = zn[tt];
             }
         }
-        if (!gpart) {            // add the residual rows to the k W_lin features
-            const bool second = f0 - H >= kFc;
-#pragma unroll
-            for (int ft = 0; ft < 4; ++ft) o[ft] += second ? rv[4 + ft] : rv[ft];
-        }
         float (*const os)[kMaxG][kFc] = (fc & 1) ? oslot1 : oslot0;
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft)
@@ -566,7 +637,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         // comes two chunks later, after every wave has passed the next barrier.
         for (int e = tid; e < G * kFc; e += kThreads) {
             const int j = e / kFc, fl = e % kFc;
-            const float v = os[0][j][fl] + os[1][j][fl] + os[2][j][fl] + os[3][j][fl];
+            float v = os[0][j][fl] + os[1][j][fl] + os[2][j][fl] + os[3][j][fl];
+            if (!gpart) {        // the residual rows belong to the k W_lin features
+                const int f = f0 - H + fl;
+                v += resS[0][j][f] + resS[1][j][f] + resS[2][j][f] + resS[3][j][f];
+            }
             rec0[j * rec_step + 2 + f0 + fl] = v;
         }
     }
@@ -579,7 +654,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         rec0[tid * rec_step + 0] = m;
         rec0[tid * rec_step + 1] = l;
     }
-    __shared__ int cnt_tok[kWaves], cnt_res[kWaves];
     if (lane == 0) {
         cnt_tok[w] = nt;
         cnt_res[w] = applied;
