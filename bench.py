@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time the fused prefill ranking (V_hat computed in the library) at its full shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -259,6 +261,8 @@ def main():
                                                                 args.cpu_seconds)
     if args.rank:
         result["rank_residuals"] = bench_rank(args.steps, args.warmup, ev)
+    if args.prefill:
+        result["prefill_rank"] = bench_prefill(max(2, args.steps // 3), 1, ev)
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -346,6 +350,47 @@ def bench_rank(steps, warmup, ev):
             "error_kernel_ms": err_ms, "error_kernel_GBs": err_bytes / (err_ms * 1e-3) / 1e9,
             "error_kernel_frac_of_8TBs": err_bytes / (err_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "whole_call_input_GBs": in_bytes / (ms * 1e-3) / 1e9}
+
+
+def bench_prefill(steps, warmup, ev):
+    """The fused prefill ranking at the composed workload's ranking shape:
+    32 layers of 131072 tokens, 8 KV heads, r = 512, h = 256, k = 13107,
+    int8 residuals. The all-token pass is timed by HIP events on the stream
+    it runs on; its work is the MFMA products of every token and head."""
+    import torch
+    import long_context_decode_lowram_amd as L
+    import synth
+
+    pc = synth.PREFILL_CONFIGS["p_c5"]
+    x = synth.gen_prefill_inputs(pc, "cuda")
+    Lr, T, hkv, d = x["v"].shape
+    k, nb, r, h = pc.n_res, -(-T // 64), pc.rank, pc.hidden
+    o = {"idx": torch.empty(Lr, hkv, k, dtype=torch.int32, device="cuda"),
+         "val": torch.empty(Lr, hkv, k, d, dtype=torch.int8, device="cuda"),
+         "scale": torch.empty(Lr, hkv, k, dtype=torch.float32, device="cuda"),
+         "ptr": torch.empty(Lr, hkv, nb + 1, dtype=torch.int32, device="cuda")}
+    args = L.make_prefill_args(x["a"], x["b_l"], x["w_lin"], x["w1"], x["w2"], x["v"], k, "i8", o["idx"],
+                               o["val"], o["scale"], o["ptr"], group=pc.group)
+    ws = torch.empty(L.prefill_workspace_size(args), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    for _ in range(warmup):
+        L.prefill_launch(args)
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(steps):
+        args.ev_main_begin, args.ev_main_end = evs[i]
+        L.prefill_launch(args)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    pass1_ms = sum(ev.elapsed_ms(a, b) for a, b in evs) / steps
+    flops = 2.0 * d * (r + d + 2 * h) * T * hkv * Lr
+    return {"shape": [Lr, T, hkv, d], "rank": r, "mlp_hidden": h, "n_res": k, "ms_per_call": ms,
+            "all_token_pass_ms": pass1_ms, "all_token_pass_TFLOPs": flops / (pass1_ms * 1e-3) / 1e12,
+            "all_token_pass_frac_of_bf16_peak": flops / (pass1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "v_read_GBs": x["v"].numel() * 2 / (ms * 1e-3) / 1e9}
 
 
 if __name__ == "__main__":

@@ -161,6 +161,60 @@ typedef struct lowram_rank_args {
 int    lowram_rank_residuals(const lowram_rank_args *args, void *stream);
 size_t lowram_rank_workspace_size(const lowram_rank_args *args);
 
+/*
+ * Fused prefill ranking: the same residual store as lowram_rank_residuals,
+ * with V_hat computed in the library from the cache's own parameters instead
+ * of read from memory (explainer, mechanism paragraph: the value predictor
+ * applied to the reconstructed keys; three-details paragraph: per-head
+ * predictors and ranking by error; project site, Figure 3: keys from a factor
+ * shared by a group of layers times a per-layer factor). For slice (layer) l,
+ * KV head h and token t:
+ *   k       = a[l / group][t] . b_l[l][h*d .. h*d+d)^T       (row vectors)
+ *   V_hat   = k W_lin^T + gelu(k W1^T + b1) W2^T + b2        (weights output-major)
+ *   e_t, I, R, ptr as for lowram_rank_residuals with this V_hat.
+ * V_hat is evaluated in bf16 MFMA products with fp32 accumulation: k and the
+ * hidden activations are rounded to bf16 before the next product, the GELU is
+ * the float32 tail evaluation of the decode kernel, and V_hat is fp32. It is
+ * computed twice (for every token, then again for the chosen ones) by the
+ * same instructions, so R uses bit-for-bit the V_hat that was ranked; pass a
+ * v_hat buffer to receive that fp32 V_hat for every token.
+ * Requirements: head_dim 128, block_size 64, rank % 64 == 0, mlp_hidden % 64
+ * == 0, act_dtype BF16, T * rank * 2 < 2^31. All tensors caller-owned device
+ * memory, 16-byte aligned (err 8, index/scale 4).
+ */
+typedef struct lowram_prefill_args {
+    int32_t n_slices;           /* Lr layers                                          */
+    int32_t group;              /* layers per shared key factor: slice l uses a[l/group] */
+    int32_t ctx_len, n_kv_heads, head_dim, rank, mlp_hidden, block_size, n_res;
+    int32_t act_dtype;          /* BF16: a, b_l, weights, biases and v                */
+    int32_t res_dtype;          /* F32 | BF16 | I8                                    */
+
+    const void *a;              /* [ceil(Lr/group), T, r]                             */
+    const void *b_l;            /* [Lr, Hkv*d, r]                                     */
+    const void *w_lin;          /* [Lr, Hkv, d, d]                                    */
+    const void *w1;             /* [Lr, Hkv, h, d]                                    */
+    const void *b1;             /* [Lr, Hkv, h] or NULL (zero)                        */
+    const void *w2;             /* [Lr, Hkv, d, h]                                    */
+    const void *b2;             /* [Lr, Hkv, d] or NULL (zero)                        */
+    const void *v;              /* [Lr, T, Hkv, d] true values                        */
+
+    int32_t    *res_idx;        /* [Lr, Hkv, k]      (may be NULL when k == 0)        */
+    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype (NULL when k == 0)      */
+    float      *res_scale;      /* [Lr, Hkv, k]  I8 only, else NULL                   */
+    int32_t    *res_blk_ptr;    /* [Lr, Hkv, nb+1]                                    */
+    double     *err;            /* [Lr, Hkv, T] or NULL (then kept in workspace)      */
+    float      *v_hat;          /* [Lr, T, Hkv, d] fp32 copy of V_hat, or NULL        */
+
+    void       *workspace;
+    size_t      workspace_bytes;
+
+    void       *ev_main_begin;  /* optional hipEvent_t around the all-token pass      */
+    void       *ev_main_end;
+} lowram_prefill_args;
+
+int    lowram_prefill_rank(const lowram_prefill_args *args, void *stream);
+size_t lowram_prefill_workspace_size(const lowram_prefill_args *args);
+
 /* Static description of a status code. */
 const char *lowram_status_string(int status);
 

@@ -40,6 +40,15 @@ class RankArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
 
 
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in (
+        "n_slices", "group", "ctx_len", "n_kv_heads", "head_dim", "rank", "mlp_hidden", "block_size",
+        "n_res", "act_dtype", "res_dtype")] + [
+        (n, _p) for n in ("a", "b_l", "w_lin", "w1", "b1", "w2", "b2", "v", "res_idx", "res_val",
+                          "res_scale", "res_blk_ptr", "err", "v_hat", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+
+
 class LowramError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"liblowram status {status}: {msg}")
@@ -65,6 +74,10 @@ def lib():
         L.lowram_rank_residuals.restype = ctypes.c_int
         L.lowram_rank_workspace_size.argtypes = [ctypes.POINTER(RankArgs)]
         L.lowram_rank_workspace_size.restype = ctypes.c_size_t
+        L.lowram_prefill_rank.argtypes = [ctypes.POINTER(PrefillArgs), _p]
+        L.lowram_prefill_rank.restype = ctypes.c_int
+        L.lowram_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
+        L.lowram_prefill_workspace_size.restype = ctypes.c_size_t
         L.lowram_status_string.argtypes = [ctypes.c_int]
         L.lowram_status_string.restype = ctypes.c_char_p
         L.lowram_last_error.argtypes = []
@@ -214,4 +227,64 @@ def rank_residuals(v, v_hat, n_res, res_dtype, *, want_err=False, workspace=None
     args.workspace = workspace.data_ptr()
     args.workspace_bytes = workspace.numel()
     rank_launch(args, stream)
+    return out
+
+
+def make_prefill_args(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, res_idx, res_val, res_scale, res_blk_ptr, *,
+                      group=4, b1=None, b2=None, err=None, v_hat=None, workspace=None, events=None):
+    """Arguments of lowram_prefill_rank. a [ceil(Lr/group), T, r], b_l [Lr, Hkv*d, r],
+    w_lin [Lr, Hkv, d, d], w1 [Lr, Hkv, h, d], w2 [Lr, Hkv, d, h], v [Lr, T, Hkv, d]."""
+    Lr, T, Hkv, d = v.shape
+    args = PrefillArgs()
+    args.n_slices, args.group, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, group, T, Hkv, d
+    args.rank, args.mlp_hidden, args.block_size, args.n_res = a.shape[-1], w1.shape[-2], BLOCK, n_res
+    args.act_dtype = _dt(v, "v")
+    args.res_dtype = {"f32": F32, "bf16": BF16, "i8": I8}[res_dtype]
+    for name, t in (("a", a), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1), ("b1", b1), ("w2", w2),
+                    ("b2", b2), ("v", v), ("res_idx", res_idx), ("res_val", res_val),
+                    ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("err", err),
+                    ("v_hat", v_hat), ("workspace", workspace)):
+        setattr(args, name, _ptr(t))
+    args.workspace_bytes = 0 if workspace is None else workspace.numel()
+    if events is not None:
+        args.ev_main_begin, args.ev_main_end = events
+    return args
+
+
+def prefill_workspace_size(args):
+    n = lib().lowram_prefill_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def prefill_launch(args, stream=None):
+    rc = lib().lowram_prefill_rank(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def prefill_rank(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, *, group=4, b1=None, b2=None, want_err=False,
+                 want_v_hat=False, workspace=None, stream=None):
+    """Fused prefill ranking: the residual store of V against the values the
+    cache's own predictor gives (computed in the library). Returns a dict like
+    ``rank_residuals`` plus ``v_hat`` (fp32, when ``want_v_hat``)."""
+    Lr, T, Hkv, d = v.shape
+    dev = v.device
+    nb = -(-T // BLOCK)
+    out = {
+        "idx": torch.empty(Lr, Hkv, n_res, dtype=torch.int32, device=dev),
+        "val": torch.empty(Lr, Hkv, n_res, d, dtype=_RES_TORCH[res_dtype], device=dev),
+        "scale": torch.empty(Lr, Hkv, n_res, dtype=torch.float32, device=dev) if res_dtype == "i8" else None,
+        "ptr": torch.empty(Lr, Hkv, nb + 1, dtype=torch.int32, device=dev),
+        "err": torch.empty(Lr, Hkv, T, dtype=torch.float64, device=dev) if want_err else None,
+        "v_hat": torch.empty(Lr, T, Hkv, d, dtype=torch.float32, device=dev) if want_v_hat else None,
+    }
+    args = make_prefill_args(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, out["idx"], out["val"], out["scale"],
+                             out["ptr"], group=group, b1=b1, b2=b2, err=out["err"], v_hat=out["v_hat"])
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(args), dtype=torch.uint8, device=dev)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    prefill_launch(args, stream)
     return out

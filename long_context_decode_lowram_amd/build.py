@@ -15,12 +15,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblowram.so")
 
-SOURCES = ["api.cpp", "decode_common.hip", "decode_generic.hip", "decode_mfma.hip", "rank.hip"]
+SOURCES = ["api.cpp", "decode_common.hip", "decode_generic.hip", "decode_mfma.hip", "rank.hip", "prefill_mfma.hip"]
 # Packed fp32 instructions are switched off for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-x", "hip", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
-PER_FILE = {"rank.hip": ["-ffp-contract=off"]}
+PER_FILE = {"rank.hip": ["-ffp-contract=off"], "prefill_mfma.hip": ["-ffp-contract=off"]}
 
 
 def hipcc():

@@ -116,6 +116,32 @@ int plan_rank(const lowram_rank_args* a, RankPlan* pl) {
     return LOWRAM_OK;
 }
 
+struct PrefillPlan { size_t off_err, off_thr, off_neq, total; int nb; };
+
+int plan_prefill(const lowram_prefill_args* a, PrefillPlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_slices < 1 || a->ctx_len < 1 || a->n_kv_heads < 1 || a->group < 1)
+        return fail(LOWRAM_ERR_ARG, "n_slices, ctx_len, n_kv_heads and group must be >= 1");
+    if (a->head_dim != kHeadDim) return fail(LOWRAM_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->block_size != kBlock) return fail(LOWRAM_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
+    if (a->rank < 64 || a->rank % 64 != 0) return fail(LOWRAM_ERR_UNSUPPORTED, "rank must be a positive multiple of 64 (got %d)", a->rank);
+    if (a->mlp_hidden < 64 || a->mlp_hidden % 64 != 0 || a->mlp_hidden > 4096)
+        return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 64 in [64, 4096] (got %d)", a->mlp_hidden);
+    if ((int64_t)a->ctx_len * a->rank * 2 >= (int64_t(1) << 31))
+        return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * rank * 2 must stay below 2^31");
+    if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
+    if (a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_UNSUPPORTED, "act_dtype must be BF16");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
+    const size_t nseg = (size_t)a->n_slices * a->n_kv_heads;
+    pl->off_err = 0;
+    const size_t err_bytes = a->err ? 0 : nseg * a->ctx_len * sizeof(double);
+    pl->off_thr = up256(err_bytes);
+    pl->off_neq = up256(pl->off_thr + nseg * sizeof(unsigned long long));
+    pl->total = up256(pl->off_neq + nseg * sizeof(int32_t));
+    return LOWRAM_OK;
+}
+
 int hip_fail(hipError_t e, const char* what) {
     return fail(LOWRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -233,6 +259,66 @@ int lowram_rank_residuals(const lowram_rank_args* a, void* stream) {
     if ((e = launch_rank_select(p, s)) != hipSuccess) return hip_fail(e, "rank select launch");
     if ((e = launch_rank_compact(p, s)) != hipSuccess) return hip_fail(e, "rank compact launch");
     if ((e = launch_rank_gather(p, s)) != hipSuccess) return hip_fail(e, "rank gather launch");
+    return LOWRAM_OK;
+}
+
+size_t lowram_prefill_workspace_size(const lowram_prefill_args* a) {
+    g_err[0] = 0;
+    PrefillPlan pl;
+    return plan_prefill(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_prefill_rank(const lowram_prefill_args* a, void* stream) {
+    g_err[0] = 0;
+    PrefillPlan pl;
+    int rc = plan_prefill(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (!a->a || !a->b_l || !a->w_lin || !a->w1 || !a->w2 || !a->v || !a->res_blk_ptr)
+        return fail(LOWRAM_ERR_ARG, "a, b_l, w_lin, w1, w2, v and res_blk_ptr must be non-NULL");
+    if (a->n_res > 0 && (!a->res_idx || !a->res_val))
+        return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
+    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale)
+        return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    const void* v16[] = {a->a, a->b_l, a->w_lin, a->w1, a->w2, a->v, a->res_val, a->v_hat, a->workspace};
+    for (const void* p : v16)
+        if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
+    if (misaligned(a->b1, 2) || misaligned(a->b2, 2)) return fail(LOWRAM_ERR_ARG, "bias pointers must be 2-byte aligned");
+    if (misaligned(a->err, 8)) return fail(LOWRAM_ERR_ARG, "err pointer is not 8-byte aligned");
+    if (misaligned(a->res_idx, 4) || misaligned(a->res_blk_ptr, 4) || misaligned(a->res_scale, 4))
+        return fail(LOWRAM_ERR_ARG, "index/scale pointers must be 4-byte aligned");
+    if (!a->workspace || a->workspace_bytes < pl.total)
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+
+    char* ws = static_cast<char*>(a->workspace);
+    PrefillParams p{};
+    p.n_slices = a->n_slices; p.group = a->group; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads;
+    p.rank = a->rank; p.hidden = a->mlp_hidden; p.n_res = a->n_res; p.n_blocks = pl.nb; p.res_dtype = a->res_dtype;
+    p.a = a->a; p.b_l = a->b_l; p.w_lin = a->w_lin; p.w1 = a->w1; p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.v = a->v;
+    p.err = a->err ? a->err : reinterpret_cast<double*>(ws + pl.off_err);
+    p.v_hat = a->v_hat;
+    p.res_idx = a->res_idx; p.res_val = a->res_val; p.res_scale = a->res_scale;
+
+    RankParams r{};
+    r.n_slices = a->n_slices; r.ctx_len = a->ctx_len; r.n_kv = a->n_kv_heads; r.n_res = a->n_res;
+    r.n_blocks = pl.nb; r.in_dtype = LOWRAM_BF16; r.res_dtype = a->res_dtype;
+    r.res_idx = a->res_idx; r.res_ptr = a->res_blk_ptr; r.err = p.err;
+    r.thr = reinterpret_cast<unsigned long long*>(ws + pl.off_thr);
+    r.n_eq = reinterpret_cast<int32_t*>(ws + pl.off_neq);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a->ev_main_begin && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_begin), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    p.n_groups = prefill_groups(p, 0);
+    if ((e = launch_prefill(p, 0, s)) != hipSuccess) return hip_fail(e, "prefill error launch");
+    if (a->ev_main_end && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_end), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    if ((e = launch_rank_select(r, s)) != hipSuccess) return hip_fail(e, "rank select launch");
+    if ((e = launch_rank_compact(r, s)) != hipSuccess) return hip_fail(e, "rank compact launch");
+    if (a->n_res > 0) {
+        p.n_groups = prefill_groups(p, 1);
+        if ((e = launch_prefill(p, 1, s)) != hipSuccess) return hip_fail(e, "prefill residual launch");
+    }
     return LOWRAM_OK;
 }
 

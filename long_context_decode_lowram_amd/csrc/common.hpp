@@ -24,6 +24,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// binary64 -> bfloat16 bits with one round-to-nearest-even step: first to
+// float32 with round-to-odd (truncate, then set the last bit if anything was
+// dropped), then float32 -> bfloat16 nearest-even. Float32 keeps 16 more
+// bits than bfloat16 at every exponent, so the two steps round exactly like
+// one.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
+    float f = static_cast<float>(x);
+    const double back = static_cast<double>(f);
+    if (back != x && x == x) {
+        uint32_t u = __float_as_uint(f);
+        if (fabs(back) > fabs(x)) u -= 1u;
+        u |= 1u;
+        f = __uint_as_float(u);
+    }
+    return f32_to_bf16_bits(f);
+}
+
 // Element load of a stored tensor as float (int8 returns the raw code).
 template <int DT> __device__ __forceinline__ float ld(const void* p, int64_t i);
 template <> __device__ __forceinline__ float ld<DT_F32>(const void* p, int64_t i) {

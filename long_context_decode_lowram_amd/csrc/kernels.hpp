@@ -36,4 +36,17 @@ hipError_t launch_rank_select(const RankParams& p, hipStream_t s);
 hipError_t launch_rank_compact(const RankParams& p, hipStream_t s);
 hipError_t launch_rank_gather(const RankParams& p, hipStream_t s);
 
+// Fused prefill ranking: V_hat from the cache parameters, then the error
+// (mode 0, every token) or the residual store (mode 1, chosen tokens).
+struct PrefillParams {
+    int n_slices, group, ctx_len, n_kv, rank, hidden, n_res, n_blocks, res_dtype;
+    int n_groups;                // workgroups per (layer, head): 4 blocks, or 256 chosen tokens
+    const void* a; const void* b_l; const void* w_lin; const void* w1; const void* b1;
+    const void* w2; const void* b2; const void* v;
+    double* err; float* v_hat;
+    int32_t* res_idx; void* res_val; float* res_scale;
+};
+int prefill_groups(const PrefillParams& p, int mode);
+hipError_t launch_prefill(const PrefillParams& p, int mode, hipStream_t s);
+
 }  // namespace lowram

@@ -340,22 +340,6 @@ hipError_t launch_rank_compact(const RankParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// binary64 -> bfloat16 bits with one round-to-nearest-even step: first to
-// float32 with round-to-odd (truncate, then set the last bit if anything was
-// dropped), then float32 -> bfloat16 nearest-even. Float32 keeps 16 more
-// bits than bfloat16 at every exponent, so the two steps round exactly like
-// one.
-__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
-    float f = static_cast<float>(x);
-    const double back = static_cast<double>(f);
-    if (back != x && x == x) {
-        uint32_t u = __float_as_uint(f);
-        if (fabs(back) > fabs(x)) u -= 1u;
-        u |= 1u;
-        f = __uint_as_float(u);
-    }
-    return f32_to_bf16_bits(f);
-}
 
 // Sixteen lanes per stored residual: lane j of a group owns elements
 // 8j .. 8j+7 of the row (16-byte loads of bf16, 32 of f32). R = V - V_hat at

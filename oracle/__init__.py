@@ -46,6 +46,7 @@ from .rank import (residual_error, select_worst, round_bf16, round_f32,
                    quantize_int8_rows, dequantize_int8_rows, block_ptr,
                    rank_residuals)
 from .factor import xkv_factorize, pinv_value_map
+from .prefill import predicted_values, prefill_rank
 from .budget import value_budget, dense_kv_bytes_per_token
 
 __all__ = [
@@ -54,4 +55,5 @@ __all__ = [
     "residual_error", "select_worst", "round_bf16", "round_f32",
     "quantize_int8_rows", "dequantize_int8_rows", "block_ptr", "rank_residuals",
     "xkv_factorize", "pinv_value_map", "value_budget", "dense_kv_bytes_per_token",
+    "predicted_values", "prefill_rank",
 ]

@@ -19,9 +19,9 @@ import math
 
 import torch
 
-__all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "make_generator",
-           "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
-           "block_ptr_from_idx"]
+__all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "PrefillConfig", "PREFILL_CONFIGS",
+           "make_generator", "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
+           "gen_prefill_inputs", "block_ptr_from_idx"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -96,6 +96,34 @@ class RankConfig:
 
 
 RANK_C5 = RankConfig(32, 131072)
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    """Shapes of the fused prefill ranking: Lr layers in groups sharing a key
+    factor, their per-layer key factor and predictor, and the true values."""
+    name: str
+    n_slices: int
+    ctx_len: int
+    rank: int
+    hidden: int
+    n_res: int
+    n_kv_heads: int = 8
+    group: int = 4
+    head_dim: int = 128
+    block: int = 64
+    res_dtype: str = "i8"
+    biases: bool = False
+    seed: int = 6
+
+
+PREFILL_CONFIGS = {c.name: c for c in (
+    PrefillConfig("p_small_ragged", 4, 1000, 256, 128, 100, n_kv_heads=2, res_dtype="bf16", biases=True),
+    PrefillConfig("p_mid", 8, 8192, 512, 256, 819),
+    # the composed workload's ranking shape (32 layers of 131072 tokens, Mistral-7B attention
+    # shapes, r = 512, h = 256, k = floor(0.1 T))
+    PrefillConfig("p_c5", 32, 131072, 512, 256, 13107),
+)}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 _SIGMA = 1.0 / math.sqrt(128.0)     # N(0, 1/sqrt(d)) draws, d = 128
@@ -274,3 +302,29 @@ def gen_rank_inputs(rc, device, *, n_slices=None, plant_ties=True):
                     v_hat[sl, grp, h] = v_hat[sl, grp[:1], h]
                     v[sl, grp, h] = (v_hat[sl, grp[:1], h].float() + 50.0).to(dt)
     return v.contiguous(), v_hat.contiguous()
+
+
+def gen_prefill_inputs(pc, device, *, res_dtype=None):
+    """Inputs of the fused prefill ranking, bf16: a [ceil(Lr/group), T, r],
+    b_l [Lr, Hkv*d, r], w_lin [Lr, Hkv, d, d], w1 [Lr, Hkv, h, d],
+    w2 [Lr, Hkv, d, h] (all N(0, 1/sqrt(128)), w2 N(0, 1/sqrt(h))), biases
+    N(0, 0.05) when ``pc.biases``, and true values V [Lr, T, Hkv, d] drawn
+    independently: N(0, 0.125) times a LogNormal(0, 1) scale per (token, head),
+    so a minority of tokens carries large errors whatever the predictor gives.
+    """
+    g = make_generator(device, pc.seed, "prefill", pc.name)
+    bf = torch.bfloat16
+    ng = -(-pc.n_slices // pc.group)
+    L, T, hkv, d, r, h = pc.n_slices, pc.ctx_len, pc.n_kv_heads, pc.head_dim, pc.rank, pc.hidden
+    out = {
+        "a": (torch.randn(ng, T, r, generator=g, device=device) * _SIGMA).to(bf),
+        "b_l": (torch.randn(L, hkv * d, r, generator=g, device=device) * _SIGMA).to(bf),
+        "w_lin": (torch.randn(L, hkv, d, d, generator=g, device=device) * _SIGMA).to(bf),
+        "w1": (torch.randn(L, hkv, h, d, generator=g, device=device) * _SIGMA).to(bf),
+        "w2": (torch.randn(L, hkv, d, h, generator=g, device=device) / math.sqrt(h)).to(bf),
+        "b1": (torch.randn(L, hkv, h, generator=g, device=device) * 0.05).to(bf) if pc.biases else None,
+        "b2": (torch.randn(L, hkv, d, generator=g, device=device) * 0.05).to(bf) if pc.biases else None,
+    }
+    s = torch.exp(torch.randn(L, T, hkv, 1, generator=g, device=device))
+    out["v"] = (torch.randn(L, T, hkv, d, generator=g, device=device) * 0.125 * s).to(bf)
+    return out

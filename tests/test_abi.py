@@ -151,3 +151,49 @@ def test_rank_rejects(field, value, status):
     a = valid_rank()
     setattr(a, field, value)
     assert call_rank(a) == status
+
+
+def test_prefill_struct_layout_matches_binding():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct lowram_prefill_args"):text.index("} lowram_prefill_args;")]
+    fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f[0] for f in B.PrefillArgs._fields_]
+    assert {"lowram_prefill_rank", "lowram_prefill_workspace_size"} <= set(declared_functions())
+
+
+def valid_prefill():
+    a = B.PrefillArgs()
+    a.n_slices, a.group, a.ctx_len, a.n_kv_heads, a.head_dim = 4, 4, 1000, 2, 128
+    a.rank, a.mlp_hidden, a.block_size, a.n_res = 256, 128, 64, 100
+    a.act_dtype, a.res_dtype = B.BF16, B.BF16
+    for n in ("a", "b_l", "w_lin", "w1", "w2", "v", "res_idx", "res_val", "res_blk_ptr"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def call_prefill(a):
+    return L.lib().lowram_prefill_rank(ctypes.byref(a), None)
+
+
+def test_prefill_valid_args_stop_at_workspace():
+    a = valid_prefill()
+    n = B.prefill_workspace_size(a)
+    assert n >= 4 * 2 * 1000 * 8
+    assert call_prefill(a) == B.ERR_WORKSPACE
+    a.err = FAKE
+    assert B.prefill_workspace_size(a) < n
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("a", None, B.ERR_ARG), ("w2", None, B.ERR_ARG), ("v", None, B.ERR_ARG), ("res_val", None, B.ERR_ARG),
+    ("v_hat", FAKE + 8, B.ERR_ARG), ("b1", FAKE + 1, B.ERR_ARG),
+    ("head_dim", 64, B.ERR_UNSUPPORTED), ("block_size", 32, B.ERR_UNSUPPORTED),
+    ("rank", 96, B.ERR_UNSUPPORTED), ("mlp_hidden", 96, B.ERR_UNSUPPORTED), ("act_dtype", B.F32, B.ERR_UNSUPPORTED),
+    ("ctx_len", 1 << 22, B.ERR_UNSUPPORTED),       # ctx_len * rank * 2 reaches 2^31
+    ("n_res", 1001, B.ERR_ARG), ("res_dtype", B.I8, B.ERR_ARG), ("group", 0, B.ERR_ARG),
+])
+def test_prefill_rejects(field, value, status):
+    a = valid_prefill()
+    setattr(a, field, value)
+    assert call_prefill(a) == status
+    assert L.last_error() != ""

@@ -377,3 +377,50 @@ def test_dense_kv_bytes_per_token():
     sh = g["shape"]
     nbytes = oracle.dense_kv_bytes_per_token(sh["layers"], sh["kv_heads"], sh["head_dim"], sh["elem_bytes"])
     assert round(nbytes / 1000, 2) == g["kb_per_token_printed"]
+
+
+# ------------------------------------------------ fused prefill: V_hat everywhere
+def test_predicted_values_slim_case_per_layer():
+    """explainer, Slim Attention paragraph, for every layer of a group sharing
+    one key factor: with A = x, B_l = the layer's invertible W_K and
+    W_lin = pinv(W_K) W_V (nonlinear branch zero), every token's predicted
+    value is x W_V exactly."""
+    rng = np.random.default_rng(21)
+    n_tok, d, n_kv, hid, n_l = 40, 8, 2, 4, 3
+    x = rng.standard_normal((n_tok, d))
+    w_k = rng.standard_normal((n_l, n_kv, d, d)) + 3 * np.eye(d)
+    w_v = rng.standard_normal((n_l, n_kv, d, d))
+    bl = np.stack([np.concatenate([w_k[l, h].T for h in range(n_kv)], axis=0) for l in range(n_l)])
+    w_lin = np.stack([[oracle.pinv_value_map(w_k[l, h], w_v[l, h]) for h in range(n_kv)] for l in range(n_l)])
+    zeros1, zeros2 = np.zeros((n_l, n_kv, hid, d)), np.zeros((n_l, n_kv, d, hid))
+    vh = oracle.predicted_values(x[None], bl, w_lin, zeros1, zeros2, group=4)
+    for l in range(n_l):
+        for h in range(n_kv):
+            np.testing.assert_allclose(vh[l, :, h, :], x @ w_v[l, h], rtol=0, atol=1e-10)
+
+
+def test_predicted_values_brute_force_groups_and_biases():
+    """Pure-Python loops with math.erf on tiny inputs: five layers in groups of
+    four (layer 4 reads the second factor), nonzero biases."""
+    rng = np.random.default_rng(22)
+    n_l, grp, n_tok, r, d, n_kv, hid = 5, 4, 3, 3, 2, 2, 3
+    a = rng.standard_normal((2, n_tok, r))
+    bl = rng.standard_normal((n_l, n_kv * d, r))
+    w_lin = rng.standard_normal((n_l, n_kv, d, d))
+    w1 = rng.standard_normal((n_l, n_kv, hid, d))
+    w2 = rng.standard_normal((n_l, n_kv, d, hid))
+    b1 = rng.standard_normal((n_l, n_kv, hid))
+    b2 = rng.standard_normal((n_l, n_kv, d))
+    vh = oracle.predicted_values(a, bl, w_lin, w1, w2, b1, b2, group=grp)
+    for l in range(n_l):
+        for t in range(n_tok):
+            for h in range(n_kv):
+                key = [sum(a[l // grp, t, c] * bl[l, h * d + i, c] for c in range(r)) for i in range(d)]
+                hidden = []
+                for j in range(hid):
+                    z = sum(key[i] * w1[l, h, j, i] for i in range(d)) + b1[l, h, j]
+                    hidden.append(0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))))
+                for o in range(d):
+                    want = (sum(key[i] * w_lin[l, h, o, i] for i in range(d)) +
+                            sum(hidden[j] * w2[l, h, o, j] for j in range(hid)) + b2[l, h, o])
+                    assert abs(vh[l, t, h, o] - want) <= 1e-12 * max(1.0, abs(want))
