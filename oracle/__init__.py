@@ -43,8 +43,8 @@ forms, and the explainer's printed memory arithmetic.
 from .decode import (gelu, reconstruct_keys, predict_values, attended_blocks,
                      decode_batch_element, decode_step, attention)
 from .rank import (residual_error, select_worst, round_bf16, round_f32,
-                   quantize_int8_rows, dequantize_int8_rows, block_ptr,
-                   rank_residuals)
+                   quantize_int8_rows, dequantize_int8_rows, quantize_i2_rows,
+                   dequantize_i2_rows, pack_i2, unpack_i2, block_ptr, rank_residuals)
 from .factor import xkv_factorize, pinv_value_map
 from .prefill import predicted_values, prefill_rank
 from .budget import value_budget, dense_kv_bytes_per_token
@@ -53,7 +53,8 @@ __all__ = [
     "gelu", "reconstruct_keys", "predict_values", "attended_blocks",
     "decode_batch_element", "decode_step", "attention",
     "residual_error", "select_worst", "round_bf16", "round_f32",
-    "quantize_int8_rows", "dequantize_int8_rows", "block_ptr", "rank_residuals",
+    "quantize_int8_rows", "dequantize_int8_rows", "quantize_i2_rows", "dequantize_i2_rows",
+    "pack_i2", "unpack_i2", "block_ptr", "rank_residuals",
     "xkv_factorize", "pinv_value_map", "value_budget", "dense_kv_bytes_per_token",
     "predicted_values", "prefill_rank",
 ]

@@ -74,6 +74,42 @@ def dequantize_int8_rows(q, s):
     return np.asarray(q).astype(np.float64) * np.asarray(s).astype(np.float64)[..., None]
 
 
+def quantize_i2_rows(r):
+    """Per-row 2-bit code (the explainer's comparison table names 2-bit
+    residuals without a codec; the reading here is the symmetric mid-rise
+    4-level quantizer): levels (q - 1.5) s for q in 0..3 with
+    s = float32(max|r| / 1.5) (binary64 division, one rounding to float32),
+    q = clamp(rint(r / s + 1.5), 0, 3) in binary64 (division, then addition,
+    ties to even). An all-zero row gets s = 0 and q = 2 (level 0).
+    Returns (q uint8 [..., d] in 0..3, s float32 [...])."""
+    r = np.asarray(r, np.float64)
+    amax = np.max(np.abs(r), axis=-1)
+    s = (amax / 1.5).astype(np.float32)
+    s64 = s.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qf = np.where(s64 > 0, np.rint(r / np.where(s64 > 0, s64, 1.0) + 1.5), 2.0)
+    return np.clip(qf, 0, 3).astype(np.uint8), s
+
+
+def dequantize_i2_rows(q, s):
+    """Exact value of a 2-bit row code: (q - 1.5) s in binary64."""
+    return (np.asarray(q).astype(np.float64) - 1.5) * np.asarray(s).astype(np.float64)[..., None]
+
+
+def pack_i2(q):
+    """Four 2-bit codes per byte: element i in bits 2(i mod 4) .. 2(i mod 4)+1
+    of byte i // 4. q [..., d] with d a multiple of 4 -> uint8 [..., d/4]."""
+    q = np.asarray(q).astype(np.uint8)
+    q4 = q.reshape(q.shape[:-1] + (q.shape[-1] // 4, 4))
+    return (q4[..., 0] | (q4[..., 1] << 2) | (q4[..., 2] << 4) | (q4[..., 3] << 6)).astype(np.uint8)
+
+
+def unpack_i2(b):
+    """Inverse of pack_i2: uint8 [..., d/4] -> codes uint8 [..., d]."""
+    b = np.asarray(b).astype(np.uint8)
+    return np.stack([(b >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(b.shape[:-1] + (4 * b.shape[-1],))
+
+
 def block_ptr(idx, n_tokens, block):
     """Block CSR over ascending residual indices: ptr[i] = #{t in idx : t < i*block}
     for i = 0..nb, nb = ceil(T/block); so block i owns slots ptr[i]..ptr[i+1]."""
@@ -88,7 +124,8 @@ def rank_residuals(v, v_hat, k, block, res_dtype):
 
     Per (l, h): errors over all T tokens; the k worst tokens (ties to the
     lower index) in ascending order; residuals R = V - V_hat at those tokens
-    (exact in binary64, then stored as ``res_dtype``: 'f32', 'bf16' or 'i8');
+    (exact in binary64, then stored as ``res_dtype``: 'f32', 'bf16', 'i8', or
+    'i2' packed four codes per byte);
     and the block CSR. Returns a dict with idx [Lr, Hkv, k], val [Lr, Hkv, k, d]
     (float64 value of the stored element, or int8 codes for 'i8'), scale
     [Lr, Hkv, k] float32 ('i8' only), ptr [Lr, Hkv, nb+1], err [Lr, Hkv, T].
@@ -100,8 +137,11 @@ def rank_residuals(v, v_hat, k, block, res_dtype):
     idx = np.zeros((n_sl, n_kv, k), np.int64)
     ptr = np.zeros((n_sl, n_kv, nb + 1), np.int64)
     err = np.zeros((n_sl, n_kv, n_tok))
-    val = np.zeros((n_sl, n_kv, k, d), np.int8 if res_dtype == "i8" else np.float64)
-    scale = np.zeros((n_sl, n_kv, k), np.float32) if res_dtype == "i8" else None
+    if res_dtype == "i2":
+        val = np.zeros((n_sl, n_kv, k, d // 4), np.uint8)
+    else:
+        val = np.zeros((n_sl, n_kv, k, d), np.int8 if res_dtype == "i8" else np.float64)
+    scale = np.zeros((n_sl, n_kv, k), np.float32) if res_dtype in ("i8", "i2") else None
     for sl in range(n_sl):
         for h in range(n_kv):
             e = residual_error(v[sl, :, h, :], v_hat[sl, :, h, :])
@@ -112,6 +152,9 @@ def rank_residuals(v, v_hat, k, block, res_dtype):
             r = v[sl, sel, h, :].astype(np.float64) - v_hat[sl, sel, h, :].astype(np.float64)
             if res_dtype == "i8":
                 val[sl, h], scale[sl, h] = quantize_int8_rows(r)
+            elif res_dtype == "i2":
+                q2, scale[sl, h] = quantize_i2_rows(r)
+                val[sl, h] = pack_i2(q2)
             elif res_dtype == "bf16":
                 val[sl, h] = round_bf16(r)
             elif res_dtype == "f32":

@@ -424,3 +424,56 @@ def test_predicted_values_brute_force_groups_and_biases():
                     want = (sum(key[i] * w_lin[l, h, o, i] for i in range(d)) +
                             sum(hidden[j] * w2[l, h, o, j] for j in range(hid)) + b2[l, h, o])
                     assert abs(vh[l, t, h, o] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# ------------------------------------------------------------- 2-bit residuals
+def test_i2_levels_closed_form():
+    """A row on the four levels comes back exactly: (-1.5, -0.5, 0.5, 1.5) c
+    with c = 1/8 gives s = c and q = 0, 1, 2, 3."""
+    c = 0.125
+    row = np.array([[-1.5, -0.5, 0.5, 1.5, 1.5, -1.5, 0.5, -0.5]]) * c
+    q, s = oracle.quantize_i2_rows(row)
+    assert s.tolist() == [np.float32(c)]
+    assert q.tolist() == [[0, 1, 2, 3, 3, 0, 2, 1]]
+    np.testing.assert_array_equal(oracle.dequantize_i2_rows(q, s), row)
+
+
+def test_i2_error_bound_and_zero_row():
+    """Every element lies within the level range (max level = max|r|), so the
+    round-to-nearest level is within s/2 of it; an all-zero row is level 0."""
+    rng = np.random.default_rng(31)
+    r = rng.standard_normal((300, 128)) * np.exp(rng.standard_normal((300, 1)))
+    q, s = oracle.quantize_i2_rows(r)
+    assert q.min() >= 0 and q.max() <= 3
+    err = np.abs(oracle.dequantize_i2_rows(q, s) - r)
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2 * (1 + 1e-6) + 1e-300)
+    q0, s0 = oracle.quantize_i2_rows(np.zeros((2, 8)))
+    assert s0.tolist() == [0.0, 0.0] and q0.tolist() == [[2] * 8] * 2
+    np.testing.assert_array_equal(oracle.dequantize_i2_rows(q0, s0), np.zeros((2, 8)))
+
+
+def test_i2_packing_layout():
+    """Element i sits in bits 2(i mod 4) of byte i // 4; pack/unpack invert."""
+    q = np.array([[1, 2, 3, 0, 0, 0, 0, 3]], np.uint8)
+    b = oracle.pack_i2(q)
+    assert b.tolist() == [[1 | (2 << 2) | (3 << 4), 3 << 6]]
+    rng = np.random.default_rng(32)
+    qq = rng.integers(0, 4, size=(5, 7, 128)).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.unpack_i2(oracle.pack_i2(qq)), qq)
+
+
+def test_rank_residuals_i2_matches_its_codec():
+    """The ranking's 'i2' store is the codec above applied to V - V_hat at the
+    chosen tokens (same tokens as any other encoding)."""
+    rng = np.random.default_rng(33)
+    v = rng.standard_normal((2, 90, 2, 8)).astype(np.float32)
+    vh = rng.standard_normal((2, 90, 2, 8)).astype(np.float32)
+    a = oracle.rank_residuals(v, vh, 11, 64, "i2")
+    b = oracle.rank_residuals(v, vh, 11, 64, "f32")
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    for sl in range(2):
+        for h in range(2):
+            r = v[sl, a["idx"][sl, h], h].astype(np.float64) - vh[sl, a["idx"][sl, h], h].astype(np.float64)
+            q, s = oracle.quantize_i2_rows(r)
+            np.testing.assert_array_equal(oracle.unpack_i2(a["val"][sl, h]), q)
+            np.testing.assert_array_equal(a["scale"][sl, h], s)
