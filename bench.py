@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--workload", default="c3_llama_131k")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--generic", action="store_true", help="force the fp32 SIMT kernel")
+    ap.add_argument("--res-dtype", choices=("f32", "bf16", "i8", "i2"), default=None,
+                    help="store the workload's residuals in this encoding instead")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
@@ -97,12 +99,11 @@ def work_per_call(cfg, n_att, n_res_att, win):
     2*Hq*(d + h) per token."""
     d, hkv, hq, r, h = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, cfg.rank, cfg.mlp_hidden
     ea = {"f32": 4, "bf16": 2, "i8": 1}[cfg.a_dtype]
-    er = {"f32": 4, "bf16": 2, "i8": 1}[cfg.res_dtype]
     ew = {"f32": 4, "bf16": 2}[cfg.act]
     byts = flops = flops_direct = 0
     for na, nr in zip(n_att, n_res_att):
         byts += na * (r * ea + (4 if cfg.a_dtype == "i8" else 0))
-        byts += nr * (d * er + 4 + (4 if cfg.res_dtype == "i8" else 0))
+        byts += nr * residual_row_bytes(cfg)
         byts += (r * hkv * d + hkv * (d * d + 2 * d * h)) * ew + 2 * hq * d * ew + win * 2 * hkv * d * ew
         flops += 2 * na * hkv * d * (r + d + h) + 2 * na * hq * d + 2 * na * hq * (d + h)
         flops_direct += 2 * na * r * hkv * d + 2 * na * hkv * (d * d + 2 * d * h) + 4 * (na + win) * hq * d
@@ -128,17 +129,24 @@ def recorded_traffic(workload, kernel_src):
     return None
 
 
+def residual_row_bytes(cfg):
+    """Bytes of one stored residual: the value row (2-bit codes pack four per
+    byte), its int32 token index and, for int8 and 2-bit codes, a float32 scale."""
+    d = cfg.head_dim
+    row = {"f32": 4 * d, "bf16": 2 * d, "i8": d, "i2": d // 4}[cfg.res_dtype]
+    return row + 4 + (4 if cfg.res_dtype in ("i8", "i2") else 0)
+
+
 def stored_bytes(cfg):
     """Compressed cache bytes per sequence over all layers (factors, predictor,
     residuals with indices and block pointers) and the dense bf16 K+V bytes."""
     d, hkv, r, h, T = cfg.head_dim, cfg.n_kv_heads, cfg.rank, cfg.mlp_hidden, cfg.ctx_len
     ea = {"f32": 4, "bf16": 2, "i8": 1}[cfg.a_dtype]
-    er = {"f32": 4, "bf16": 2, "i8": 1}[cfg.res_dtype]
     ew = {"f32": 4, "bf16": 2}[cfg.act]
     groups = -(-cfg.n_layers // cfg.group)
     a = groups * T * (r * ea + (4 if cfg.a_dtype == "i8" else 0))
     per_layer = r * hkv * d * ew + hkv * (d * d + 2 * d * h) * ew
-    per_layer += hkv * cfg.n_res * (d * er + 4 + (4 if cfg.res_dtype == "i8" else 0)) + hkv * (cfg.nb + 1) * 4
+    per_layer += hkv * cfg.n_res * residual_row_bytes(cfg) + hkv * (cfg.nb + 1) * 4
     stored = a + cfg.n_layers * per_layer
     dense = cfg.n_layers * 2 * hkv * d * 2 * T
     return stored, dense
@@ -155,6 +163,8 @@ def main():
     import synth
 
     cfg = synth.CONFIGS[args.workload]
+    if args.res_dtype is not None:
+        cfg = cfg.replace(res_dtype=args.res_dtype)
     if args.batch:
         cfg = cfg.replace(batch=args.batch)
     dev = "cuda"
@@ -240,7 +250,7 @@ def main():
         "config": {"workload": args.workload, "batch": cfg.batch, "ctx_len": cfg.ctx_len,
                    "layers": cfg.n_layers, "rank": cfg.rank, "mlp_hidden": cfg.mlp_hidden,
                    "blocks_attended_per_layer": int(sum(c[0][0] for c in counts) / cfg.n_layers // cfg.block),
-                   "n_res": cfg.n_res, "window": win, "kernel": "generic-f32" if generic else "mfma-bf16"},
+                   "n_res": cfg.n_res, "res_dtype": cfg.res_dtype, "window": win, "kernel": "generic-f32" if generic else "mfma-bf16"},
         "hbm": {"algorithmic_bytes_per_step": step_bytes, "achieved_GBs": hbm_gbs,
                 "frac_of_8TBs": hbm_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "alu" if generic else "mfma", "achieved": achieved, "peak": peak,

@@ -47,6 +47,11 @@ extern "C" {
 #define LOWRAM_F32  0
 #define LOWRAM_BF16 1
 #define LOWRAM_I8   2   /* symmetric codes with a float32 scale per row */
+/* 2-bit residual codes (residuals only; explainer, comparison table: LowRAM
+ * combined with quantization stores 2-bit residuals). Four codes per byte,
+ * element i in bits 2(i mod 4) of byte i / 4, so a d-element row takes d / 4
+ * bytes; value (q - 1.5) s with a float32 scale s per row. */
+#define LOWRAM_I2   3
 
 /* Flags for lowram_decode_args.flags. */
 #define LOWRAM_FLAG_GENERIC 1  /* use the fp32 SIMT kernel even where the MFMA kernel applies */
@@ -81,7 +86,7 @@ typedef struct lowram_decode_args {
     int32_t win_cap;      /* rows allocated per sequence in win_k / win_v           */
     int32_t act_dtype;    /* F32 | BF16: q, b_l, w_*, b*, win_*, out                */
     int32_t a_dtype;      /* F32 | BF16 | I8                                        */
-    int32_t res_dtype;    /* F32 | BF16 | I8                                        */
+    int32_t res_dtype;    /* F32 | BF16 | I8 | I2                                   */
     int32_t flags;        /* LOWRAM_FLAG_*                                          */
 
     const void    *q;           /* [B, Hq, d]                                       */
@@ -94,8 +99,8 @@ typedef struct lowram_decode_args {
     const void    *w2;          /* [B, Hkv, d, h]                                   */
     const void    *b2;          /* [B, Hkv, d]  or NULL (= 0)                       */
     const int32_t *res_idx;     /* [B, Hkv, k] strictly ascending (NULL if k == 0) */
-    const void    *res_val;     /* [B, Hkv, k, d]                  (NULL if k == 0) */
-    const float   *res_scale;   /* [B, Hkv, k] int8 residuals only, else NULL       */
+    const void    *res_val;     /* [B, Hkv, k, d] (I2: [B, Hkv, k, d/4] bytes; NULL if k == 0) */
+    const float   *res_scale;   /* [B, Hkv, k] I8 / I2 residuals only, else NULL    */
     const int32_t *res_blk_ptr; /* [B, Hkv, nb+1] slots of block i: [p[i], p[i+1])  */
     const int32_t *sel;         /* [B, n_sel] ascending block indices, or NULL      */
     const uint8_t *keep;        /* [B, nb] 1 = kept, 0 = evicted, or NULL           */
@@ -134,20 +139,23 @@ size_t lowram_decode_workspace_size(const lowram_decode_args *args);
  *          stored in ascending order;
  *   R    = V - V_hat at those tokens, computed exactly in binary64 and stored
  *          as res_dtype: F32 / BF16 rounded to nearest-even in one step, or
- *          I8 with s = float32(max|R| / 127) and q = clamp(rint(R / s), +-127);
+ *          I8 with s = float32(max|R| / 127) and q = clamp(rint(R / s), +-127),
+ *          or I2 with s = float32(max|R| / 1.5) and
+ *          q = clamp(rint(R / s + 1.5), 0, 3) (q = 2 for a zero row), the
+ *          quotient and sum in binary64;
  *   ptr  = block CSR: ptr[i] = #{t in I : t < i * block_size}, ptr[nb] = n_res.
  */
 typedef struct lowram_rank_args {
     int32_t n_slices, ctx_len, n_kv_heads, head_dim, block_size, n_res;
     int32_t in_dtype;           /* F32 | BF16                                       */
-    int32_t res_dtype;          /* F32 | BF16 | I8                                  */
+    int32_t res_dtype;          /* F32 | BF16 | I8 | I2                             */
 
     const void *v;              /* [Lr, T, Hkv, d]                                  */
     const void *v_hat;          /* [Lr, T, Hkv, d]                                  */
 
     int32_t    *res_idx;        /* [Lr, Hkv, k]      (may be NULL when k == 0)      */
-    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype (NULL when k == 0)    */
-    float      *res_scale;      /* [Lr, Hkv, k]  I8 only, else NULL                 */
+    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype, I2: [.., d/4] bytes  */
+    float      *res_scale;      /* [Lr, Hkv, k]  I8 / I2 only, else NULL            */
     int32_t    *res_blk_ptr;    /* [Lr, Hkv, nb+1]                                  */
     double     *err;            /* [Lr, Hkv, T] or NULL (then kept in workspace)    */
 
@@ -187,7 +195,7 @@ typedef struct lowram_prefill_args {
     int32_t group;              /* layers per shared key factor: slice l uses a[l/group] */
     int32_t ctx_len, n_kv_heads, head_dim, rank, mlp_hidden, block_size, n_res;
     int32_t act_dtype;          /* BF16: a, b_l, weights, biases and v                */
-    int32_t res_dtype;          /* F32 | BF16 | I8                                    */
+    int32_t res_dtype;          /* F32 | BF16 | I8 | I2                               */
 
     const void *a;              /* [ceil(Lr/group), T, r]                             */
     const void *b_l;            /* [Lr, Hkv*d, r]                                     */
@@ -199,8 +207,8 @@ typedef struct lowram_prefill_args {
     const void *v;              /* [Lr, T, Hkv, d] true values                        */
 
     int32_t    *res_idx;        /* [Lr, Hkv, k]      (may be NULL when k == 0)        */
-    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype (NULL when k == 0)      */
-    float      *res_scale;      /* [Lr, Hkv, k]  I8 only, else NULL                   */
+    void       *res_val;        /* [Lr, Hkv, k, d]  res_dtype, I2: [.., d/4] bytes    */
+    float      *res_scale;      /* [Lr, Hkv, k]  I8 / I2 only, else NULL              */
     int32_t    *res_blk_ptr;    /* [Lr, Hkv, nb+1]                                    */
     double     *err;            /* [Lr, Hkv, T] or NULL (then kept in workspace)      */
     float      *v_hat;          /* [Lr, T, Hkv, d] fp32 copy of V_hat, or NULL        */

@@ -3,13 +3,13 @@ a compressed cache and the prefill-side residual ranking, as HIP kernels
 behind the C ABI declared in include/lowram.h. This package is the thin
 Python binding; build the library with
 ``python -m long_context_decode_lowram_amd.build``."""
-from ._binding import (BF16, F32, FLAG_GENERIC, I8, BLOCK, DecodeArgs, LowramError, PrefillArgs, RankArgs,
+from ._binding import (BF16, F32, FLAG_GENERIC, I2, I8, BLOCK, DecodeArgs, LowramError, PrefillArgs, RankArgs,
                        decode_launch, decode_step, decode_workspace_size, last_error, lib,
                        make_decode_args, make_prefill_args, make_rank_args, prefill_launch, prefill_rank,
                        prefill_workspace_size, rank_launch, rank_residuals, rank_workspace_size,
                        status_string)
 
-__all__ = ["BF16", "F32", "FLAG_GENERIC", "I8", "BLOCK", "DecodeArgs", "LowramError", "PrefillArgs", "RankArgs",
+__all__ = ["BF16", "F32", "FLAG_GENERIC", "I2", "I8", "BLOCK", "DecodeArgs", "LowramError", "PrefillArgs", "RankArgs",
            "decode_launch", "decode_step", "decode_workspace_size", "last_error", "lib",
            "make_decode_args", "make_prefill_args", "make_rank_args", "prefill_launch", "prefill_rank",
            "prefill_workspace_size", "rank_launch", "rank_residuals", "rank_workspace_size",

@@ -13,11 +13,13 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowram.so")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_WINDOW_FULL, ERR_EMPTY, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, I2 = 0, 1, 2, 3
 FLAG_GENERIC = 1
 BLOCK = 64
 
-_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+# uint8 tensors carry 2-bit codes packed four per byte (residual rows [.., d/4]).
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: I2}
+_RES_CODE = {"f32": F32, "bf16": BF16, "i8": I8, "i2": I2}
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int32
@@ -180,7 +182,7 @@ def make_rank_args(v, v_hat, n_res, res_dtype, res_idx, res_val, res_scale, res_
     args.n_slices, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, T, Hkv, d
     args.block_size, args.n_res = BLOCK, n_res
     args.in_dtype = _dt(v, "v")
-    args.res_dtype = {"f32": F32, "bf16": BF16, "i8": I8}[res_dtype]
+    args.res_dtype = _RES_CODE[res_dtype]
     for name, t in (("v", v), ("v_hat", v_hat), ("res_idx", res_idx), ("res_val", res_val),
                     ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("err", err),
                     ("workspace", workspace)):
@@ -204,19 +206,26 @@ def rank_launch(args, stream=None):
         raise LowramError(rc, last_error())
 
 
-_RES_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+_RES_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i2": torch.uint8}
+
+
+def _res_store(Lr, Hkv, n_res, d, res_dtype, dev):
+    """Residual value rows (i2: d/4 packed bytes) and per-row scales (i8, i2)."""
+    width = d // 4 if res_dtype == "i2" else d
+    val = torch.empty(Lr, Hkv, n_res, width, dtype=_RES_TORCH[res_dtype], device=dev)
+    scale = torch.empty(Lr, Hkv, n_res, dtype=torch.float32, device=dev) if res_dtype in ("i8", "i2") else None
+    return val, scale
 
 
 def rank_residuals(v, v_hat, n_res, res_dtype, *, want_err=False, workspace=None, stream=None):
     """Residual store for V, V_hat [Lr, T, Hkv, d]. Returns a dict with idx,
-    val, scale (int8 only), ptr and err (when ``want_err``)."""
+    val, scale (int8 and 2-bit only), ptr and err (when ``want_err``)."""
     Lr, T, Hkv, d = v.shape
     dev = v.device
     nb = -(-T // BLOCK)
     out = {
         "idx": torch.empty(Lr, Hkv, n_res, dtype=torch.int32, device=dev),
-        "val": torch.empty(Lr, Hkv, n_res, d, dtype=_RES_TORCH[res_dtype], device=dev),
-        "scale": torch.empty(Lr, Hkv, n_res, dtype=torch.float32, device=dev) if res_dtype == "i8" else None,
+        **dict(zip(("val", "scale"), _res_store(Lr, Hkv, n_res, d, res_dtype, dev))),
         "ptr": torch.empty(Lr, Hkv, nb + 1, dtype=torch.int32, device=dev),
         "err": torch.empty(Lr, Hkv, T, dtype=torch.float64, device=dev) if want_err else None,
     }
@@ -239,7 +248,7 @@ def make_prefill_args(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, res_idx, res_v
     args.n_slices, args.group, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, group, T, Hkv, d
     args.rank, args.mlp_hidden, args.block_size, args.n_res = a.shape[-1], w1.shape[-2], BLOCK, n_res
     args.act_dtype = _dt(v, "v")
-    args.res_dtype = {"f32": F32, "bf16": BF16, "i8": I8}[res_dtype]
+    args.res_dtype = _RES_CODE[res_dtype]
     for name, t in (("a", a), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1), ("b1", b1), ("w2", w2),
                     ("b2", b2), ("v", v), ("res_idx", res_idx), ("res_val", res_val),
                     ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("err", err),
@@ -274,8 +283,7 @@ def prefill_rank(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, *, group=4, b1=None
     nb = -(-T // BLOCK)
     out = {
         "idx": torch.empty(Lr, Hkv, n_res, dtype=torch.int32, device=dev),
-        "val": torch.empty(Lr, Hkv, n_res, d, dtype=_RES_TORCH[res_dtype], device=dev),
-        "scale": torch.empty(Lr, Hkv, n_res, dtype=torch.float32, device=dev) if res_dtype == "i8" else None,
+        **dict(zip(("val", "scale"), _res_store(Lr, Hkv, n_res, d, res_dtype, dev))),
         "ptr": torch.empty(Lr, Hkv, nb + 1, dtype=torch.int32, device=dev),
         "err": torch.empty(Lr, Hkv, T, dtype=torch.float64, device=dev) if want_err else None,
         "v_hat": torch.empty(Lr, T, Hkv, d, dtype=torch.float32, device=dev) if want_v_hat else None,

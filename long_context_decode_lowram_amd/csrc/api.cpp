@@ -45,7 +45,7 @@ int plan_decode(const lowram_decode_args* a, DecodePlan* pl) {
         return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 16 in [16, 1024] (got %d)", a->mlp_hidden);
     if (a->act_dtype != LOWRAM_F32 && a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_ARG, "act_dtype must be F32 or BF16");
     if (a->a_dtype < LOWRAM_F32 || a->a_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad a_dtype");
-    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I2) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
     if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
     if (a->win_len < 0 || a->win_cap < 0) return fail(LOWRAM_ERR_ARG, "win_len and win_cap must be >= 0");
     if (a->win_len > a->win_cap) return fail(LOWRAM_ERR_WINDOW_FULL, "win_len (%d) > win_cap (%d)", a->win_len, a->win_cap);
@@ -82,7 +82,8 @@ int check_decode_ptrs(const lowram_decode_args* a, const DecodePlan& pl) {
         return fail(LOWRAM_ERR_ARG, "q, a, b_l, w_lin, w1, w2, res_blk_ptr and out must be non-NULL");
     if (a->n_res > 0 && (!a->res_idx || !a->res_val)) return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
     if (a->a_dtype == LOWRAM_I8 && !a->a_scale) return fail(LOWRAM_ERR_ARG, "int8 A needs a_scale");
-    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale) return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    if ((a->res_dtype == LOWRAM_I8 || a->res_dtype == LOWRAM_I2) && a->n_res > 0 && !a->res_scale)
+        return fail(LOWRAM_ERR_ARG, "int8 and 2-bit residuals need res_scale");
     if (a->win_len > 0 && (!a->win_k || !a->win_v)) return fail(LOWRAM_ERR_ARG, "win_k and win_v must be non-NULL when win_len > 0");
     const void* v16[] = {a->q, a->a, a->b_l, a->w_lin, a->w1, a->w2, a->res_val, a->win_k, a->win_v, a->out, a->workspace};
     for (const void* p : v16)
@@ -105,7 +106,7 @@ int plan_rank(const lowram_rank_args* a, RankPlan* pl) {
     if (a->block_size != kBlock) return fail(LOWRAM_ERR_UNSUPPORTED, "block_size must be 64 (got %d)", a->block_size);
     if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
     if (a->in_dtype != LOWRAM_F32 && a->in_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_ARG, "in_dtype must be F32 or BF16");
-    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I2) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
     pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
     const size_t nseg = (size_t)a->n_slices * a->n_kv_heads;
     pl->off_err = 0;
@@ -131,7 +132,7 @@ int plan_prefill(const lowram_prefill_args* a, PrefillPlan* pl) {
         return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * rank * 2 must stay below 2^31");
     if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
     if (a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_UNSUPPORTED, "act_dtype must be BF16");
-    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I8) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
+    if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I2) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
     pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
     const size_t nseg = (size_t)a->n_slices * a->n_kv_heads;
     pl->off_err = 0;
@@ -226,8 +227,8 @@ int lowram_rank_residuals(const lowram_rank_args* a, void* stream) {
         return fail(LOWRAM_ERR_ARG, "v, v_hat and res_blk_ptr must be non-NULL");
     if (a->n_res > 0 && (!a->res_idx || !a->res_val))
         return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
-    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale)
-        return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    if ((a->res_dtype == LOWRAM_I8 || a->res_dtype == LOWRAM_I2) && a->n_res > 0 && !a->res_scale)
+        return fail(LOWRAM_ERR_ARG, "int8 and 2-bit residuals need res_scale");
     const void* v16[] = {a->v, a->v_hat, a->res_val, a->workspace};
     for (const void* p : v16)
         if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
@@ -277,8 +278,8 @@ int lowram_prefill_rank(const lowram_prefill_args* a, void* stream) {
         return fail(LOWRAM_ERR_ARG, "a, b_l, w_lin, w1, w2, v and res_blk_ptr must be non-NULL");
     if (a->n_res > 0 && (!a->res_idx || !a->res_val))
         return fail(LOWRAM_ERR_ARG, "res_idx and res_val must be non-NULL when n_res > 0");
-    if (a->res_dtype == LOWRAM_I8 && a->n_res > 0 && !a->res_scale)
-        return fail(LOWRAM_ERR_ARG, "int8 residuals need res_scale");
+    if ((a->res_dtype == LOWRAM_I8 || a->res_dtype == LOWRAM_I2) && a->n_res > 0 && !a->res_scale)
+        return fail(LOWRAM_ERR_ARG, "int8 and 2-bit residuals need res_scale");
     const void* v16[] = {a->a, a->b_l, a->w_lin, a->w1, a->w2, a->v, a->res_val, a->v_hat, a->workspace};
     for (const void* p : v16)
         if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);

@@ -6,7 +6,10 @@
 
 namespace lowram {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_I2 = 3 };
+
+// Residual encodings that carry a per-row scale (int8 codes, 2-bit codes).
+constexpr bool res_scaled(int dt) { return dt == DT_I8 || dt == DT_I2; }
 
 constexpr int kHeadDim = 128;   // head_dim the kernels are built for
 constexpr int kBlock = 64;      // tokens per cache block
@@ -51,6 +54,12 @@ template <> __device__ __forceinline__ float ld<DT_BF16>(const void* p, int64_t 
 }
 template <> __device__ __forceinline__ float ld<DT_I8>(const void* p, int64_t i) {
     return static_cast<float>(static_cast<const int8_t*>(p)[i]);
+}
+// 2-bit codes, four per byte (element i in bits 2(i mod 4) of byte i / 4):
+// returns the unscaled level q - 1.5.
+template <> __device__ __forceinline__ float ld<DT_I2>(const void* p, int64_t i) {
+    const unsigned b = static_cast<const uint8_t*>(p)[i >> 2];
+    return static_cast<float>((b >> (2 * (i & 3))) & 3u) - 1.5f;
 }
 
 template <int DT> __device__ __forceinline__ void st(void* p, int64_t i, float v);

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
                     const int tl = p.res_idx[res_row + q] - t0;
                     if (tl < 0 || tl >= nt) continue;
                     float rv = ld<RDT>(p.res_val, (res_row + q) * kHeadDim + (f - H));
-                    if (RDT == DT_I8) rv *= p.res_scale[res_row + q];
+                    if (res_scaled(RDT)) rv *= p.res_scale[res_row + q];
                     o += Ps[jj * kBlock + tl] * rv;
                 }
             }
@@ -162,7 +162,8 @@ static hipError_t launch_r(const DecodeParams& p, int rdt, hipStream_t s) {
     switch (rdt) {
         case DT_F32: hipLaunchKernelGGL((decode_generic_kernel<ACT, ADT, DT_F32>), grid, dim3(kThreads), 0, s, p); break;
         case DT_BF16: hipLaunchKernelGGL((decode_generic_kernel<ACT, ADT, DT_BF16>), grid, dim3(kThreads), 0, s, p); break;
-        default: hipLaunchKernelGGL((decode_generic_kernel<ACT, ADT, DT_I8>), grid, dim3(kThreads), 0, s, p); break;
+        case DT_I8: hipLaunchKernelGGL((decode_generic_kernel<ACT, ADT, DT_I8>), grid, dim3(kThreads), 0, s, p); break;
+        default: hipLaunchKernelGGL((decode_generic_kernel<ACT, ADT, DT_I2>), grid, dim3(kThreads), 0, s, p); break;
     }
     return hipGetLastError();
 }

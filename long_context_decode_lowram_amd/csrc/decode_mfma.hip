@@ -155,21 +155,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // The block's residual rows are consecutive rows of res_val. Each wave
     // copies up to kResRows of them at a time into its 4 KB of sres; the first
     // batch starts here, so it lands while the keys are rebuilt.
-    constexpr int kResRowB = kHeadDim * (RDT == DT_F32 ? 4 : (RDT == DT_BF16 ? 2 : 1));
-    constexpr int kResRows = 4096 / kResRowB;            // 8 (f32), 16 (bf16), 32 (int8)
+    constexpr int kResRowB = RDT == DT_I2 ? kHeadDim / 4 : kHeadDim * (RDT == DT_F32 ? 4 : (RDT == DT_BF16 ? 2 : 1));
+    // 8 (f32), 16 (bf16), 32 (int8), 64 (2-bit: one row per lane holds the tokens)
+    constexpr int kResRows = 4096 / kResRowB < kWave ? 4096 / kResRowB : kWave;
+    constexpr int kResPieces = kResRows * kResRowB / 1024;
     unsigned char* const rs_w = sres + w * 4096;
     auto dma_res = [&](int q0) {
         const int n = min(kResRows, hi - q0);
         const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(
             static_cast<const unsigned char*>(p.res_val) + (res_row + q0) * (int64_t)kResRowB, (uint32_t)(n * kResRowB));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dma16(rr, rs_w + q * 1024, (uint32_t)(q * 1024 + lane * 16), 0u);
+        for (int q = 0; q < kResPieces; ++q) dma16(rr, rs_w + q * 1024, (uint32_t)(q * 1024 + lane * 16), 0u);
     };
     // Token (relative to the block) and int8 scale of residual row q0 + lane.
     auto res_meta = [&](int q0, int& tok, float& scl) {
         const int n = min(kResRows, hi - q0);
         tok = lane < n ? p.res_idx[res_row + q0 + lane] - t0 : -1;
-        scl = (RDT == DT_I8 && lane < n) ? p.res_scale[res_row + q0 + lane] : 1.f;
+        scl = (res_scaled(RDT) && lane < n) ? p.res_scale[res_row + q0 + lane] : 1.f;
     };
     int tok0 = -1;
     float scl0 = 1.f;
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 const bool ok = r < n && t >= 0 && t < nt;
                 applied += ok ? 1 : 0;
                 const int tc = ok ? t : 0;
-                const float wr = RDT == DT_I8 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), r)) : 1.f;
+                const float wr = res_scaled(RDT) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), r)) : 1.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = 4 * g4 + i;
@@ -476,7 +478,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                     const int f = ft * 16 + l16;
                     if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
                     else if (RDT == DT_BF16) v[u][ft] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rs_w + r * kResRowB + f * 2));
-                    else v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
+                    else if (RDT == DT_I8) v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
+                    else v[u][ft] = static_cast<float>((rs_w[r * kResRowB + (f >> 2)] >> (2 * (f & 3))) & 3u) - 1.5f;
                 }
             }
 #pragma unroll
@@ -603,7 +606,8 @@ static hipError_t launch_r(const DecodeParams& p, int rdt, hipStream_t s) {
     switch (rdt) {
         case DT_F32: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_F32>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
         case DT_BF16: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_BF16>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
-        default: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_I8>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
+        case DT_I8: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_I8>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
+        default: hipLaunchKernelGGL((decode_mfma_kernel<ADT, DT_I2>), grid, dim3(kThreads), 0, s, p, n_split_pad); break;
     }
     return hipGetLastError();
 }

@@ -358,7 +358,37 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
                 }
             }
             const int64_t o = (lh * p.n_res + s) * kHeadDim + 4 * g4;
-            if (RDT == DT_I8) {
+            if (RDT == DT_I2) {
+                // Symmetric mid-rise 4-level code; the lane's four features
+                // 16 ot + 4 g4 .. + 3 are exactly byte 4 ot + g4 of the row.
+                double amax = 0.0;
+#pragma unroll
+                for (int ot = 0; ot < 8; ++ot)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) amax = fmax(amax, fabs(rr[ot][i]));
+                amax = fmax(amax, __shfl_xor(amax, 16, kWave));
+                amax = fmax(amax, __shfl_xor(amax, 32, kWave));
+                const float sc = static_cast<float>(amax / 1.5);
+                const double s64 = static_cast<double>(sc);
+                if (t >= 0) {
+                    uint8_t* const dst = static_cast<uint8_t*>(p.res_val) + (lh * p.n_res + s) * (kHeadDim / 4) + g4;
+#pragma unroll
+                    for (int ot = 0; ot < 8; ++ot) {
+                        uint32_t byte = 0u;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            double q = 2.0;
+                            if (s64 > 0.0) {
+                                q = rint(rr[ot][i] / s64 + 1.5);
+                                q = q > 3.0 ? 3.0 : (q < 0.0 ? 0.0 : q);
+                            }
+                            byte |= (uint32_t)q << (2 * i);
+                        }
+                        dst[ot * 4] = (uint8_t)byte;
+                    }
+                    if (g4 == 0) p.res_scale[lh * p.n_res + s] = sc;
+                }
+            } else if (RDT == DT_I8) {
                 double amax = 0.0;
 #pragma unroll
                 for (int ot = 0; ot < 8; ++ot)
@@ -418,8 +448,10 @@ hipError_t launch_prefill(const PrefillParams& p, int mode, hipStream_t s) {
         hipLaunchKernelGGL((prefill_mfma_kernel<1, DT_F32>), grid, dim3(kPThreads), 0, s, p, pad);
     } else if (p.res_dtype == DT_BF16) {
         hipLaunchKernelGGL((prefill_mfma_kernel<1, DT_BF16>), grid, dim3(kPThreads), 0, s, p, pad);
-    } else {
+    } else if (p.res_dtype == DT_I8) {
         hipLaunchKernelGGL((prefill_mfma_kernel<1, DT_I8>), grid, dim3(kPThreads), 0, s, p, pad);
+    } else {
+        hipLaunchKernelGGL((prefill_mfma_kernel<1, DT_I2>), grid, dim3(kPThreads), 0, s, p, pad);
     }
     return hipGetLastError();
 }

@@ -368,7 +368,28 @@ __device__ __forceinline__ void load_row8(const void* base, int64_t e0, double (
 template <int RDT>
 __device__ __forceinline__ void store_res8(const RankParams& p, int64_t gid, int j, const double (&d)[8]) {
     const int64_t o = gid * kHeadDim + 8 * j;
-    if (RDT == DT_F32) {
+    if (RDT == DT_I2) {
+        // Symmetric mid-rise 4-level code: s = f32(amax / 1.5),
+        // q = clamp(rint(r / s + 1.5), 0, 3) in binary64; a zero row is level 2.
+        double amax = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmax(amax, fabs(d[k]));
+        for (int off = 8; off > 0; off >>= 1) amax = fmax(amax, __shfl_xor(amax, off, kWave));
+        const float s = static_cast<float>(amax / 1.5);
+        const double s64 = static_cast<double>(s);
+        uint32_t w = 0u;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            double q = 2.0;
+            if (s64 > 0.0) {
+                q = rint(d[k] / s64 + 1.5);
+                q = q > 3.0 ? 3.0 : (q < 0.0 ? 0.0 : q);
+            }
+            w |= (uint32_t)q << (2 * k);
+        }
+        *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.res_val) + gid * (kHeadDim / 4) + 2 * j) = (uint16_t)w;
+        if (j == 0) p.res_scale[gid] = s;
+    } else if (RDT == DT_F32) {
         float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.res_val) + o);
         dst[0] = make_float4((float)d[0], (float)d[1], (float)d[2], (float)d[3]);
         dst[1] = make_float4((float)d[4], (float)d[5], (float)d[6], (float)d[7]);
@@ -431,11 +452,13 @@ hipError_t launch_rank_gather(const RankParams& p, hipStream_t s) {
     if (p.in_dtype == DT_F32) {
         if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_F32>), grid, dim3(256), 0, s, p, n_slots);
         else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_BF16>), grid, dim3(256), 0, s, p, n_slots);
-        else hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
+        else if (p.res_dtype == DT_I8) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
+        else hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_I2>), grid, dim3(256), 0, s, p, n_slots);
     } else {
         if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_F32>), grid, dim3(256), 0, s, p, n_slots);
         else if (p.res_dtype == DT_BF16) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_BF16>), grid, dim3(256), 0, s, p, n_slots);
-        else hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
+        else if (p.res_dtype == DT_I8) hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_I8>), grid, dim3(256), 0, s, p, n_slots);
+        else hipLaunchKernelGGL((rank_gather_kernel<DT_BF16, DT_I2>), grid, dim3(256), 0, s, p, n_slots);
     }
     return hipGetLastError();
 }

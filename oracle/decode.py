@@ -11,6 +11,8 @@ import math
 import numpy as np
 from scipy.special import erf
 
+from .rank import dequantize_i2_rows, unpack_i2
+
 
 def gelu(x):
     """GELU in its exact error-function form, 0.5*x*(1 + erf(x/sqrt(2))).
@@ -29,6 +31,15 @@ def _f64(x, scale=None):
     if scale is not None:
         y = y * np.asarray(scale).astype(np.float64)[..., None]
     return y
+
+
+def _residual_rows(val, scale):
+    """Stored residual rows as float64: uint8 rows are 2-bit codes packed four
+    per byte ((q - 1.5) s), int8 rows are q s, float rows are exact."""
+    val = np.asarray(val)
+    if val.dtype == np.uint8:
+        return dequantize_i2_rows(unpack_i2(val), scale)
+    return _f64(val, scale)
 
 
 def reconstruct_keys(a_rows, bl):
@@ -131,7 +142,7 @@ def decode_batch_element(q, a, bl, w_lin, w1, w2, res_idx, res_val, *, block,
         k_h = keys_all[:, h * d:(h + 1) * d]
         v_h = predict_values(k_h, w_lin[h], w1[h], w2[h],
                              None if b1 is None else b1[h], None if b2 is None else b2[h])
-        rv = _f64(res_val[h], None if res_scale is None else res_scale[h])
+        rv = _residual_rows(res_val[h], None if res_scale is None else res_scale[h])
         rows = pos[np.asarray(res_idx[h], dtype=np.int64)] if tau.size else np.full(len(res_idx[h]), -1)
         hit = rows >= 0
         v_h[rows[hit]] += rv[hit]

@@ -36,7 +36,7 @@ class DecodeConfig:
     sel_den: int               # 1 = every block, else n_sel = nb / sel_den
     act: str                   # 'f32' | 'bf16'  (q, factors, weights, window, out)
     a_dtype: str               # 'f32' | 'bf16' | 'i8'
-    res_dtype: str             # 'f32' | 'bf16' | 'i8'
+    res_dtype: str             # 'f32' | 'bf16' | 'i8' | 'i2'
     evict_half: bool = False
     win_cap: int = 0
     steps: int = 1
@@ -154,6 +154,16 @@ def _int8_rows(shape, std, device, g):
     return codes.to(torch.int8), scale.to(torch.float32)
 
 
+def _i2_rows(shape, std, device, g):
+    """2-bit codes packed four per byte ([..., d/4] uint8, every byte value
+    equally likely) with a float32 scale per row around std / 1.118 (the rms
+    of the levels -1.5, -0.5, 0.5, 1.5 is 1.118)."""
+    packed = torch.randint(0, 256, shape[:-1] + (shape[-1] // 4,), generator=g, device=device,
+                           dtype=torch.int32)
+    scale = torch.rand(shape[:-1], generator=g, device=device).add_(0.5).mul_(std / 1.118)
+    return packed.to(torch.uint8), scale.to(torch.float32)
+
+
 def gen_group_factor(cfg, group, device, batch=None):
     """The shared key factor A of one layer group: [B, T, r] in ``cfg.a_dtype``
     (int8 codes plus a [B, T] float32 scale for 'i8')."""
@@ -242,6 +252,8 @@ def gen_layer(cfg, layer, device, *, step=0, batch=None, biases=False, res_idx=N
     gr = make_generator(device, cfg.seed, "res_val", layer)
     if cfg.res_dtype == "i8":
         out["res_val"], out["res_scale"] = _int8_rows((bsz, hkv, k, d), 0.05, device, gr)
+    elif cfg.res_dtype == "i2":
+        out["res_val"], out["res_scale"] = _i2_rows((bsz, hkv, k, d), 0.05, device, gr)
     else:
         out["res_val"] = _normal((bsz, hkv, k, d), 0.05, _DT[cfg.res_dtype], device, gr)
         out["res_scale"] = None

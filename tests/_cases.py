@@ -37,6 +37,9 @@ def set_residuals(case, cfg, idx):
     if cfg.res_dtype == "i8":
         case["res_val"] = torch.randint(-127, 128, (bsz, hkv, k, 128), generator=g).to(torch.int8).to(dev)
         case["res_scale"] = (torch.rand(bsz, hkv, k, generator=g) * 1e-3 + 1e-4).to(dev)
+    elif cfg.res_dtype == "i2":
+        case["res_val"] = torch.randint(0, 256, (bsz, hkv, k, 32), generator=g, dtype=torch.int32).to(torch.uint8).to(dev)
+        case["res_scale"] = (torch.rand(bsz, hkv, k, generator=g) * 0.05 + 0.01).to(dev)
     else:
         dt = torch.float32 if cfg.res_dtype == "f32" else torch.bfloat16
         case["res_val"] = (torch.randn(bsz, hkv, k, 128, generator=g) * 0.05).to(dt).to(dev)

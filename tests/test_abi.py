@@ -39,6 +39,15 @@ def test_header_struct_layout_matches_binding():
     assert fields == [f[0] for f in B.RankArgs._fields_]
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+LOWRAM_([A-Z0-9_]+)\s+(-?\d+)", text))
+    for name in ("F32", "BF16", "I8", "I2", "FLAG_GENERIC"):
+        assert int(defs[name]) == getattr(B, name), name
+    for name in ("OK", "ERR_ARG", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_WINDOW_FULL", "ERR_EMPTY", "ERR_HIP"):
+        assert int(defs[name]) == getattr(B, name), name
+
+
 def test_status_strings():
     codes = [0, -1, -2, -3, -4, -5, -6]
     strs = [L.status_string(c) for c in codes]
@@ -91,6 +100,8 @@ def test_decode_valid_args_stop_at_workspace():
     ("batch", 0, B.ERR_ARG),
     ("a_dtype", B.I8, B.ERR_ARG),               # int8 A without a_scale
     ("res_dtype", B.I8, B.ERR_ARG),             # int8 residuals without res_scale
+    ("res_dtype", B.I2, B.ERR_ARG),             # 2-bit residuals without res_scale
+    ("res_dtype", 4, B.ERR_ARG),
 ])
 def test_decode_rejects(field, value, status):
     a = valid_decode()
@@ -145,6 +156,7 @@ def test_rank_valid_args_stop_at_workspace():
     ("v", None, B.ERR_ARG), ("res_idx", None, B.ERR_ARG), ("res_val", None, B.ERR_ARG),
     ("head_dim", 96, B.ERR_UNSUPPORTED), ("block_size", 128, B.ERR_UNSUPPORTED),
     ("n_res", 1001, B.ERR_ARG), ("in_dtype", B.I8, B.ERR_ARG), ("res_dtype", B.I8, B.ERR_ARG),
+    ("res_dtype", B.I2, B.ERR_ARG), ("res_dtype", 4, B.ERR_ARG), ("in_dtype", B.I2, B.ERR_ARG),
     ("n_slices", 0, B.ERR_ARG), ("v_hat", FAKE + 2, B.ERR_ARG),
 ])
 def test_rank_rejects(field, value, status):
@@ -191,6 +203,7 @@ def test_prefill_valid_args_stop_at_workspace():
     ("rank", 96, B.ERR_UNSUPPORTED), ("mlp_hidden", 96, B.ERR_UNSUPPORTED), ("act_dtype", B.F32, B.ERR_UNSUPPORTED),
     ("ctx_len", 1 << 22, B.ERR_UNSUPPORTED),       # ctx_len * rank * 2 reaches 2^31
     ("n_res", 1001, B.ERR_ARG), ("res_dtype", B.I8, B.ERR_ARG), ("group", 0, B.ERR_ARG),
+    ("res_dtype", B.I2, B.ERR_ARG), ("res_dtype", 4, B.ERR_ARG),
 ])
 def test_prefill_rejects(field, value, status):
     a = valid_prefill()

@@ -22,6 +22,9 @@ SMALL = {
     "bf16_r1024_sel": C4.replace(ctx_len=64 * 96 + 50, batch=2, win_cap=64),
     "i8_keep": C5.replace(ctx_len=64 * 48 + 5, batch=3),
     "f32_a_bf16_res": C1.replace(ctx_len=1000, res_dtype="bf16", a_dtype="bf16"),
+    "i2_keep": C5.replace(ctx_len=64 * 48 + 5, batch=3, res_dtype="i2"),
+    "bf16_i2_sel": C2.replace(ctx_len=64 * 40 + 9, batch=2, res_dtype="i2"),
+    "f32_i2": C1.replace(ctx_len=1000, res_dtype="i2"),
 }
 
 
@@ -57,13 +60,31 @@ def test_peaked_attention(generic):
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
 def test_no_residuals_and_every_token_a_residual(generic):
-    for cfg in (SMALL["f32_ragged"], SMALL["bf16_sel"], SMALL["i8_keep"]):
+    for cfg in (SMALL["f32_ragged"], SMALL["bf16_sel"], SMALL["i8_keep"], SMALL["i2_keep"]):
         case = make_case(cfg, layer=0)
         bsz = case["q"].shape[0]
         set_residuals(case, cfg, torch.zeros(bsz, 8, 0, dtype=torch.int32))
         check(case, cfg, generic=generic)
         set_residuals(case, cfg, torch.arange(cfg.ctx_len, dtype=torch.int32).expand(bsz, 8, -1))
         check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+@pytest.mark.parametrize("name", ["i2_keep", "f32_i2"])
+def test_two_bit_residuals_carry_the_output(name, generic):
+    """Every token holds a 2-bit residual of about the values' size, so the
+    output moves by far more than the tolerance if a code is decoded from the
+    wrong bits, with the wrong level offset or without its scale."""
+    cfg = SMALL[name]
+    case = make_case(cfg, layer=7)
+    bsz = case["q"].shape[0]
+    set_residuals(case, cfg, torch.arange(cfg.ctx_len, dtype=torch.int32).expand(bsz, 8, -1))
+    case["res_scale"] = case["res_scale"] * 20.0
+    ref, _ = oracle_decode(case)
+    plain = dict(case, res_scale=torch.zeros_like(case["res_scale"]))
+    ref0, _ = oracle_decode(plain)
+    assert rel_err(ref0, ref) > 10 * TOL[cfg.act]
+    check(case, cfg, generic=generic)
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])

@@ -226,6 +226,31 @@ def test_brute_force_int8_keep_and_no_bias():
     assert not out.any() and stats.tolist() == [[0, 0], [0, 0]]
 
 
+def test_brute_force_two_bit_residuals():
+    """Packed 2-bit residual rows in the decode: the scalar decoder reads each
+    code with plain bit operations, element o in bits 2(o mod 4) of byte
+    o // 4, and applies (q - 1.5) s."""
+    rng = np.random.default_rng(6)
+    case = _tiny_case(rng, 150)
+    n_kv, k, d = case["rv"].shape
+    packed = rng.integers(0, 256, (n_kv, k, d // 4)).astype(np.uint8)
+    scale = rng.uniform(0.05, 0.2, (n_kv, k)).astype(np.float32)
+    levels = [[[((int(packed[h, p, o // 4]) >> (2 * (o % 4))) & 3) - 1.5 for o in range(d)]
+               for p in range(k)] for h in range(n_kv)]
+    wk = rng.standard_normal((1, n_kv * d))
+    wv = rng.standard_normal((1, n_kv * d))
+    got, gstats = oracle.decode_batch_element(
+        case["q"], case["a"], case["bl"], case["w_lin"], case["w1"], case["w2"], case["idx"], packed,
+        block=64, b1=case["b1"], b2=case["b2"], res_scale=scale, win_k=wk, win_v=wv)
+    tl = lambda x: None if x is None else np.asarray(x, np.float64).tolist()  # noqa: E731
+    ref, rstats = _brute_decode(
+        tl(case["q"]), tl(case["a"]), None, tl(case["bl"]), tl(case["w_lin"]), tl(case["w1"]), tl(case["b1"]),
+        tl(case["w2"]), tl(case["b2"]), case["idx"].tolist(), levels, tl(scale), None, None,
+        wk.tolist(), wv.tolist(), 64)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-11, atol=1e-12)
+    assert gstats.tolist() == rstats
+
+
 # ------------------------------------------------------------ invariants
 def test_selection_invariants():
     rng = np.random.default_rng(6)

@@ -52,7 +52,7 @@ def _check_segment(x, out, pc, res_dtype, l, h):
     np.testing.assert_array_equal(out["err"][l, h].cpu().numpy(), ref["err"][0, 0])
     np.testing.assert_array_equal(out["idx"][l, h].cpu().numpy(), ref["idx"][0, 0])
     np.testing.assert_array_equal(out["ptr"][l, h].cpu().numpy(), ref["ptr"][0, 0])
-    if res_dtype == "i8":
+    if res_dtype in ("i8", "i2"):
         np.testing.assert_array_equal(out["val"][l, h].cpu().numpy(), ref["val"][0, 0])
         np.testing.assert_array_equal(out["scale"][l, h].cpu().numpy(), ref["scale"][0, 0])
     else:
@@ -60,7 +60,7 @@ def _check_segment(x, out, pc, res_dtype, l, h):
     return rel.max()
 
 
-@pytest.mark.parametrize("res_dtype", ["bf16", "f32", "i8"])
+@pytest.mark.parametrize("res_dtype", ["bf16", "f32", "i8", "i2"])
 def test_small_ragged_all_segments(res_dtype):
     pc = synth.PREFILL_CONFIGS["p_small_ragged"]          # T = 1000: a partial last block
     x, out = _launch(pc, res_dtype)

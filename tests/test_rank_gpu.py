@@ -26,7 +26,7 @@ def compare(got, ref, res_dtype, segs=None):
         assert np.array_equal(got["err"][gs].numpy().view(np.uint64), ref["err"][rs].view(np.uint64))
         np.testing.assert_array_equal(got["idx"][gs].numpy(), ref["idx"][rs])
         np.testing.assert_array_equal(got["ptr"][gs].numpy(), ref["ptr"][rs])
-        if res_dtype == "i8":
+        if res_dtype in ("i8", "i2"):
             np.testing.assert_array_equal(got["val"][gs].numpy(), ref["val"][rs])
             np.testing.assert_array_equal(got["scale"][gs].numpy(), ref["scale"][rs])
         else:
@@ -34,7 +34,7 @@ def compare(got, ref, res_dtype, segs=None):
 
 
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("res_dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("res_dtype", ["f32", "bf16", "i8", "i2"])
 def test_small_exact(in_dtype, res_dtype):
     rc = synth.RankConfig(3, 64 * 30 + 21, n_kv_heads=4, in_dtype=in_dtype, res_dtype=res_dtype)
     v, vh = synth.gen_rank_inputs(rc, "cpu")
@@ -52,6 +52,26 @@ def test_all_errors_equal_and_zero():
     got = gpu_rank(vh, vh, 50, "bf16")              # every error zero: lowest indices, zero residuals
     assert got["idx"][0, 1].tolist() == list(range(50))
     assert not got["val"].float().abs().sum().item()
+
+
+def test_two_bit_ties_and_zero_rows():
+    """Residuals on the 2-bit rounding boundaries: with max|R| = 1.5 c and
+    c = 2^-4 the scale is c exactly, so R = -c, 0, c give r/s + 1.5 = 0.5,
+    1.5, 2.5, which round to the even codes 0, 2, 2; a zero row stores code 2
+    and scale 0."""
+    c = 2.0 ** -4
+    row = np.resize(np.array([1.5, -1.5, -1.0, 0.0, 1.0, 0.5, -0.5, 0.25]) * c, 128)
+    v = torch.zeros(1, 200, 2, 128, dtype=torch.float32)
+    v[0, 7, 0] = torch.from_numpy(row)
+    v[0, 9, 1] = torch.from_numpy(-row)
+    vh = torch.zeros_like(v)
+    got = gpu_rank(v, vh, 3, "i2")
+    ref = oracle.rank_residuals(np64(v), np64(vh), 3, 64, "i2")
+    compare(got, ref, "i2")
+    q = oracle.unpack_i2(got["val"][0, 0, 1].numpy())
+    assert got["idx"][0, 0].tolist() == [0, 1, 7] and got["scale"][0, 0, 2].item() == c
+    assert oracle.unpack_i2(got["val"][0, 0, 2].numpy())[:8].tolist() == [3, 0, 0, 2, 2, 2, 1, 2]
+    assert q.tolist() == [2] * 128 and got["scale"][0, 0, 1].item() == 0.0
 
 
 def test_c5_full_shape_sampled_segments():
