@@ -1,8 +1,8 @@
 """Oracle helpers that produce the path's factor inputs (float64).
 
-Test infrastructure only (see the package docstring). These are not on the
-decode path; they exist so the pins can drive the decode oracle with factors
-whose exact result is known.
+Test infrastructure only (see the package docstring). ``xkv_factorize`` and
+``pinv_value_map`` are the plain definitions; ``xkv_subspace_iteration`` is
+the iterative prefill step the library runs, written out step by step.
 """
 import numpy as np
 
@@ -35,3 +35,32 @@ def pinv_value_map(w_k, w_v):
     square and invertible. W_K, W_V are [hidden, d] in the row-vector
     convention; the result is returned output-major ([d_out, d_in])."""
     return (np.linalg.pinv(np.asarray(w_k, np.float64)) @ np.asarray(w_v, np.float64)).T
+
+
+def xkv_subspace_iteration(keys, rank, omega, n_iter):
+    """Cross-layer key factors by randomized subspace iteration.
+
+    The factors of ``xkv_factorize`` (project site, Figure 3; explainer, keys
+    paragraph: one basis for a group of adjacent layers) computed the way the
+    library does: Halko, Martinsson and Tropp, "Finding structure with
+    randomness" (SIAM Review 2011), Algorithm 4.4, run on the row space. With
+    C = [K_1 | ... | K_G] (T x n) and its Gram matrix M = C^T C:
+        X_0 = omega  (n x r, the caller's Gaussian draw),
+        X_i = orth(M X_{i-1})  for i = 1 .. n_iter,
+        A   = C X_q,   B_l = (rows l*D .. l*D+D-1 of X_q)^T,
+    so K_l ~ A B_l with K_l's reconstruction C X_q X_q^T restricted to layer
+    l's columns. orth returns an orthonormal basis of the span (Householder
+    QR here); the span, hence A B_l, does not depend on which basis.
+
+    ``keys`` is a list of G arrays [T, D]. Returns (A [T, r], [bl_l] with
+    bl_l = B_l^T [D, r], X_q [n, r])."""
+    cat = np.concatenate([np.asarray(k, np.float64) for k in keys], axis=1)
+    m = cat.T @ cat
+    x = np.asarray(omega, np.float64)
+    assert x.shape == (cat.shape[1], rank) and n_iter >= 1
+    for _ in range(n_iter):
+        x = np.linalg.qr(m @ x)[0]
+    a = cat @ x
+    width = np.asarray(keys[0]).shape[1]
+    bls = [x[l * width:(l + 1) * width].copy() for l in range(len(keys))]
+    return a, bls, x

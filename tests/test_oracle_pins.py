@@ -115,6 +115,77 @@ def test_xkv_full_rank_exact_and_eckart_young_tail():
         assert abs(np.linalg.norm(cat - rec) - tail) < 1e-8 * max(1.0, tail)
 
 
+def _xkv_case(rng, n_tok, width, n_layers, decay, floor):
+    """Keys whose concatenation has a decaying spectrum: Z diag(s) W with
+    s_i = exp(-i / decay) + floor."""
+    m = n_layers * width
+    z = rng.standard_normal((n_tok, m)) * (np.exp(-np.arange(m) / decay) + floor)
+    cat = z @ rng.standard_normal((m, m)) / math.sqrt(m)
+    return [cat[:, l * width:(l + 1) * width] for l in range(n_layers)], cat
+
+
+def _rebuild(a, bls):
+    return np.concatenate([oracle.reconstruct_keys(a, b) for b in bls], axis=1)
+
+
+def test_xkv_iteration_exact_cases():
+    """Full rank (r = n), keys of exact rank r, and fewer tokens than the rank:
+    in each the span of M X holds the whole row space of C after one step, so
+    the factors rebuild every layer exactly; the basis is orthonormal and A is
+    C times it."""
+    rng = np.random.default_rng(40)
+    keys, cat = _xkv_case(rng, 90, 8, 3, 5.0, 0.1)
+    a, bls, x = oracle.xkv_subspace_iteration(keys, 24, rng.standard_normal((24, 24)), 1)
+    np.testing.assert_allclose(_rebuild(a, bls), cat, atol=1e-10)
+    low = rng.standard_normal((90, 6)) @ rng.standard_normal((6, 24))
+    keys = [low[:, l * 8:(l + 1) * 8] for l in range(3)]
+    a, bls, x = oracle.xkv_subspace_iteration(keys, 6, rng.standard_normal((24, 6)), 1)
+    np.testing.assert_allclose(_rebuild(a, bls), low, atol=1e-9)
+    np.testing.assert_allclose(x.T @ x, np.eye(6), atol=1e-12)
+    np.testing.assert_allclose(a, low @ x, atol=1e-12)
+    short = rng.standard_normal((5, 24))                     # T = 5 < r = 8
+    keys = [short[:, l * 8:(l + 1) * 8] for l in range(3)]
+    a, bls, _ = oracle.xkv_subspace_iteration(keys, 8, rng.standard_normal((24, 8)), 2)
+    np.testing.assert_allclose(_rebuild(a, bls), short, atol=1e-10)
+
+
+def test_xkv_iteration_reaches_the_truncated_svd_across_a_gap():
+    """Rank-r signal plus noise 1e-6 below it: the iteration converges to the
+    truncated SVD (the plain definition, pinned above) geometrically in the
+    squared singular-value ratio; three steps match it to 1e-9."""
+    rng = np.random.default_rng(41)
+    sig = rng.standard_normal((200, 10)) @ rng.standard_normal((10, 48))
+    cat = sig + 1e-6 * rng.standard_normal((200, 48))
+    keys = [cat[:, l * 16:(l + 1) * 16] for l in range(3)]
+    a, bls, _ = oracle.xkv_factorize(keys, 10)
+    best = _rebuild(a, bls)
+    a, bls, _ = oracle.xkv_subspace_iteration(keys, 10, rng.standard_normal((48, 10)), 3)
+    assert np.linalg.norm(_rebuild(a, bls) - best) <= 1e-9 * np.linalg.norm(best)
+
+
+def test_xkv_iteration_eckart_young_bounds_and_basis_independence():
+    """On a smoothly decaying spectrum the error never beats the singular-value
+    tail (Eckart-Young), shrinks with every step, and is within 5% of it after
+    three; the result depends on the span only: an orthonormalisation by
+    Cholesky (X = Y L^-T, L L^T = Y^T Y) instead of QR gives the same factors'
+    product."""
+    rng = np.random.default_rng(42)
+    keys, cat = _xkv_case(rng, 600, 32, 4, 20.0, 0.02)
+    tail = math.sqrt(float(np.sum(np.linalg.svd(cat, compute_uv=False)[24:] ** 2)))
+    om = rng.standard_normal((128, 24))
+    errs = []
+    for q in (1, 2, 3):
+        a, bls, _ = oracle.xkv_subspace_iteration(keys, 24, om, q)
+        errs.append(np.linalg.norm(cat - _rebuild(a, bls)))
+    assert tail <= errs[2] < errs[1] < errs[0] and errs[2] <= 1.05 * tail
+    x = om
+    m = cat.T @ cat
+    for _ in range(3):
+        y = m @ x
+        x = np.linalg.solve(np.linalg.cholesky(y.T @ y), y.T).T
+    np.testing.assert_allclose(cat @ x @ x.T, cat - (cat - _rebuild(a, bls)), rtol=0, atol=1e-9 * np.abs(cat).max())
+
+
 # ---------------------------------------------------------- brute force, tiny
 def _gelu_py(v):
     return 0.5 * v * (1.0 + math.erf(v / math.sqrt(2.0)))
