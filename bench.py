@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
+    ap.add_argument("--xkv", action="store_true", help="also time the cross-layer key factorisation")
     ap.add_argument("--prefill", action="store_true",
                     help="also time the fused prefill ranking (V_hat computed in the library) at its full shape")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -273,6 +274,8 @@ def main():
         result["rank_residuals"] = bench_rank(args.steps, args.warmup, ev)
     if args.prefill:
         result["prefill_rank"] = bench_prefill(max(2, args.steps // 3), 1, ev)
+    if args.xkv:
+        result["xkv_factorize"] = bench_xkv(max(2, args.steps // 3), 1, ev)
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -401,6 +404,50 @@ def bench_prefill(steps, warmup, ev):
             "all_token_pass_ms": pass1_ms, "all_token_pass_TFLOPs": flops / (pass1_ms * 1e-3) / 1e12,
             "all_token_pass_frac_of_bf16_peak": flops / (pass1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "v_read_GBs": x["v"].numel() * 2 / (ms * 1e-3) / 1e9}
+
+
+def bench_xkv(steps, warmup, ev):
+    """The cross-layer key factorisation of a whole Llama-3.1-8B prefill at
+    131072 tokens: 32 layers in 8 groups of 4 (8 KV heads x 128 per layer),
+    rank 512, 3 iterations, all 8 groups in one call. The Gram kernel (bf16
+    MFMA over every token) is timed by HIP events on the stream it runs on;
+    its work is the T n (n + 1) flops of the symmetric product's unique
+    entries."""
+    import torch
+    import long_context_decode_lowram_amd as L
+    import synth
+
+    xc = synth.XKV_CONFIGS["x_llama_131k"]
+    bt = 8
+    x = synth.gen_xkv_inputs(xc, "cuda", batch=bt)
+    T, n, r = xc.ctx_len, xc.n, xc.rank
+    o = {"a": torch.empty(bt, T, r, dtype=torch.bfloat16, device="cuda"),
+         "b_l": torch.empty(bt, xc.n_layers, xc.width, r, dtype=torch.bfloat16, device="cuda")}
+    args = L.make_xkv_args(x["keys"], x["omega"], xc.n_iter, o["a"], o["b_l"])
+    ws = torch.empty(L.xkv_workspace_size(args), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    for _ in range(warmup):
+        L.xkv_launch(args)
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(steps):
+        args.ev_main_begin, args.ev_main_end = evs[i]
+        L.xkv_launch(args)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    gram_ms = sum(ev.elapsed_ms(a, b) for a, b in evs) / steps
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    gram_flops = float(T) * n * (n + 1) * bt
+    return {"groups": bt, "layers_per_group": xc.n_layers, "ctx_len": T, "width": xc.width, "rank": r,
+            "n_iter": xc.n_iter, "ms_per_call": ms, "ms_per_group": ms / bt,
+            "keys_GBs": x["keys"].numel() * 2 / (ms * 1e-3) / 1e9, "gram_kernel_ms": gram_ms,
+            "gram_kernel_TFLOPs": gram_flops / (gram_ms * 1e-3) / 1e12,
+            "gram_kernel_frac_of_bf16_peak": gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
 if __name__ == "__main__":

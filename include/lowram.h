@@ -223,6 +223,63 @@ typedef struct lowram_prefill_args {
 int    lowram_prefill_rank(const lowram_prefill_args *args, void *stream);
 size_t lowram_prefill_workspace_size(const lowram_prefill_args *args);
 
+/*
+ * Cross-layer key factors of n_batch independent layer groups (project site,
+ * Figure 3: K ~ A . B with A shared by a group of adjacent layers and a
+ * smaller factor per layer; explainer, keys paragraph: xKV, one low-rank basis
+ * for adjacent layers). With C = [K_1 | ... | K_G] (T x n, n = G D) and its
+ * Gram matrix M = C^T C, randomized subspace iteration (Halko, Martinsson and
+ * Tropp, "Finding structure with randomness", SIAM Review 2011, Algorithm 4.4)
+ * from the caller's draw omega:
+ *   X_0 = omega,  X_i = orth(M X_{i-1}) for i = 1 .. n_iter,
+ *   A = C X,      B_l = (rows l D .. l D + D - 1 of X)^T,
+ * so K_l ~ A B_l with the reconstruction C X X^T, which approaches the best
+ * rank-r fit (the truncated SVD) as n_iter grows. orth is CholeskyQR applied
+ * twice, M is accumulated in float32 per token chunk and summed in binary64,
+ * the iteration runs in binary64, A = C X in bf16 products with float32 sums.
+ * A Cholesky pivot at or below r 2^-52 times the largest diagonal entry drops
+ * that basis column (zero column of X, A and B_l): the block is numerically
+ * rank deficient there (e.g. fewer tokens than the rank, or zero keys), and
+ * the dropped direction carries none of the keys' energy.
+ *
+ * Shapes (Bt = n_batch problems, e.g. the layer groups of a model, or of
+ * several sequences, all of length T): keys [Bt, G, T, D] bf16 (layer-major,
+ * each layer's keys [T, D] with D = Hkv d); omega [n, r] binary64, one draw
+ * shared by every problem, e.g. standard normal; outputs a [Bt, T, r] bf16
+ * (the factor the decode step reads as this group's A for every layer of it)
+ * and b_l [Bt, G, D, r] bf16 (layer l's B_l output-major, as the decode step
+ * reads it); basis [Bt, n, r] binary64 (X) if not NULL. Limits: G <= 16, D a
+ * multiple of 256, n <= 16384, r a multiple of 64 in [64, min(1024, n)],
+ * n_iter in [1, 16], T D 2 < 2^31. Buffers are caller-owned device memory,
+ * 16-byte aligned; the call allocates nothing. The problems run side by side
+ * in every kernel (the r x r Cholesky factorisations, one workgroup each,
+ * then overlap).
+ */
+typedef struct lowram_xkv_args {
+    int32_t n_batch;            /* Bt, independent problems                         */
+    int32_t n_layers;           /* G, layers sharing A                              */
+    int32_t ctx_len;            /* T                                                */
+    int32_t width;              /* D = n_kv_heads * head_dim                        */
+    int32_t rank;               /* r                                                */
+    int32_t n_iter;             /* subspace iterations                              */
+
+    const void   *keys;         /* [Bt, G, T, D] bf16                               */
+    const double *omega;        /* [G*D, r] starting block                          */
+
+    void         *a;            /* [Bt, T, r] bf16 out                              */
+    void         *b_l;          /* [Bt, G, D, r] bf16 out                           */
+    double       *basis;        /* [Bt, G*D, r] out, or NULL                        */
+
+    void         *workspace;    /* >= lowram_xkv_workspace_size bytes               */
+    size_t        workspace_bytes;
+
+    void         *ev_main_begin; /* optional hipEvent_t around the Gram MFMA kernel */
+    void         *ev_main_end;
+} lowram_xkv_args;
+
+int    lowram_xkv_factorize(const lowram_xkv_args *args, void *stream);
+size_t lowram_xkv_workspace_size(const lowram_xkv_args *args);
+
 /* Static description of a status code. */
 const char *lowram_status_string(int status);
 

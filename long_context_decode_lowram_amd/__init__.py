@@ -1,16 +1,16 @@
 """LowRAM decode-time path on MI355X (gfx950): reconstructed-KV attention over
-a compressed cache and the prefill-side residual ranking, as HIP kernels
-behind the C ABI declared in include/lowram.h. This package is the thin
-Python binding; build the library with
+a compressed cache, the prefill-side residual ranking and the cross-layer key
+factorisation, as HIP kernels behind the C ABI declared in include/lowram.h.
+This package is the thin Python binding; build the library with
 ``python -m long_context_decode_lowram_amd.build``."""
 from ._binding import (BF16, F32, FLAG_GENERIC, I2, I8, BLOCK, DecodeArgs, LowramError, PrefillArgs, RankArgs,
-                       decode_launch, decode_step, decode_workspace_size, last_error, lib,
-                       make_decode_args, make_prefill_args, make_rank_args, prefill_launch, prefill_rank,
-                       prefill_workspace_size, rank_launch, rank_residuals, rank_workspace_size,
-                       status_string)
+                       XkvArgs, decode_launch, decode_step, decode_workspace_size, last_error, lib,
+                       make_decode_args, make_prefill_args, make_rank_args, make_xkv_args, prefill_launch,
+                       prefill_rank, prefill_workspace_size, rank_launch, rank_residuals, rank_workspace_size,
+                       status_string, xkv_factorize, xkv_launch, xkv_workspace_size)
 
 __all__ = ["BF16", "F32", "FLAG_GENERIC", "I2", "I8", "BLOCK", "DecodeArgs", "LowramError", "PrefillArgs", "RankArgs",
-           "decode_launch", "decode_step", "decode_workspace_size", "last_error", "lib",
-           "make_decode_args", "make_prefill_args", "make_rank_args", "prefill_launch", "prefill_rank",
-           "prefill_workspace_size", "rank_launch", "rank_residuals", "rank_workspace_size",
-           "status_string"]
+           "XkvArgs", "decode_launch", "decode_step", "decode_workspace_size", "last_error", "lib",
+           "make_decode_args", "make_prefill_args", "make_rank_args", "make_xkv_args", "prefill_launch",
+           "prefill_rank", "prefill_workspace_size", "rank_launch", "rank_residuals", "rank_workspace_size",
+           "status_string", "xkv_factorize", "xkv_launch", "xkv_workspace_size"]

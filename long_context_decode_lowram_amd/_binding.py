@@ -51,6 +51,12 @@ class PrefillArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
 
 
+class XkvArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("n_batch", "n_layers", "ctx_len", "width", "rank", "n_iter")] + [
+        (n, _p) for n in ("keys", "omega", "a", "b_l", "basis", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+
+
 class LowramError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"liblowram status {status}: {msg}")
@@ -80,6 +86,10 @@ def lib():
         L.lowram_prefill_rank.restype = ctypes.c_int
         L.lowram_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
         L.lowram_prefill_workspace_size.restype = ctypes.c_size_t
+        L.lowram_xkv_factorize.argtypes = [ctypes.POINTER(XkvArgs), _p]
+        L.lowram_xkv_factorize.restype = ctypes.c_int
+        L.lowram_xkv_workspace_size.argtypes = [ctypes.POINTER(XkvArgs)]
+        L.lowram_xkv_workspace_size.restype = ctypes.c_size_t
         L.lowram_status_string.argtypes = [ctypes.c_int]
         L.lowram_status_string.restype = ctypes.c_char_p
         L.lowram_last_error.argtypes = []
@@ -295,4 +305,62 @@ def prefill_rank(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, *, group=4, b1=None
     args.workspace = workspace.data_ptr()
     args.workspace_bytes = workspace.numel()
     prefill_launch(args, stream)
+    return out
+
+
+def make_xkv_args(keys, omega, n_iter, a, b_l, *, basis=None, workspace=None, events=None):
+    """Fill an XkvArgs: keys [Bt, G, T, D] (or one problem [G, T, D]) bf16,
+    omega [G*D, r] float64, a [Bt, T, r] and b_l [Bt, G, D, r] bf16 outputs,
+    basis [Bt, G*D, r] float64 or None."""
+    if keys.dim() == 3:
+        keys = keys.unsqueeze(0)
+    Bt, G, T, D = keys.shape
+    if keys.dtype != torch.bfloat16 or omega.dtype != torch.float64:
+        raise ValueError("keys must be bfloat16 and omega float64")
+    args = XkvArgs()
+    args.n_batch, args.n_layers, args.ctx_len, args.width = Bt, G, T, D
+    args.rank, args.n_iter = omega.shape[1], n_iter
+    for name, t in (("keys", keys), ("omega", omega), ("a", a), ("b_l", b_l), ("basis", basis),
+                    ("workspace", workspace)):
+        setattr(args, name, _ptr(t))
+    args.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if events is not None:
+        args.ev_main_begin, args.ev_main_end = events
+    return args
+
+
+def xkv_workspace_size(args):
+    n = lib().lowram_xkv_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def xkv_launch(args, stream=None):
+    rc = lib().lowram_xkv_factorize(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def xkv_factorize(keys, omega, n_iter=3, *, want_basis=False, workspace=None, stream=None):
+    """Cross-layer key factors of Bt layer groups (keys [Bt, G, T, D], or one
+    group [G, T, D]): returns a dict with a [Bt, T, r] bf16, b_l [Bt, G, D, r]
+    bf16 and basis [Bt, G*D, r] float64 (when asked), without the batch
+    dimension for a single group."""
+    single = keys.dim() == 3
+    k4 = keys.unsqueeze(0) if single else keys
+    Bt, G, T, D = k4.shape
+    r = omega.shape[1]
+    dev = keys.device
+    out = {"a": torch.empty(Bt, T, r, dtype=torch.bfloat16, device=dev),
+           "b_l": torch.empty(Bt, G, D, r, dtype=torch.bfloat16, device=dev),
+           "basis": torch.empty(Bt, G * D, r, dtype=torch.float64, device=dev) if want_basis else None}
+    args = make_xkv_args(k4, omega, n_iter, out["a"], out["b_l"], basis=out["basis"])
+    if workspace is None:
+        workspace = torch.empty(xkv_workspace_size(args), dtype=torch.uint8, device=dev)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    xkv_launch(args, stream)
+    if single:
+        out = {k: (None if v is None else v[0]) for k, v in out.items()}
     return out

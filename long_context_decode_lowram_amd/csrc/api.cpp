@@ -143,6 +143,58 @@ int plan_prefill(const lowram_prefill_args* a, PrefillPlan* pl) {
     return LOWRAM_OK;
 }
 
+struct XkvPlan {
+    XkvParams p;
+    size_t off_part, off_m, off_x, off_y, off_g, off_gp, off_rinv, off_dead, off_xt, total;
+};
+
+int plan_xkv(const lowram_xkv_args* a, XkvPlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_batch < 1 || a->n_batch > 65535) return fail(LOWRAM_ERR_ARG, "n_batch (%d) must be in [1, 65535]", a->n_batch);
+    if (a->n_layers < 1 || a->n_layers > 16) return fail(LOWRAM_ERR_ARG, "n_layers (%d) must be in [1, 16]", a->n_layers);
+    if (a->ctx_len < 1) return fail(LOWRAM_ERR_ARG, "ctx_len must be >= 1");
+    if (a->width < 256 || a->width % 256 != 0 || a->width > 8192)
+        return fail(LOWRAM_ERR_UNSUPPORTED, "width must be a multiple of 256 in [256, 8192] (got %d)", a->width);
+    const int n = a->n_layers * a->width;
+    if (n > 16384) return fail(LOWRAM_ERR_UNSUPPORTED, "n_layers * width must be at most 16384 (got %d)", n);
+    if (a->rank < 64 || a->rank % 64 != 0 || a->rank > 1024 || a->rank > n)
+        return fail(LOWRAM_ERR_UNSUPPORTED, "rank must be a multiple of 64 in [64, min(1024, n_layers * width)] (got %d)", a->rank);
+    if (a->n_iter < 1 || a->n_iter > 16) return fail(LOWRAM_ERR_ARG, "n_iter (%d) must be in [1, 16]", a->n_iter);
+    if ((int64_t)a->ctx_len * a->width * 2 >= (int64_t(1) << 31))
+        return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * width * 2 must stay below 2^31");
+    XkvParams& p = pl->p;
+    p = XkvParams{};
+    p.n_batch = a->n_batch;
+    p.n_layers = a->n_layers; p.ctx_len = a->ctx_len; p.width = a->width; p.rank = a->rank; p.n_iter = a->n_iter;
+    p.n = n;
+    p.nt = n / 256;
+    p.n_upper = p.nt * (p.nt + 1) / 2;
+    // About 2048 Gram workgroups over the batch, chunks of at least 64 tokens.
+    const int max_chunks = (a->ctx_len + 63) / 64;
+    const int64_t per_chunk = (int64_t)p.n_upper * a->n_batch;
+    int nc = (int)((2048 + per_chunk - 1) / per_chunk);
+    nc = nc < 1 ? 1 : (nc > 64 ? 64 : nc);
+    nc = nc > max_chunks ? max_chunks : nc;
+    p.chunk_len = ((a->ctx_len + nc - 1) / nc + 63) / 64 * 64;
+    p.n_chunks = (a->ctx_len + p.chunk_len - 1) / p.chunk_len;
+    const int tiles = (p.rank / 64) * (p.rank / 64) * a->n_batch;
+    int ks = (512 + tiles - 1) / tiles;
+    ks = ks > n / 256 ? n / 256 : ks;
+    p.k_splits = ks < 1 ? 1 : ks;
+    const size_t r = (size_t)p.rank, bt = (size_t)a->n_batch;
+    pl->off_part = 0;
+    pl->off_m = up256(pl->off_part + bt * xkv_partials_floats(p) * sizeof(float));
+    pl->off_x = up256(pl->off_m + bt * n * n * sizeof(double));
+    pl->off_y = up256(pl->off_x + bt * n * r * sizeof(double));
+    pl->off_g = up256(pl->off_y + bt * n * r * sizeof(double));
+    pl->off_gp = up256(pl->off_g + bt * r * r * sizeof(double));
+    pl->off_rinv = up256(pl->off_gp + bt * p.k_splits * r * r * sizeof(double));
+    pl->off_dead = up256(pl->off_rinv + bt * r * r * sizeof(double));
+    pl->off_xt = up256(pl->off_dead + bt * r * sizeof(int32_t));
+    pl->total = up256(pl->off_xt + bt * r * n * 2);
+    return LOWRAM_OK;
+}
+
 int hip_fail(hipError_t e, const char* what) {
     return fail(LOWRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -320,6 +372,51 @@ int lowram_prefill_rank(const lowram_prefill_args* a, void* stream) {
         p.n_groups = prefill_groups(p, 1);
         if ((e = launch_prefill(p, 1, s)) != hipSuccess) return hip_fail(e, "prefill residual launch");
     }
+    return LOWRAM_OK;
+}
+
+size_t lowram_xkv_workspace_size(const lowram_xkv_args* a) {
+    g_err[0] = 0;
+    XkvPlan pl;
+    return plan_xkv(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_xkv_factorize(const lowram_xkv_args* a, void* stream) {
+    g_err[0] = 0;
+    XkvPlan pl;
+    int rc = plan_xkv(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (!a->keys || !a->omega || !a->a || !a->b_l) return fail(LOWRAM_ERR_ARG, "keys, omega, a and b_l must be non-NULL");
+    const void* v16[] = {a->keys, a->omega, a->a, a->b_l, a->basis, a->workspace};
+    for (const void* q : v16)
+        if (misaligned(q, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", q);
+    if (!a->workspace || a->workspace_bytes < pl.total)
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+    char* ws = static_cast<char*>(a->workspace);
+    XkvParams p = pl.p;
+    p.keys = static_cast<const __bf16*>(a->keys);
+    p.omega = a->omega;
+    p.a = static_cast<__bf16*>(a->a);
+    p.b_l = static_cast<__bf16*>(a->b_l);
+    p.basis = a->basis;
+    p.partials = reinterpret_cast<float*>(ws + pl.off_part);
+    p.m = reinterpret_cast<double*>(ws + pl.off_m);
+    p.x = reinterpret_cast<double*>(ws + pl.off_x);
+    p.y = reinterpret_cast<double*>(ws + pl.off_y);
+    p.g = reinterpret_cast<double*>(ws + pl.off_g);
+    p.g_parts = reinterpret_cast<double*>(ws + pl.off_gp);
+    p.rinv = reinterpret_cast<double*>(ws + pl.off_rinv);
+    p.dead = reinterpret_cast<int32_t*>(ws + pl.off_dead);
+    p.xt = reinterpret_cast<__bf16*>(ws + pl.off_xt);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a->ev_main_begin && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_begin), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    if ((e = launch_xkv_gram(p, s)) != hipSuccess) return hip_fail(e, "xkv gram launch");
+    if (a->ev_main_end && (e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_end), s)) != hipSuccess)
+        return hip_fail(e, "event record");
+    if ((e = launch_xkv_factor(p, s)) != hipSuccess) return hip_fail(e, "xkv iteration launch");
     return LOWRAM_OK;
 }
 

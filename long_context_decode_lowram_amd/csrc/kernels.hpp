@@ -49,4 +49,33 @@ struct PrefillParams {
 int prefill_groups(const PrefillParams& p, int mode);
 hipError_t launch_prefill(const PrefillParams& p, int mode, hipStream_t s);
 
+// Cross-layer key factors by subspace iteration on the Gram matrix, for a
+// batch of independent problems (every pointer below has a leading batch
+// dimension except omega, which all problems share).
+struct XkvParams {
+    int n_batch, n_layers, ctx_len, width, rank, n_iter;
+    int n;                        // n_layers * width
+    int nt, n_upper;              // 256-column tiles per side, tiles with I <= J
+    int n_chunks, chunk_len;      // token chunks of the Gram partials
+    int k_splits;                 // contraction splits of the r x r Gram products
+    const __bf16* keys;           // [Bt, G, T, D]
+    const double* omega;          // [n, r]
+    __bf16* a;                    // [Bt, T, r]
+    __bf16* b_l;                  // [Bt, n, r]
+    double* basis;                // [Bt, n, r] or null
+    // workspace
+    float* partials;              // [Bt, n_chunks, n_upper, 256, 256]
+    double* m;                    // [Bt, n, n]
+    double* x;                    // [Bt, n, r]
+    double* y;                    // [Bt, n, r]
+    double* g;                    // [Bt, r, r]  Gram, then its Cholesky factor
+    double* g_parts;              // [Bt, k_splits, r, r]
+    double* rinv;                 // [Bt, r, r]  L^-T
+    int32_t* dead;                // [Bt, r]
+    __bf16* xt;                   // [Bt, r, n]
+};
+size_t xkv_partials_floats(const XkvParams& p);   // per problem
+hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s);     // chunk partials of C^T C
+hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s);   // M, iterations, A and B_l
+
 }  // namespace lowram

@@ -1,0 +1,552 @@
+// Cross-layer key factors for the prefill side.
+//
+// project site, Figure 3 (K ~ A . B: a factor shared by a group of adjacent
+// layers and a smaller factor per layer) and the explainer's keys paragraph
+// (xKV: one low-rank basis for adjacent layers, because key energy sits in few
+// directions). The group's keys C = [K_1 | ... | K_G] (T x n, n = G D) are
+// reduced to an orthonormal rank-r basis X (n x r) of their row space by
+// randomized subspace iteration on the Gram matrix (Halko, Martinsson and
+// Tropp, "Finding structure with randomness", SIAM Review 2011, Algorithm
+// 4.4): M = C^T C, X_0 = Omega, X_i = orth(M X_{i-1}); then A = C X and
+// B_l = (rows l D .. l D + D - 1 of X)^T, so K_l ~ A B_l.
+//
+//   xkv_gram_kernel        bf16 MFMA: partial 256 x 256 Gram tiles per token chunk
+//   xkv_gram_reduce_kernel fp64 sum of the chunk partials into symmetric M
+//   xkv_gemm_f64_kernel    fp64 products of the iteration (M X, Y^T Y)
+//   xkv_chol_kernel        Cholesky of the r x r Gram of the block (one workgroup)
+//   xkv_trsm_kernel        X = Y L^-T, rows in parallel (CholeskyQR)
+//   xkv_emit_kernel        bf16 B_l and the transposed basis
+//   xkv_a_kernel           bf16 MFMA: A = C X
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace lowram {
+
+constexpr int kXT = 256;                 // tile edge of the MFMA kernels
+constexpr int kXK = 64;                  // contraction step
+constexpr int kXThreads = 512;           // 8 waves
+constexpr int kXRowB = kXK * 2;          // LDS row: 64 bf16 along the contraction
+constexpr int kXStage = kXT * kXRowB;    // one operand of one step: 32 KB
+constexpr int kXMaxRank = 1024;
+
+// LDS rows of 128 bytes hold eight 16-byte pieces; piece p of row r sits in
+// slot p ^ (r & 7), so the MFMA reads (16 rows, one piece) hit distinct banks.
+__device__ __forceinline__ uint32_t xslot(int row, int piece) {
+    return (uint32_t)(row * kXRowB + ((piece ^ (row & 7)) << 4));
+}
+
+// One 64-wide contraction step of the wave's 64 x 128 block of a 256 x 256
+// tile: operand rows [256][64 k] in swizzled LDS. acc[mt][nt] holds
+// D[m][n] = sum_k op0[wi + 16 mt + m][k] op1[wj + 16 nt + n][k].
+__device__ __forceinline__ void xkv_mma_step(const unsigned char* op0, const unsigned char* op1,
+                                             f32x4 (&acc)[4][8], int wi, int wj, int lane) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[4], bf[8];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) af[mt] = lds16(op0, xslot(wi + mt * 16 + l16, ks * 4 + g4));
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) bf[nt] = lds16(op1, xslot(wj + nt * 16 + l16, ks * 4 + g4));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma(af[mt], bf[nt], acc[mt][nt]);
+    }
+}
+
+// Upper-triangle tile index -> (I, J), I <= J, row by row.
+__device__ __forceinline__ void xkv_tile(int k, int nt, int& ti, int& tj) {
+    int i = 0;
+    while (k >= nt - i) {
+        k -= nt - i;
+        ++i;
+    }
+    ti = i;
+    tj = i + k;
+}
+
+// ---------------------------------------------------------------- Gram
+// Block (b, problem): token chunk b / n_upper, tile b % n_upper (chunk-major,
+// so the workgroups resident together share one chunk of C). The stored
+// partial is the transposed tile: P[a][b] = sum_t C[t][256 I + b] C[t][256 J + a]
+// = M[256 J + a][256 I + b].
+__global__ __launch_bounds__(kXThreads, 1) void xkv_gram_kernel(XkvParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char stg[2][2][kXStage];   // [buffer][operand]
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int chunk = blockIdx.x / p.n_upper;
+    const int tile = blockIdx.x - chunk * p.n_upper;
+    int ti, tj;
+    xkv_tile(tile, p.nt, ti, tj);
+    const bool diag = ti == tj;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.ctx_len, t_begin + p.chunk_len);
+    const int n_steps = (t_end - t_begin + kXK - 1) / kXK;
+
+    // Staging: waves 0-3 bring tile I's columns, waves 4-7 tile J's (idle on
+    // a diagonal tile). A thread moves an 8-token x 8-column block per step
+    // and transposes it in registers, so that LDS rows run along the tokens.
+    const int op = w >> 2;
+    const bool stager = !(diag && op == 1);
+    const int cb = (w & 3) * 8 + (lane >> 3);      // column block of the tile (8 columns)
+    const int tb = lane & 7;                       // token block of the step (8 tokens)
+    const int col0 = (op == 0 ? ti : tj) * kXT;
+    const int layer = col0 / p.width;
+    const int64_t prob = blockIdx.y;
+    const __bf16* src = p.keys + (prob * p.n_layers + layer) * p.ctx_len * (int64_t)p.width + (col0 - layer * p.width) + cb * 8;
+    u32x4 pre[8];
+    auto load = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + tb * 8 + j;
+            pre[j] = (stager && t < t_end) ? *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.width)
+                                           : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf) {
+        if (!stager) return;
+        unsigned char* dst = stg[buf][op];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = pre[2 * q][c >> 1], hi = pre[2 * q + 1][c >> 1];
+                o[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            *reinterpret_cast<u32x4*>(dst + xslot(cb * 8 + c, tb)) = o;
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wi = (w >> 1) * 64, wj = (w & 1) * 128;
+    load(t_begin);
+    store(0);
+    for (int s = 0; s < n_steps; ++s) {
+        __syncthreads();    // step s's buffer is written; step s-1's reads of the other are done
+        if (s + 1 < n_steps) load(t_begin + (s + 1) * kXK);
+        const int b = s & 1;
+        xkv_mma_step(stg[b][0], stg[b][diag ? 0 : 1], acc, wi, wj, lane);
+        if (s + 1 < n_steps) store(b ^ 1);
+    }
+    float* out = p.partials + ((prob * p.n_chunks + chunk) * p.n_upper + tile) * (kXT * kXT);
+    const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+            *reinterpret_cast<f32x4*>(out + (wj + nt * 16 + l16) * kXT + wi + mt * 16 + g4 * 4) = acc[mt][nt];
+}
+
+// M[256 J + a][256 I + b] = sum over chunks of P (binary64, chunk order),
+// mirrored off the diagonal. Grid (256 rows a, n_upper tiles, problems), 256 threads (b).
+__global__ __launch_bounds__(256) void xkv_gram_reduce_kernel(XkvParams p) {
+    const int tile = blockIdx.y, a = blockIdx.x, b = threadIdx.x;
+    const int64_t prob = blockIdx.z;
+    int ti, tj;
+    xkv_tile(tile, p.nt, ti, tj);
+    const float* src = p.partials + (prob * p.n_chunks * p.n_upper + tile) * (kXT * kXT) + a * kXT + b;
+    double* const m = p.m + prob * p.n * (int64_t)p.n;
+    const int64_t chunk_stride = (int64_t)p.n_upper * (kXT * kXT);
+    double v = 0.0;
+    for (int c = 0; c < p.n_chunks; ++c) v += (double)src[c * chunk_stride];
+    const int64_t row = (int64_t)tj * kXT + a, col = (int64_t)ti * kXT + b;
+    m[row * p.n + col] = v;
+    if (ti != tj) m[col * p.n + row] = v;
+}
+
+// ------------------------------------------------------- fp64 products
+// Per problem q = z / splits and split z % splits: C_q (+ split * c_split)
+// = op(A_q) op(B_q) over k in [split kc, min(k, split kc + kc)), with
+// X_q = X + q sX, op(A)(i, kk) = TA ? A[kk lda + i] : A[i lda + kk] and
+// op(B)(kk, j) = TB ? B[j ldb + kk] : B[kk ldb + j]. 64 x 64 tiles, 16 deep;
+// each thread owns a 4 x 4 block.
+struct GemmArgs {
+    int m, n, k, kc, splits;
+    const double* A; int64_t lda, sA;
+    const double* B; int64_t ldb, sB;
+    double* C; int64_t ldc, sC, c_split;
+};
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void xkv_gemm_f64_kernel(GemmArgs g) {
+    __shared__ double as[16][64 + 4], bs[16][64 + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const int q = blockIdx.z / g.splits, split = blockIdx.z - q * g.splits;
+    const int m = g.m, n = g.n, k = g.k;
+    const double* const A = g.A + q * g.sA;
+    const double* const B = g.B + q * g.sB;
+    const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
+    const int kb = split * g.kc, ke = min(k, kb + g.kc);
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            const int il = TA ? (e & 63) : (e >> 4), kl = TA ? (e >> 6) : (e & 15);
+            const int gi = i0 + il, gk = k0 + kl;
+            as[kl][il] = (gi < m && gk < ke) ? (TA ? A[(int64_t)gk * lda + gi] : A[(int64_t)gi * lda + gk]) : 0.0;
+            const int jl = TB ? (e >> 4) : (e & 63), kl2 = TB ? (e & 15) : (e >> 6);
+            const int gj = j0 + jl, gk2 = k0 + kl2;
+            bs[kl2][jl] = (gj < n && gk2 < ke) ? (TB ? B[(int64_t)gj * ldb + gk2] : B[(int64_t)gk2 * ldb + gj]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) av[a] = as[kk][ty * 4 + a];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bv[b] = bs[kk][tx * 4 + b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+        }
+        __syncthreads();
+    }
+    double* out = g.C + q * g.sC + split * g.c_split;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int i = i0 + ty * 4 + a;
+        if (i >= m) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = j0 + tx * 4 + b;
+            if (j < n) out[(int64_t)i * ldc + j] = acc[a][b];
+        }
+    }
+}
+
+// out_q[i] = sum over s of parts_q[s count + i], in split order (grid y: problem q).
+__global__ __launch_bounds__(256) void xkv_sum_splits_kernel(const double* parts, double* out, int64_t count, int splits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const int64_t q = blockIdx.y;
+    double v = 0.0;
+    for (int s = 0; s < splits; ++s) v += parts[(q * splits + s) * count + i];
+    out[q * count + i] = v;
+}
+
+// ---------------------------------------------------------- CholeskyQR
+constexpr int kCholPw = 16;
+
+// In-place lower Cholesky factor of the r x r Gram g (row-major; the strict
+// upper triangle is left as it was), one workgroup: 16-column panels factored
+// in LDS, trailing lower triangle updated in 4 x 4 blocks. A pivot at or below
+// r * 2^-52 * max diag marks the column dead: its L column is zero and the
+// solve gives that basis column zero (the block is rank deficient there).
+// One workgroup per problem (grid x).
+__global__ __launch_bounds__(1024) void xkv_chol_kernel(double* g, int r, int32_t* dead) {
+    __shared__ double pan[kXMaxRank * kCholPw];
+    __shared__ double red[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    g += (int64_t)blockIdx.x * r * r;
+    dead += (int64_t)blockIdx.x * r;
+    double dm = 0.0;
+    for (int i = tid; i < r; i += 1024) dm = fmax(dm, g[(int64_t)i * r + i]);
+    for (int off = 32; off > 0; off >>= 1) dm = fmax(dm, __shfl_xor(dm, off, kWave));
+    if (lane == 0) red[w] = dm;
+    __syncthreads();
+    dm = red[0];
+    for (int i = 1; i < 16; ++i) dm = fmax(dm, red[i]);
+    const double tau = (double)r * 0x1p-52 * dm;
+
+    for (int j0 = 0; j0 < r; j0 += kCholPw) {
+        const int rows = r - j0;
+        for (int e = tid; e < rows * kCholPw; e += 1024) {
+            const int i = e / kCholPw, c = e % kCholPw;
+            pan[e] = g[(int64_t)(j0 + i) * r + j0 + c];
+        }
+        __syncthreads();
+        for (int c = 0; c < kCholPw; ++c) {
+            const double d = pan[c * kCholPw + c];
+            const bool dd = !(d > tau);
+            const double piv = dd ? 0.0 : sqrt(d);
+            const double inv = dd ? 0.0 : 1.0 / piv;
+            __syncthreads();
+            for (int i = c + tid; i < rows; i += 1024) pan[i * kCholPw + c] = i == c ? piv : pan[i * kCholPw + c] * inv;
+            if (tid == 0) dead[j0 + c] = dd ? 1 : 0;
+            __syncthreads();
+            const int nc = kCholPw - 1 - c;
+            for (int e = tid; e < (rows - c - 1) * nc; e += 1024) {
+                const int i = c + 1 + e / nc, cc = c + 1 + e % nc;
+                if (cc <= i) pan[i * kCholPw + cc] -= pan[i * kCholPw + c] * pan[cc * kCholPw + c];
+            }
+            __syncthreads();
+        }
+        for (int e = tid; e < rows * kCholPw; e += 1024) {
+            const int i = e / kCholPw, c = e % kCholPw;
+            if (c <= i) g[(int64_t)(j0 + i) * r + j0 + c] = pan[e];
+        }
+        const int nb = (rows - kCholPw) / 4;
+        const int64_t nblk = (int64_t)nb * (nb + 1) / 2;
+        for (int64_t e = tid; e < nblk; e += 1024) {
+            int bi = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+            while ((int64_t)bi * (bi + 1) / 2 > e) --bi;
+            while ((int64_t)(bi + 1) * (bi + 2) / 2 <= e) ++bi;
+            const int bk = (int)(e - (int64_t)bi * (bi + 1) / 2);
+            const int i0 = kCholPw + bi * 4, k0 = kCholPw + bk * 4;
+            double s[4][4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) s[a][b] = 0.0;
+#pragma unroll 4
+            for (int c = 0; c < kCholPw; ++c) {
+                double li[4], lk[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    li[q] = pan[(i0 + q) * kCholPw + c];
+                    lk[q] = pan[(k0 + q) * kCholPw + c];
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) s[a][b] = fma(li[a], lk[b], s[a][b]);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (k0 + b <= i0 + a) g[(int64_t)(j0 + i0 + a) * r + j0 + k0 + b] -= s[a][b];
+        }
+        __syncthreads();
+    }
+}
+
+// X = Y L^-T for 16 rows per workgroup: x_j = (y_j - sum_{k<j} L[j][k] x_k) / L[j][j],
+// x_j = 0 for a dead column. Lanes 16 q .. 16 q + 15 of a wave share one row.
+// Y = I (r rows) when y is null, which gives L^-T itself. Grid y: problem.
+constexpr int kTrRows = 16;
+__global__ __launch_bounds__(256) void xkv_trsm_kernel(const double* y, double* x, const double* l, const int32_t* dead,
+                                                       int nrows, int r) {
+    __shared__ double xs[kTrRows][kXMaxRank];
+    const int tid = threadIdx.x, lane = tid & 63, row = tid >> 4, c = tid & 15;
+    const int r0 = blockIdx.x * kTrRows;
+    const int64_t q = blockIdx.y;
+    l += q * r * r;
+    dead += q * r;
+    x += q * nrows * r;
+    if (y) y += q * nrows * r;
+    for (int e = tid; e < kTrRows * r; e += 256) {
+        const int i = e / r, j = e % r;
+        xs[i][j] = r0 + i >= nrows ? 0.0 : (y ? y[(int64_t)(r0 + i) * r + j] : (r0 + i == j ? 1.0 : 0.0));
+    }
+    __syncthreads();
+    for (int jb = 0; jb < r; jb += 16) {
+        const int j = jb + c;
+        const double* lj = l + (int64_t)j * r;
+        double s0 = 0.0, s1 = 0.0;
+        for (int k = 0; k < jb; k += 2) {
+            s0 = fma(xs[row][k], lj[k], s0);
+            s1 = fma(xs[row][k + 1], lj[k + 1], s1);
+        }
+        double v = xs[row][j] - (s0 + s1);
+        const double ljj = lj[j];
+        const bool dj = dead[j] != 0;
+        for (int cc = 0; cc < 16; ++cc) {
+            double xv = (dj || !(ljj != 0.0)) ? 0.0 : v / ljj;
+            xv = __shfl(xv, (lane & ~15) | cc, kWave);
+            if (c > cc) v = fma(-lj[jb + cc], xv, v);
+            if (c == cc) xs[row][j] = xv;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < kTrRows * r; e += 256) {
+        const int i = e / r, j = e % r;
+        if (r0 + i < nrows) x[(int64_t)(r0 + i) * r + j] = xs[i][j];
+    }
+}
+
+// ------------------------------------------------------------- outputs
+// b_l = bf16(X) in X's own [n, r] layout, xt = bf16(X)^T [r, n], basis = X
+// (grid z: problem).
+__global__ __launch_bounds__(256) void xkv_emit_kernel(XkvParams p, const double* xb) {
+    __shared__ uint16_t tl[64][64 + 2];
+    const int i0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t off = (int64_t)blockIdx.z * p.n * p.rank;
+    for (int q = ty; q < 64; q += 4) {
+        const int64_t e = off + (int64_t)(i0 + q) * p.rank + c0 + tx;
+        const double v = xb[e];
+        const uint16_t h = f64_to_bf16_bits(v);
+        reinterpret_cast<uint16_t*>(p.b_l)[e] = h;
+        if (p.basis) p.basis[e] = v;
+        tl[q][tx] = h;
+    }
+    __syncthreads();
+    for (int q = ty; q < 64; q += 4)
+        reinterpret_cast<uint16_t*>(p.xt)[off + (int64_t)(c0 + q) * p.n + i0 + tx] = tl[tx][q];
+}
+
+// A = C X as A^T tiles: operand 0 = rows c of xt (256 per tile, zeros past
+// r), operand 1 = token rows of C (zeros past T), contraction over n in
+// steps of 64 inside one layer. Both come in by direct copies into two static
+// stage buffers. Lane (l16, g4) holds A[t][c .. c+3] for 4 consecutive c.
+__global__ __launch_bounds__(kXThreads, 1) void xkv_a_kernel(XkvParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char st0[2 * kXStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[2 * kXStage];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_ct = (p.rank + kXT - 1) / kXT;
+    const int ct = blockIdx.x % n_ct, tt = blockIdx.x / n_ct;
+    const int c0 = ct * kXT, t0 = tt * kXT;
+    const int n_steps = p.n / kXK;
+    const int64_t prob = blockIdx.y;
+    const __bf16* const keys = p.keys + prob * p.n_layers * p.ctx_len * (int64_t)p.width;
+    const __bf16* const xt = p.xt + prob * p.rank * (int64_t)p.n;
+    __bf16* const a_out = p.a + prob * p.ctx_len * (int64_t)p.rank;
+
+    // Waves 0-3 copy operand 0, waves 4-7 operand 1; each wave 64 rows, eight
+    // 1 KB copies (8 rows x 8 pieces, lane i -> row i / 8, slot i % 8).
+    const int op = w >> 2;
+    const int dma_row = lane >> 3;
+    const uint32_t dma_piece = (uint32_t)(((lane & 7) ^ dma_row) * 16);
+    const int rbase = (w & 3) * 64;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xt, (uint32_t)((int64_t)p.rank * p.n * 2));
+    auto dma = [&](int s, unsigned char* buf) {
+        const int k0 = s * kXK;
+        if (op == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = c0 + rbase + q * 8 + dma_row;
+                dma16(rx, buf + (rbase + q * 8) * kXRowB, (uint32_t)(((int64_t)row * p.n + k0) * 2) + dma_piece, 0u);
+            }
+        } else {
+            const int layer = k0 / p.width;
+            const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(keys + (int64_t)layer * p.ctx_len * p.width,
+                                                          (uint32_t)((int64_t)p.ctx_len * p.width * 2));
+            const int kcol = k0 - layer * p.width;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = t0 + rbase + q * 8 + dma_row;
+                dma16(rc, buf + kXStage + (rbase + q * 8) * kXRowB,
+                      (uint32_t)(((int64_t)row * p.width + kcol) * 2) + dma_piece, 0u);
+            }
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wi = (w >> 1) * 64, wj = (w & 1) * 128;
+    dma(0, st0);
+    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+        wait_vmcnt<0>();
+        barrier_lds();      // every wave's copies of step s landed; step s-1's reads are done
+        if (s + 1 < n_steps) dma(s + 1, nxt);
+        xkv_mma_step(cur, cur + kXStage, acc, wi, wj, lane);
+    };
+    for (int s = 0; s < n_steps; s += 2) {
+        step(s, st0, st1);
+        if (s + 1 < n_steps) step(s + 1, st1, st0);
+    }
+    wait_vmcnt<0>();
+    const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const int t = t0 + wj + nt * 16 + l16;
+        if (t >= p.ctx_len) continue;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int c = c0 + wi + mt * 16 + g4 * 4;
+            if (c >= p.rank) continue;
+            const f32x4 v = acc[mt][nt];
+            const uint32_t w0 = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a_out) + (int64_t)t * p.rank + c) = u32x2{w0, w1};
+        }
+    }
+}
+
+// -------------------------------------------------------------- launchers
+size_t xkv_partials_floats(const XkvParams& p) { return (size_t)p.n_chunks * p.n_upper * kXT * kXT; }
+
+hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(xkv_gram_kernel, dim3((unsigned)(p.n_chunks * p.n_upper), (unsigned)p.n_batch), dim3(kXThreads),
+                       0, s, p);
+    return hipGetLastError();
+}
+
+// out = in (rows x r) times the r x r matrix w, per problem (in's problem
+// stride 0 for the shared starting block).
+static void gemm_nn(const XkvParams& p, int rows, int k, const double* in, int64_t s_in, int64_t ld_in,
+                    const double* w, int64_t s_w, double* out, hipStream_t s) {
+    GemmArgs g{};
+    g.m = rows; g.n = p.rank; g.k = k; g.kc = k; g.splits = 1;
+    g.A = in; g.lda = ld_in; g.sA = s_in;
+    g.B = w; g.ldb = p.rank; g.sB = s_w;
+    g.C = out; g.ldc = p.rank; g.sC = (int64_t)rows * p.rank; g.c_split = 0;
+    const dim3 grid((unsigned)((p.rank + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)p.n_batch);
+    hipLaunchKernelGGL((xkv_gemm_f64_kernel<false, false>), grid, dim3(256), 0, s, g);
+}
+
+// g = y^T y (r x r per problem), the n-long contraction split k_splits ways.
+static void gram_tn(const XkvParams& p, const double* y, hipStream_t s) {
+    const int r = p.rank;
+    const int64_t nr = (int64_t)p.n * r, rr = (int64_t)r * r;
+    GemmArgs g{};
+    g.m = r; g.n = r; g.k = p.n; g.kc = (p.n + p.k_splits - 1) / p.k_splits; g.splits = p.k_splits;
+    g.A = y; g.lda = r; g.sA = nr;
+    g.B = y; g.ldb = r; g.sB = nr;
+    g.C = p.g_parts; g.ldc = r; g.sC = rr * p.k_splits; g.c_split = rr;
+    const dim3 grid((unsigned)((r + 63) / 64), (unsigned)((r + 63) / 64), (unsigned)(p.n_batch * p.k_splits));
+    hipLaunchKernelGGL((xkv_gemm_f64_kernel<true, false>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL(xkv_sum_splits_kernel, dim3((unsigned)((rr + 255) / 256), (unsigned)p.n_batch), dim3(256), 0, s,
+                       p.g_parts, p.g, rr, p.k_splits);
+}
+
+// out = orth(in) by one CholeskyQR pass: G = in^T in = L L^T, out = in L^-T
+// (L^-T from a triangular solve on the identity, then one product).
+static void cholqr(const XkvParams& p, const double* in, double* out, hipStream_t s) {
+    const int r = p.rank;
+    gram_tn(p, in, s);
+    hipLaunchKernelGGL(xkv_chol_kernel, dim3((unsigned)p.n_batch), dim3(1024), 0, s, p.g, r, p.dead);
+    hipLaunchKernelGGL(xkv_trsm_kernel, dim3((unsigned)((r + kTrRows - 1) / kTrRows), (unsigned)p.n_batch), dim3(256), 0,
+                       s, (const double*)nullptr, p.rinv, p.g, p.dead, r, r);
+    gemm_nn(p, p.n, r, in, (int64_t)p.n * r, r, p.rinv, (int64_t)r * r, out, s);
+}
+
+// Iterations, then the outputs. X_i = orth(M X_{i-1}); the intermediate
+// steps take one CholeskyQR pass (only their span feeds the next product),
+// the last one two (the second restores orthogonality to rounding level).
+hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(xkv_gram_reduce_kernel, dim3(kXT, (unsigned)p.n_upper, (unsigned)p.n_batch), dim3(256), 0, s, p);
+    const int64_t nr = (int64_t)p.n * p.rank;
+    double* buf[2] = {p.x, p.y};
+    const double* in = p.omega;
+    int64_t s_in = 0;
+    int cur = -1;
+    for (int it = 0; it < p.n_iter; ++it) {
+        const int prod = cur == 0 ? 1 : 0;
+        gemm_nn(p, p.n, p.n, p.m, (int64_t)p.n * p.n, p.n, in, s_in, buf[prod], s);   // M X: M is the left operand
+        cur = prod;
+        const int passes = it + 1 == p.n_iter ? 2 : 1;
+        for (int ps = 0; ps < passes; ++ps) {
+            cholqr(p, buf[cur], buf[1 - cur], s);
+            cur = 1 - cur;
+        }
+        in = buf[cur];
+        s_in = nr;
+    }
+    hipLaunchKernelGGL(xkv_emit_kernel, dim3((unsigned)(p.rank / 64), (unsigned)(p.n / 64), (unsigned)p.n_batch),
+                       dim3(256), 0, s, p, (const double*)buf[cur]);
+    const int n_ct = (p.rank + kXT - 1) / kXT, n_tt = (p.ctx_len + kXT - 1) / kXT;
+    hipLaunchKernelGGL(xkv_a_kernel, dim3((unsigned)(n_ct * n_tt), (unsigned)p.n_batch), dim3(kXThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace lowram

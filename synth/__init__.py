@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "PrefillConfig", "PREFILL_CONFIGS",
            "make_generator", "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
-           "gen_prefill_inputs", "block_ptr_from_idx"]
+           "gen_prefill_inputs", "block_ptr_from_idx", "XkvConfig", "XKV_CONFIGS", "gen_xkv_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -340,3 +340,55 @@ def gen_prefill_inputs(pc, device, *, res_dtype=None):
     s = torch.exp(torch.randn(L, T, hkv, 1, generator=g, device=device))
     out["v"] = (torch.randn(L, T, hkv, d, generator=g, device=device) * 0.125 * s).to(bf)
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class XkvConfig:
+    """A layer group's keys for the cross-layer factorisation: G layers of
+    [T, D] keys (D = Hkv d), factored at rank r with n_iter iterations. The
+    concatenated keys are Z diag(s) W with Z [T, m] standard normal,
+    s_i = exp(-i / decay) + floor and W [m, G D] normal / sqrt(m): energy in
+    few directions with a slowly decaying tail, no gap at r."""
+    name: str
+    n_layers: int
+    ctx_len: int
+    width: int
+    rank: int
+    latent: int
+    decay: float
+    floor: float = 0.03
+    n_iter: int = 3
+    seed: int = 7
+
+    @property
+    def n(self):
+        return self.n_layers * self.width
+
+
+XKV_CONFIGS = {c.name: c for c in (
+    XkvConfig("x_small_ragged", 2, 1000, 256, 64, 384, 40.0),
+    XkvConfig("x_short", 2, 40, 256, 64, 64, 10.0),          # fewer tokens than the rank
+    XkvConfig("x_mid", 4, 8192, 1024, 512, 1536, 200.0),
+    # one group of four Llama-3.1-8B layers (8 KV heads x 128) at 131072 tokens, r = 512
+    XkvConfig("x_llama_131k", 4, 131072, 1024, 512, 1536, 200.0),
+)}
+
+
+def gen_xkv_inputs(xc, device, batch=None):
+    """keys [G, T, D] bf16 (scaled to unit rms), or [batch, G, T, D] with an
+    independent draw per problem, and omega [G D, r] float64 standard normal,
+    the iteration's starting block shared by the problems."""
+    def one(tag):
+        g = make_generator(device, xc.seed, "xkv", xc.name, tag)
+        m = xc.latent
+        s = torch.exp(-torch.arange(m, device=device, dtype=torch.float32) / xc.decay) + xc.floor
+        z = torch.randn(xc.ctx_len, m, generator=g, device=device) * s
+        w = torch.randn(m, xc.n, generator=g, device=device) / math.sqrt(m)
+        cat = z @ w
+        del z
+        cat = cat / cat.pow(2).mean().sqrt()
+        return cat.reshape(xc.ctx_len, xc.n_layers, xc.width).permute(1, 0, 2).contiguous().to(torch.bfloat16)
+    keys = one(0) if batch is None else torch.stack([one(b) for b in range(batch)])
+    g = make_generator(device, xc.seed, "xkv-omega", xc.name)
+    omega = torch.randn(xc.n, xc.rank, generator=g, device=device, dtype=torch.float64)
+    return {"keys": keys, "omega": omega}

@@ -170,7 +170,8 @@ def test_prefill_struct_layout_matches_binding():
     body = text[text.index("typedef struct lowram_prefill_args"):text.index("} lowram_prefill_args;")]
     fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
     assert fields == [f[0] for f in B.PrefillArgs._fields_]
-    assert {"lowram_prefill_rank", "lowram_prefill_workspace_size"} <= set(declared_functions())
+    assert {"lowram_prefill_rank", "lowram_prefill_workspace_size", "lowram_xkv_factorize",
+            "lowram_xkv_workspace_size"} <= set(declared_functions())
 
 
 def valid_prefill():
@@ -210,3 +211,50 @@ def test_prefill_rejects(field, value, status):
     setattr(a, field, value)
     assert call_prefill(a) == status
     assert L.last_error() != ""
+
+
+# ------------------------------------------------------- cross-layer factors
+def valid_xkv():
+    a = B.XkvArgs()
+    a.n_batch, a.n_layers, a.ctx_len, a.width, a.rank, a.n_iter = 1, 4, 1000, 1024, 512, 3
+    for n in ("keys", "omega", "a", "b_l"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def call_xkv(a):
+    return L.lib().lowram_xkv_factorize(ctypes.byref(a), None)
+
+
+def test_xkv_valid_args_stop_at_workspace():
+    a = valid_xkv()
+    n = B.xkv_workspace_size(a)
+    assert n >= 4096 * 4096 * 8 + 2 * 4096 * 512 * 8      # M and the two basis blocks at least
+    assert call_xkv(a) == B.ERR_WORKSPACE
+
+
+def test_xkv_header_layout_matches_binding():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct lowram_xkv_args"):text.index("} lowram_xkv_args;")]
+    fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f[0] for f in B.XkvArgs._fields_]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("keys", None, B.ERR_ARG), ("omega", None, B.ERR_ARG), ("a", None, B.ERR_ARG), ("b_l", None, B.ERR_ARG),
+    ("basis", FAKE + 8, B.ERR_ARG), ("n_layers", 0, B.ERR_ARG), ("n_layers", 17, B.ERR_ARG), ("n_batch", 0, B.ERR_ARG),
+    ("ctx_len", 0, B.ERR_ARG), ("width", 128, B.ERR_UNSUPPORTED), ("width", 1000, B.ERR_UNSUPPORTED),
+    ("rank", 96, B.ERR_UNSUPPORTED), ("rank", 2048, B.ERR_UNSUPPORTED), ("n_iter", 0, B.ERR_ARG),
+    ("n_iter", 17, B.ERR_ARG), ("ctx_len", 1 << 20, B.ERR_UNSUPPORTED),   # T * D * 2 reaches 2^31
+])
+def test_xkv_rejects(field, value, status):
+    a = valid_xkv()
+    setattr(a, field, value)
+    assert call_xkv(a) == status
+    assert L.last_error() != ""
+
+
+def test_xkv_rank_above_width_rejected():
+    a = valid_xkv()
+    a.n_layers, a.width, a.rank = 1, 256, 320
+    assert call_xkv(a) == B.ERR_UNSUPPORTED
