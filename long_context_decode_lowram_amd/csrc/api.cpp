@@ -177,7 +177,7 @@ int plan_xkv(const lowram_xkv_args* a, XkvPlan* pl) {
     nc = nc > max_chunks ? max_chunks : nc;
     p.chunk_len = ((a->ctx_len + nc - 1) / nc + 63) / 64 * 64;
     p.n_chunks = (a->ctx_len + p.chunk_len - 1) / p.chunk_len;
-    const int tiles = (p.rank / 64) * (p.rank / 64) * a->n_batch;
+    const int tiles = ((p.rank + 127) / 128) * ((p.rank + 127) / 128) * a->n_batch;
     int ks = (512 + tiles - 1) / tiles;
     ks = ks > n / 256 ? n / 256 : ks;
     p.k_splits = ks < 1 ? 1 : ks;

@@ -166,67 +166,129 @@ __global__ __launch_bounds__(256) void xkv_gram_reduce_kernel(XkvParams p) {
 // Per problem q = z / splits and split z % splits: C_q (+ split * c_split)
 // = op(A_q) op(B_q) over k in [split kc, min(k, split kc + kc)), with
 // X_q = X + q sX, op(A)(i, kk) = TA ? A[kk lda + i] : A[i lda + kk] and
-// op(B)(kk, j) = TB ? B[j ldb + kk] : B[kk ldb + j]. 64 x 64 tiles, 16 deep;
-// each thread owns a 4 x 4 block.
+// op(B)(kk, j) = TB ? B[j ldb + kk] : B[kk ldb + j].
+//
+// fp64 MFMA (v_mfma_f64_16x16x4_f64): 128 x 128 tiles, 16 deep, four waves
+// of 64 x 64 (4 x 4 blocks of 16 x 16). LDS holds op(A) as [k][i] and op(B)
+// as [k][j], rows padded to 144 doubles so that the operand reads (16
+// consecutive i or j, four k rows per wave) and the staging writes hit
+// distinct banks; two stages, the next tile's loads held in registers while
+// the current one is multiplied.
 struct GemmArgs {
     int m, n, k, kc, splits;
     const double* A; int64_t lda, sA;
     const double* B; int64_t ldb, sB;
     double* C; int64_t ldc, sC, c_split;
 };
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kGm = 128, kGk = 16, kGld = 144;
+
+template <bool T>
+__device__ __forceinline__ void gemm_load(const double* X, int64_t ld, int rows, int k0, int ke, int r0, int tid,
+                                          double (&v)[8]) {
+    // The 128 x 16 tile of op(X) (rows r0.., k k0..): T means X is stored
+    // [k][row] (rows contiguous), else [row][k]. Thread tid fetches four
+    // 2-element pieces.
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        int row, kk;
+        if (T) { row = (e & 63) * 2; kk = e >> 6; }        // 2 consecutive rows at one k
+        else { row = e & 127; kk = (e >> 7) * 2; }         // 2 consecutive k at one row
+        const int gr = r0 + row, gk = k0 + kk;
+        if (T) {
+            v[2 * u] = (gr < rows && gk < ke) ? X[(int64_t)gk * ld + gr] : 0.0;
+            v[2 * u + 1] = (gr + 1 < rows && gk < ke) ? X[(int64_t)gk * ld + gr + 1] : 0.0;
+        } else {
+            v[2 * u] = (gr < rows && gk < ke) ? X[(int64_t)gr * ld + gk] : 0.0;
+            v[2 * u + 1] = (gr < rows && gk + 1 < ke) ? X[(int64_t)gr * ld + gk + 1] : 0.0;
+        }
+    }
+}
+
+template <bool T>
+__device__ __forceinline__ void gemm_store(double* s, int tid, const double (&v)[8]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = tid + 256 * u;
+        if (T) {
+            const int row = (e & 63) * 2, kk = e >> 6;
+            s[kk * kGld + row] = v[2 * u];
+            s[kk * kGld + row + 1] = v[2 * u + 1];
+        } else {
+            const int row = e & 127, kk = (e >> 7) * 2;
+            s[kk * kGld + row] = v[2 * u];
+            s[(kk + 1) * kGld + row] = v[2 * u + 1];
+        }
+    }
+}
+
 template <bool TA, bool TB>
-__global__ __launch_bounds__(256) void xkv_gemm_f64_kernel(GemmArgs g) {
-    __shared__ double as[16][64 + 4], bs[16][64 + 4];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+__global__ __launch_bounds__(256, 2) void xkv_gemm_f64_kernel(GemmArgs g) {
+    __shared__ double as[2][kGk * kGld], bs[2][kGk * kGld];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i0 = blockIdx.y * kGm, j0 = blockIdx.x * kGm;
     const int q = blockIdx.z / g.splits, split = blockIdx.z - q * g.splits;
-    const int m = g.m, n = g.n, k = g.k;
     const double* const A = g.A + q * g.sA;
     const double* const B = g.B + q * g.sB;
-    const int64_t lda = g.lda, ldb = g.ldb, ldc = g.ldc;
-    const int kb = split * g.kc, ke = min(k, kb + g.kc);
-    double acc[4][4];
+    const int kb = split * g.kc, ke = min(g.k, kb + g.kc);
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+    const int l16 = lane & 15, kl = lane >> 4;
+    f64x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = kb; k0 < ke; k0 += 16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = tid + 256 * q;
-            const int il = TA ? (e & 63) : (e >> 4), kl = TA ? (e >> 6) : (e & 15);
-            const int gi = i0 + il, gk = k0 + kl;
-            as[kl][il] = (gi < m && gk < ke) ? (TA ? A[(int64_t)gk * lda + gi] : A[(int64_t)gi * lda + gk]) : 0.0;
-            const int jl = TB ? (e >> 4) : (e & 63), kl2 = TB ? (e & 15) : (e >> 6);
-            const int gj = j0 + jl, gk2 = k0 + kl2;
-            bs[kl2][jl] = (gj < n && gk2 < ke) ? (TB ? B[(int64_t)gj * ldb + gk2] : B[(int64_t)gk2 * ldb + gj]) : 0.0;
+        for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    double va[8], vb[8];
+    // op(A)(i, k): stored [k][i] when TA; op(B)(k, j): stored [k][j] unless TB.
+    gemm_load<TA>(A, g.lda, g.m, kb, ke, i0, tid, va);
+    gemm_load<!TB>(B, g.ldb, g.n, kb, ke, j0, tid, vb);
+    gemm_store<TA>(as[0], tid, va);
+    gemm_store<!TB>(bs[0], tid, vb);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kb; k0 < ke; k0 += kGk) {
+        const bool more = k0 + kGk < ke;
+        if (more) {
+            gemm_load<TA>(A, g.lda, g.m, k0 + kGk, ke, i0, tid, va);
+            gemm_load<!TB>(B, g.ldb, g.n, k0 + kGk, ke, j0, tid, vb);
         }
-        __syncthreads();
+        const double* sa = as[buf];
+        const double* sb = bs[buf];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            double av[4], bv[4];
+        for (int ks = 0; ks < kGk / 4; ++ks) {
+            double fa[4], fb[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = as[kk][ty * 4 + a];
+            for (int a = 0; a < 4; ++a) fa[a] = sa[(ks * 4 + kl) * kGld + wm + a * 16 + l16];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = bs[kk][tx * 4 + b];
+            for (int b = 0; b < 4; ++b) fb[b] = sb[(ks * 4 + kl) * kGld + wn + b * 16 + l16];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+                for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        }
+        if (more) {
+            gemm_store<TA>(as[buf ^ 1], tid, va);
+            gemm_store<!TB>(bs[buf ^ 1], tid, vb);
         }
         __syncthreads();
+        buf ^= 1;
     }
+    // D block (a, b) of the fp64 MFMA: value v of a lane is row lane / 16 + 4 v,
+    // column lane % 16 (rows interleaved, unlike the fp32 variants).
     double* out = g.C + q * g.sC + split * g.c_split;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int i = i0 + ty * 4 + a;
-        if (i >= m) continue;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int j = j0 + tx * 4 + b;
-            if (j < n) out[(int64_t)i * ldc + j] = acc[a][b];
+            const int j = j0 + wn + b * 16 + l16;
+            if (j >= g.n) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = i0 + wm + a * 16 + kl + 4 * v;
+                if (i < g.m) out[(int64_t)i * g.ldc + j] = acc[a][b][v];
+            }
         }
-    }
 }
 
 // out_q[i] = sum over s of parts_q[s count + i], in split order (grid y: problem q).
@@ -483,15 +545,20 @@ hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s) {
 
 // out = in (rows x r) times the r x r matrix w, per problem (in's problem
 // stride 0 for the shared starting block).
+// `symmetric` says in == in^T (the Gram matrix), which is then read in its
+// transposed, coalesced form.
 static void gemm_nn(const XkvParams& p, int rows, int k, const double* in, int64_t s_in, int64_t ld_in,
-                    const double* w, int64_t s_w, double* out, hipStream_t s) {
+                    const double* w, int64_t s_w, double* out, bool symmetric, hipStream_t s) {
     GemmArgs g{};
     g.m = rows; g.n = p.rank; g.k = k; g.kc = k; g.splits = 1;
     g.A = in; g.lda = ld_in; g.sA = s_in;
     g.B = w; g.ldb = p.rank; g.sB = s_w;
     g.C = out; g.ldc = p.rank; g.sC = (int64_t)rows * p.rank; g.c_split = 0;
-    const dim3 grid((unsigned)((p.rank + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)p.n_batch);
-    hipLaunchKernelGGL((xkv_gemm_f64_kernel<false, false>), grid, dim3(256), 0, s, g);
+    const dim3 grid((unsigned)((p.rank + kGm - 1) / kGm), (unsigned)((rows + kGm - 1) / kGm), (unsigned)p.n_batch);
+    if (symmetric)
+        hipLaunchKernelGGL((xkv_gemm_f64_kernel<true, false>), grid, dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((xkv_gemm_f64_kernel<false, false>), grid, dim3(256), 0, s, g);
 }
 
 // g = y^T y (r x r per problem), the n-long contraction split k_splits ways.
@@ -503,7 +570,7 @@ static void gram_tn(const XkvParams& p, const double* y, hipStream_t s) {
     g.A = y; g.lda = r; g.sA = nr;
     g.B = y; g.ldb = r; g.sB = nr;
     g.C = p.g_parts; g.ldc = r; g.sC = rr * p.k_splits; g.c_split = rr;
-    const dim3 grid((unsigned)((r + 63) / 64), (unsigned)((r + 63) / 64), (unsigned)(p.n_batch * p.k_splits));
+    const dim3 grid((unsigned)((r + kGm - 1) / kGm), (unsigned)((r + kGm - 1) / kGm), (unsigned)(p.n_batch * p.k_splits));
     hipLaunchKernelGGL((xkv_gemm_f64_kernel<true, false>), grid, dim3(256), 0, s, g);
     hipLaunchKernelGGL(xkv_sum_splits_kernel, dim3((unsigned)((rr + 255) / 256), (unsigned)p.n_batch), dim3(256), 0, s,
                        p.g_parts, p.g, rr, p.k_splits);
@@ -517,7 +584,7 @@ static void cholqr(const XkvParams& p, const double* in, double* out, hipStream_
     hipLaunchKernelGGL(xkv_chol_kernel, dim3((unsigned)p.n_batch), dim3(1024), 0, s, p.g, r, p.dead);
     hipLaunchKernelGGL(xkv_trsm_kernel, dim3((unsigned)((r + kTrRows - 1) / kTrRows), (unsigned)p.n_batch), dim3(256), 0,
                        s, (const double*)nullptr, p.rinv, p.g, p.dead, r, r);
-    gemm_nn(p, p.n, r, in, (int64_t)p.n * r, r, p.rinv, (int64_t)r * r, out, s);
+    gemm_nn(p, p.n, r, in, (int64_t)p.n * r, r, p.rinv, (int64_t)r * r, out, false, s);
 }
 
 // Iterations, then the outputs. X_i = orth(M X_{i-1}); the intermediate
@@ -532,7 +599,7 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s) {
     int cur = -1;
     for (int it = 0; it < p.n_iter; ++it) {
         const int prod = cur == 0 ? 1 : 0;
-        gemm_nn(p, p.n, p.n, p.m, (int64_t)p.n * p.n, p.n, in, s_in, buf[prod], s);   // M X: M is the left operand
+        gemm_nn(p, p.n, p.n, p.m, (int64_t)p.n * p.n, p.n, in, s_in, buf[prod], true, s);   // M X
         cur = prod;
         const int passes = it + 1 == p.n_iter ? 2 : 1;
         for (int ps = 0; ps < passes; ++ps) {
