@@ -74,72 +74,140 @@ __device__ __forceinline__ void xkv_tile(int k, int nt, int& ti, int& tj) {
 // so the workgroups resident together share one chunk of C). The stored
 // partial is the transposed tile: P[a][b] = sum_t C[t][256 I + b] C[t][256 J + a]
 // = M[256 J + a][256 I + b].
-__global__ __launch_bounds__(kXThreads, 1) void xkv_gram_kernel(XkvParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char stg[2][2][kXStage];   // [buffer][operand]
+//
+// Four waves, one per SIMD, each owning a 128 x 128 quarter of the tile (256
+// accumulator registers). The keys come into LDS untransposed, by direct
+// copies three 32-token steps ahead in a ring of four stages: per stage and
+// operand 32 token rows x 256 columns (512-byte rows of 32 pieces of 16
+// bytes, piece p of row t in slot p ^ gsw(t)). The MFMA fragments are read
+// with the transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lanes 4r .. 4r+3 name row r's 16 consecutive columns and lane j gets
+// column j of those 4 rows, i.e. 4 consecutive tokens of one column; two such
+// reads make the 8 tokens of a fragment.
+constexpr int kGramThreads = 256;
+constexpr int kGK = 32;                          // tokens per step
+constexpr int kGRowB = kXT * 2;                  // 512-byte rows
+constexpr int kGOp = kGK * kGRowB;               // 16 KB per operand per stage
+constexpr int kGStage = 2 * kGOp;                // both operands
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+
+// Row t's slot swizzle: twice a 4-bit value from bits 0-1 and 3-4 of t, so the
+// 16 rows (8 g + v, g, v < 4) that one transposing read touches hit 16
+// distinct 32-byte column pairs, two per bank set.
+__device__ __forceinline__ int gsw(int t) { return 2 * ((t & 3) | (((t >> 3) & 3) << 2)); }
+
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* op, uint32_t off) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off + 4 * kGRowB));
+    u32x4 v;
+    v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return as_bf16x8(v);
+}
+
+// 64 MFMAs of one 32-token step of the wave's 128 x 128 block.
+__device__ __forceinline__ void gram_step(const unsigned char* stage, f32x4 (&acc)[8][8], int wi, int wj,
+                                          uint32_t lane_off, int lane_sw) {
+    const unsigned char* op0 = stage;
+    const unsigned char* op1 = stage + kGOp;
+    auto off = [&](int m0) { return lane_off + ((uint32_t)(((m0 >> 3) ^ lane_sw)) << 4); };
+    bf16x8 af[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) af[mt] = tr_frag(op0, off(wi + mt * 16));
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh) {
+        bf16x8 bf[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bf[nt] = tr_frag(op1, off(wj + (nh * 4 + nt) * 16));
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nh * 4 + nt] = mfma(af[mt], bf[nt], acc[mt][nh * 4 + nt]);
+    }
+}
+
+__global__ __launch_bounds__(kGramThreads, 1) void xkv_gram_kernel(XkvParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char st0[kGStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[kGStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st2[kGStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st3[kGStage];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = blockIdx.x / p.n_upper;
     const int tile = blockIdx.x - chunk * p.n_upper;
     int ti, tj;
     xkv_tile(tile, p.nt, ti, tj);
-    const bool diag = ti == tj;
     const int t_begin = chunk * p.chunk_len;
     const int t_end = min(p.ctx_len, t_begin + p.chunk_len);
-    const int n_steps = (t_end - t_begin + kXK - 1) / kXK;
-
-    // Staging: waves 0-3 bring tile I's columns, waves 4-7 tile J's (idle on
-    // a diagonal tile). A thread moves an 8-token x 8-column block per step
-    // and transposes it in registers, so that LDS rows run along the tokens.
-    const int op = w >> 2;
-    const bool stager = !(diag && op == 1);
-    const int cb = (w & 3) * 8 + (lane >> 3);      // column block of the tile (8 columns)
-    const int tb = lane & 7;                       // token block of the step (8 tokens)
-    const int col0 = (op == 0 ? ti : tj) * kXT;
-    const int layer = col0 / p.width;
+    const int n_steps = (t_end - t_begin + kGK - 1) / kGK;
     const int64_t prob = blockIdx.y;
-    const __bf16* src = p.keys + (prob * p.n_layers + layer) * p.ctx_len * (int64_t)p.width + (col0 - layer * p.width) + cb * 8;
-    u32x4 pre[8];
-    auto load = [&](int t0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = t0 + tb * 8 + j;
-            pre[j] = (stager && t < t_end) ? *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.width)
-                                           : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store = [&](int buf) {
-        if (!stager) return;
-        unsigned char* dst = stg[buf][op];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = pre[2 * q][c >> 1], hi = pre[2 * q + 1][c >> 1];
-                o[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            *reinterpret_cast<u32x4*>(dst + xslot(cb * 8 + c, tb)) = o;
-        }
-    };
 
-    f32x4 acc[4][8];
+    // Operand slices as buffers over this chunk's tokens (zeros past t_end).
+    auto slice = [&](int tcol) {
+        const int col0 = tcol * kXT, layer = col0 / p.width;
+        const __bf16* base = p.keys + (prob * p.n_layers + layer) * p.ctx_len * (int64_t)p.width +
+                             (int64_t)t_begin * p.width + (col0 - layer * p.width);
+        return buffer_rsrc(base, (uint32_t)((int64_t)(t_end - t_begin) * p.width * 2));
+    };
+    const __amdgpu_buffer_rsrc_t r0 = slice(ti), r1 = slice(tj);
+    // Copies: wave w fills rows 8 w .. 8 w + 7 of both operands, 2 rows per
+    // instruction; lane i lands in row 8 w + 2 q + i / 32, slot i % 32, and
+    // fetches the piece that belongs there.
+    const uint32_t row_b = (uint32_t)(p.width * 2);
+    uint32_t voff[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int q = 0; q < 4; ++q) {
+        const int row = w * 8 + q * 2 + (lane >> 5);
+        const int piece = (lane & 31) ^ gsw(row);
+        voff[q] = (uint32_t)row * row_b + (uint32_t)piece * 16;
+    }
+    auto dma = [&](int s, unsigned char* stage) {
+        const uint32_t soff = (uint32_t)s * kGK * row_b;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            dma16(r0, stage + (w * 8 + q * 2) * kGRowB, voff[q], soff);
+            dma16(r1, stage + kGOp + (w * 8 + q * 2) * kGRowB, voff[q], soff);
+        }
+    };
+    // Transposing-read address of this lane (fragment rows m0 added per read).
+    const int g = lane >> 4, i16 = lane & 15;
+    const int trow = 8 * g + (i16 >> 2);
+    const int lane_sw = gsw(trow) | ((i16 & 3) >> 1);
+    const uint32_t lane_off = (uint32_t)(trow * kGRowB + ((i16 & 1) << 3));
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int wi = (w >> 1) * 64, wj = (w & 1) * 128;
-    load(t_begin);
-    store(0);
-    for (int s = 0; s < n_steps; ++s) {
-        __syncthreads();    // step s's buffer is written; step s-1's reads of the other are done
-        if (s + 1 < n_steps) load(t_begin + (s + 1) * kXK);
-        const int b = s & 1;
-        xkv_mma_step(stg[b][0], stg[b][diag ? 0 : 1], acc, wi, wj, lane);
-        if (s + 1 < n_steps) store(b ^ 1);
+    const int wi = (w >> 1) * 128, wj = (w & 1) * 128;
+
+    dma(0, st0);
+    if (n_steps > 1) dma(1, st1);
+    if (n_steps > 2) dma(2, st2);
+    // Step s: wait for this wave's copies of s (those of s+1 and s+2 may stay
+    // in flight, 8 per step), meet, start s+3 into the stage s-1 used, multiply.
+    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+        if (s + 2 < n_steps) wait_vmcnt<16>();
+        else if (s + 1 < n_steps) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        barrier_lds();
+        if (s + 3 < n_steps) dma(s + 3, nxt);
+        gram_step(cur, acc, wi, wj, lane_off, lane_sw);
+    };
+    for (int s = 0; s < n_steps; s += 4) {
+        step(s, st0, st3);
+        if (s + 1 < n_steps) step(s + 1, st1, st0);
+        if (s + 2 < n_steps) step(s + 2, st2, st1);
+        if (s + 3 < n_steps) step(s + 3, st3, st2);
     }
     float* out = p.partials + ((prob * p.n_chunks + chunk) * p.n_upper + tile) * (kXT * kXT);
     const int l16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
             *reinterpret_cast<f32x4*>(out + (wj + nt * 16 + l16) * kXT + wi + mt * 16 + g4 * 4) = acc[mt][nt];
@@ -538,8 +606,8 @@ __global__ __launch_bounds__(kXThreads, 1) void xkv_a_kernel(XkvParams p) {
 size_t xkv_partials_floats(const XkvParams& p) { return (size_t)p.n_chunks * p.n_upper * kXT * kXT; }
 
 hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(xkv_gram_kernel, dim3((unsigned)(p.n_chunks * p.n_upper), (unsigned)p.n_batch), dim3(kXThreads),
-                       0, s, p);
+    hipLaunchKernelGGL(xkv_gram_kernel, dim3((unsigned)(p.n_chunks * p.n_upper), (unsigned)p.n_batch),
+                       dim3(kGramThreads), 0, s, p);
     return hipGetLastError();
 }
 
