@@ -46,6 +46,7 @@ from .rank import (residual_error, select_worst, round_bf16, round_f32,
                    quantize_int8_rows, dequantize_int8_rows, quantize_i2_rows,
                    dequantize_i2_rows, pack_i2, unpack_i2, block_ptr, rank_residuals)
 from .factor import xkv_factorize, xkv_subspace_iteration, pinv_value_map
+from .fit import gelu_grad, predictor_loss_and_grads, fit_predictor
 from .prefill import predicted_values, prefill_rank
 from .budget import value_budget, dense_kv_bytes_per_token
 
@@ -55,6 +56,7 @@ __all__ = [
     "residual_error", "select_worst", "round_bf16", "round_f32",
     "quantize_int8_rows", "dequantize_int8_rows", "quantize_i2_rows", "dequantize_i2_rows",
     "pack_i2", "unpack_i2", "block_ptr", "rank_residuals",
-    "xkv_factorize", "xkv_subspace_iteration", "pinv_value_map", "value_budget", "dense_kv_bytes_per_token",
+    "xkv_factorize", "xkv_subspace_iteration", "pinv_value_map", "gelu_grad", "predictor_loss_and_grads",
+    "fit_predictor", "value_budget", "dense_kv_bytes_per_token",
     "predicted_values", "prefill_rank",
 ]

@@ -573,3 +573,78 @@ def test_rank_residuals_i2_matches_its_codec():
             q, s = oracle.quantize_i2_rows(r)
             np.testing.assert_array_equal(oracle.unpack_i2(a["val"][sl, h]), q)
             np.testing.assert_array_equal(a["scale"][sl, h], s)
+
+
+# ------------------------------------------------------------ predictor fit
+def _fit_case(rng, n_tok=7, d=3, hid=4):
+    return dict(k=rng.standard_normal((n_tok, d)), v=rng.standard_normal((n_tok, d)),
+                w_lin=rng.standard_normal((d, d)) * 0.5, w1=rng.standard_normal((hid, d)) * 0.7,
+                b1=rng.standard_normal(hid) * 0.3, w2=rng.standard_normal((d, hid)) * 0.6,
+                b2=rng.standard_normal(d) * 0.2)
+
+
+def _loss_py(c):
+    """Scalar loop from the definitions: mean over tokens of the squared error
+    of the predictor (math.erf GELU, no numpy arithmetic)."""
+    tl = lambda x: np.asarray(x, np.float64).tolist()  # noqa: E731
+    k, v, wl, w1, b1, w2, b2 = (tl(c[n]) for n in ("k", "v", "w_lin", "w1", "b1", "w2", "b2"))
+    tot = 0.0
+    for t in range(len(k)):
+        hid = [_gelu_py(sum(k[t][i] * w1[u][i] for i in range(len(k[t]))) + b1[u]) for u in range(len(w1))]
+        for o in range(len(v[t])):
+            vh = sum(k[t][i] * wl[o][i] for i in range(len(k[t]))) + sum(hid[u] * w2[o][u] for u in range(len(hid))) + b2[o]
+            tot += (vh - v[t][o]) ** 2
+    return tot / len(k)
+
+
+def test_fit_gradient_matches_central_differences():
+    """One gradient step recovers the gradient, (theta0 - theta1) / lr, which
+    must match central differences of the scalar-loop loss for every
+    parameter of a tiny case."""
+    rng = np.random.default_rng(50)
+    c = _fit_case(rng)
+    lr = 1e-3
+    w1, b1, w2, b2, losses = oracle.fit_predictor(c["k"], c["v"], c["w_lin"], c["w1"], c["b1"], c["w2"], c["b2"], lr, 1)
+    assert abs(losses[0] - _loss_py(c)) < 1e-12
+    got = {"w1": (c["w1"] - w1) / lr, "b1": (c["b1"] - b1) / lr, "w2": (c["w2"] - w2) / lr, "b2": (c["b2"] - b2) / lr}
+    eps = 1e-6
+    for name, g in got.items():
+        num = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            cp = {kk: np.array(vv, np.float64) for kk, vv in c.items()}
+            cm = {kk: np.array(vv, np.float64) for kk, vv in c.items()}
+            cp[name][idx] += eps
+            cm[name][idx] -= eps
+            num[idx] = (_loss_py(cp) - _loss_py(cm)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_fit_special_cases():
+    """No steps leave the parameters as they are; values that the linear map
+    already predicts exactly (w2 = 0, b2 = 0) give zero loss and zero
+    gradients, so steps change nothing; on a generic case a small rate lowers
+    the loss at every step."""
+    rng = np.random.default_rng(51)
+    c = _fit_case(rng, n_tok=40)
+    out = oracle.fit_predictor(c["k"], c["v"], c["w_lin"], c["w1"], c["b1"], c["w2"], c["b2"], 0.1, 0)
+    for a, b in zip(out[:4], (c["w1"], c["b1"], c["w2"], c["b2"])):
+        np.testing.assert_array_equal(a, b)
+    assert len(out[4]) == 1
+    v_lin = c["k"] @ c["w_lin"].T
+    out = oracle.fit_predictor(c["k"], v_lin, c["w_lin"], c["w1"], c["b1"], np.zeros_like(c["w2"]),
+                               np.zeros_like(c["b2"]), 0.5, 3)
+    np.testing.assert_array_equal(out[0], c["w1"])
+    np.testing.assert_array_equal(out[2], 0.0)
+    assert np.all(out[4] < 1e-28)
+    losses = oracle.fit_predictor(c["k"], c["v"], c["w_lin"], c["w1"], c["b1"], c["w2"], c["b2"], 0.02, 25)[4]
+    assert np.all(np.diff(losses) < 0)
+
+
+def test_gelu_grad_closed_form():
+    """gelu'(0) = 1/2; gelu'(z) + gelu'(-z) = 1 (from gelu(z) - gelu(-z) = z);
+    central differences of the oracle's gelu."""
+    z = np.linspace(-6, 6, 121)
+    assert oracle.gelu_grad(0.0) == 0.5
+    np.testing.assert_allclose(oracle.gelu_grad(z) + oracle.gelu_grad(-z), 1.0, atol=1e-15)
+    h = 1e-6
+    np.testing.assert_allclose(oracle.gelu_grad(z), (oracle.gelu(z + h) - oracle.gelu(z - h)) / (2 * h), atol=1e-8)
