@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rank", action="store_true", help="also time the residual ranking at its full shape")
     ap.add_argument("--xkv", action="store_true", help="also time the cross-layer key factorisation")
+    ap.add_argument("--fit", action="store_true", help="also time the predictor's test-time fit")
     ap.add_argument("--prefill", action="store_true",
                     help="also time the fused prefill ranking (V_hat computed in the library) at its full shape")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -276,6 +277,8 @@ def main():
         result["prefill_rank"] = bench_prefill(max(2, args.steps // 3), 1, ev)
     if args.xkv:
         result["xkv_factorize"] = bench_xkv(max(2, args.steps // 3), 1, ev)
+    if args.fit:
+        result["fit_predictor"] = bench_fit(2, 1, ev)
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -448,6 +451,48 @@ def bench_xkv(steps, warmup, ev):
             "keys_GBs": x["keys"].numel() * 2 / (ms * 1e-3) / 1e9, "gram_kernel_ms": gram_ms,
             "gram_kernel_TFLOPs": gram_flops / (gram_ms * 1e-3) / 1e12,
             "gram_kernel_frac_of_bf16_peak": gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def bench_fit(steps, warmup, ev):
+    """The predictor's test-time fit for a whole Llama-3.1-8B prefill at
+    131072 tokens: 32 layers x 8 KV heads, h = 256, the quick two-step fit,
+    all (layer, head) problems in one call. The gradient steps are timed by
+    HIP events on the stream they run on; their work is 2 d (5 h + d) FLOP per
+    token and problem (forward W1 and W_lin/W2 products, the W2 product of the
+    backward, and the two weight-gradient products)."""
+    import torch
+    import long_context_decode_lowram_amd as L
+    import synth
+
+    fc = synth.FIT_CONFIGS["f_llama_131k"]
+    x = synth.gen_fit_inputs(fc, "cuda")
+    P, T, d, h = fc.n_layers * fc.n_kv_heads, fc.ctx_len, fc.head_dim, fc.hidden
+    losses = torch.empty(fc.n_layers, fc.n_kv_heads, fc.n_steps + 1, dtype=torch.float32, device="cuda")
+    args = L.make_fit_args(x["keys"], x["v"], x["w_lin"], x["w1"], x["b1"], x["w2"], x["b2"], fc.n_steps, fc.lr,
+                           losses=losses)
+    ws = torch.empty(L.fit_workspace_size(args), dtype=torch.uint8, device="cuda")
+    args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+    for _ in range(warmup):
+        L.fit_launch(args)
+    torch.cuda.synchronize()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(steps):
+        args.ev_main_begin, args.ev_main_end = evs[i]
+        L.fit_launch(args)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / steps
+    step_ms = sum(ev.elapsed_ms(a, b) for a, b in evs) / steps / fc.n_steps
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    flops = 2.0 * d * (5 * h + d) * T * P
+    return {"problems": P, "ctx_len": T, "hidden": h, "n_steps": fc.n_steps, "lr": fc.lr, "ms_per_call": ms,
+            "ms_per_gradient_step": step_ms, "step_TFLOPs": flops / (step_ms * 1e-3) / 1e12,
+            "step_frac_of_bf16_peak": flops / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "loss_first_last_mean": [float(losses[..., 0].mean()), float(losses[..., -1].mean())]}
 
 
 if __name__ == "__main__":

@@ -280,6 +280,75 @@ typedef struct lowram_xkv_args {
 int    lowram_xkv_factorize(const lowram_xkv_args *args, void *stream);
 size_t lowram_xkv_workspace_size(const lowram_xkv_args *args);
 
+/*
+ * Pseudoinverse start of the per-head linear value map (explainer, Slim
+ * Attention paragraph: the predictor starts from the best linear guess the
+ * projections allow). For each of n_maps problems (e.g. layer x KV head),
+ * with row vectors k = x W_K and v = x W_V over the model width:
+ *   W_lin = pinv(W_K) W_V = (W_K^T W_K)^-1 W_K^T W_V,
+ * computed in binary64 (Cholesky of W_K^T W_K; a pivot at or below
+ * d 2^-52 times the largest diagonal entry drops that direction, which is
+ * the pseudoinverse on a rank-deficient W_K's range). Output w_lin is
+ * output-major [d, d] = W_lin^T, the layout the decode step reads, rounded to
+ * bf16 once; w_lin64 the same in binary64 if not NULL.
+ * Shapes: w_k, w_v [P, hidden, d] bf16; hidden in [d, 65536], d = 128.
+ */
+typedef struct lowram_pinv_args {
+    int32_t n_maps;             /* P                                                */
+    int32_t hidden;             /* model width                                      */
+    int32_t head_dim;           /* d                                                */
+    const void *w_k;            /* [P, hidden, d] bf16                              */
+    const void *w_v;            /* [P, hidden, d] bf16                              */
+    void       *w_lin;          /* [P, d, d] bf16 out                               */
+    double     *w_lin64;        /* [P, d, d] out, or NULL                           */
+    void       *workspace;
+    size_t      workspace_bytes;
+} lowram_pinv_args;
+
+int    lowram_pinv_value_map(const lowram_pinv_args *args, void *stream);
+size_t lowram_pinv_workspace_size(const lowram_pinv_args *args);
+
+/*
+ * Test-time fit of the predictor's nonlinear branch (explainer, mechanism
+ * paragraph: a small two-layer network per head fitted during prefill to this
+ * context; Slim Attention paragraph: it learns what the linear map leaves;
+ * cost paragraph: a number of gradient steps per context). The pages name
+ * neither loss nor optimiser; this library takes the mean over tokens of the
+ * squared L2 value error,
+ *   L = (1/T) sum_t || k_t W_lin + gelu(k_t W1 + b1) W2 + b2 - v_t ||^2,
+ * and n_steps of plain gradient descent theta <- theta - lr dL/dtheta on
+ * W1, b1, W2, b2 (W_lin fixed), for every (layer, KV head) at once. Products
+ * in bf16 with float32 sums (keys, values, the bf16 copies of the weights and
+ * the intermediate activations and gradients are bf16); the parameters are
+ * float32 masters updated in place. gelu is the exact erf form.
+ * losses[l, h, i] is L before step i and losses[l, h, n_steps] after the
+ * last step.
+ * Shapes (L layers, T tokens, Hkv heads, d = 128, h = mlp_hidden, a multiple
+ * of 128 in [128, 1024]): keys [L, T, Hkv*d] bf16 (e.g. A B_l), v [L, T, Hkv,
+ * d] bf16, w_lin [L, Hkv, d, d] bf16 output-major; w1 [L, Hkv, h, d], b1
+ * [L, Hkv, h], w2 [L, Hkv, d, h], b2 [L, Hkv, d] float32 in/out (output-major,
+ * as the decode step reads them after a bf16 conversion). T Hkv d 2 < 2^31.
+ */
+typedef struct lowram_fit_args {
+    int32_t n_layers, ctx_len, n_kv_heads, head_dim, mlp_hidden, n_steps;
+    float   lr;
+    const void *keys;           /* [L, T, Hkv*d] bf16                               */
+    const void *v;              /* [L, T, Hkv, d] bf16                              */
+    const void *w_lin;          /* [L, Hkv, d, d] bf16                              */
+    float      *w1;             /* [L, Hkv, h, d] float32 in/out                    */
+    float      *b1;             /* [L, Hkv, h]                                      */
+    float      *w2;             /* [L, Hkv, d, h]                                   */
+    float      *b2;             /* [L, Hkv, d]                                      */
+    float      *losses;         /* [L, Hkv, n_steps + 1] out, or NULL               */
+    void       *workspace;
+    size_t      workspace_bytes;
+    void       *ev_main_begin;  /* optional hipEvent_t around the gradient steps    */
+    void       *ev_main_end;
+} lowram_fit_args;
+
+int    lowram_fit_predictor(const lowram_fit_args *args, void *stream);
+size_t lowram_fit_workspace_size(const lowram_fit_args *args);
+
 /* Static description of a status code. */
 const char *lowram_status_string(int status);
 

@@ -57,6 +57,18 @@ class XkvArgs(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
 
 
+class PinvArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("n_maps", "hidden", "head_dim")] + [
+        (n, _p) for n in ("w_k", "w_v", "w_lin", "w_lin64", "workspace")] + [("workspace_bytes", ctypes.c_size_t)]
+
+
+class FitArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("n_layers", "ctx_len", "n_kv_heads", "head_dim", "mlp_hidden", "n_steps")] + [
+        ("lr", ctypes.c_float)] + [
+        (n, _p) for n in ("keys", "v", "w_lin", "w1", "b1", "w2", "b2", "losses", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+
+
 class LowramError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"liblowram status {status}: {msg}")
@@ -90,6 +102,12 @@ def lib():
         L.lowram_xkv_factorize.restype = ctypes.c_int
         L.lowram_xkv_workspace_size.argtypes = [ctypes.POINTER(XkvArgs)]
         L.lowram_xkv_workspace_size.restype = ctypes.c_size_t
+        for name, st in (("pinv_value_map", PinvArgs), ("fit_predictor", FitArgs)):
+            getattr(L, "lowram_" + name).argtypes = [ctypes.POINTER(st), _p]
+            getattr(L, "lowram_" + name).restype = ctypes.c_int
+        for name, st in (("pinv", PinvArgs), ("fit", FitArgs)):
+            getattr(L, f"lowram_{name}_workspace_size").argtypes = [ctypes.POINTER(st)]
+            getattr(L, f"lowram_{name}_workspace_size").restype = ctypes.c_size_t
         L.lowram_status_string.argtypes = [ctypes.c_int]
         L.lowram_status_string.restype = ctypes.c_char_p
         L.lowram_last_error.argtypes = []
@@ -364,3 +382,73 @@ def xkv_factorize(keys, omega, n_iter=3, *, want_basis=False, workspace=None, st
     if single:
         out = {k: (None if v is None else v[0]) for k, v in out.items()}
     return out
+
+
+def _run(fn, args, size_fn, device, workspace, stream):
+    if workspace is None:
+        n = size_fn(ctypes.byref(args))
+        if n == 0:
+            raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    args.workspace = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    rc = fn(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def pinv_value_map(w_k, w_v, *, want_f64=False, workspace=None, stream=None):
+    """W_lin = pinv(W_K) W_V for P maps: w_k, w_v [P, hidden, d] bf16 ->
+    (w_lin [P, d, d] bf16 output-major, w_lin64 float64 or None)."""
+    P, hidden, d = w_k.shape
+    args = PinvArgs()
+    args.n_maps, args.hidden, args.head_dim = P, hidden, d
+    w_lin = torch.empty(P, d, d, dtype=torch.bfloat16, device=w_k.device)
+    w64 = torch.empty(P, d, d, dtype=torch.float64, device=w_k.device) if want_f64 else None
+    for name, t in (("w_k", w_k), ("w_v", w_v), ("w_lin", w_lin), ("w_lin64", w64)):
+        setattr(args, name, _ptr(t))
+    L = lib()
+    _run(L.lowram_pinv_value_map, args, L.lowram_pinv_workspace_size, w_k.device, workspace, stream)
+    return w_lin, w64
+
+
+def make_fit_args(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, *, losses=None, workspace=None, events=None):
+    """Fill a FitArgs: keys [L, T, Hkv*d] bf16, v [L, T, Hkv, d] bf16,
+    w_lin [L, Hkv, d, d] bf16, float32 parameters w1 [L, Hkv, h, d],
+    b1 [L, Hkv, h], w2 [L, Hkv, d, h], b2 [L, Hkv, d] (updated in place)."""
+    Lr, T, hkv, d = v.shape
+    args = FitArgs()
+    args.n_layers, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, T, hkv, d
+    args.mlp_hidden, args.n_steps, args.lr = w1.shape[2], n_steps, lr
+    for name, t in (("keys", keys), ("v", v), ("w_lin", w_lin), ("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2),
+                    ("losses", losses), ("workspace", workspace)):
+        setattr(args, name, _ptr(t))
+    args.workspace_bytes = 0 if workspace is None else workspace.numel()
+    if events is not None:
+        args.ev_main_begin, args.ev_main_end = events
+    return args
+
+
+def fit_workspace_size(args):
+    n = lib().lowram_fit_workspace_size(ctypes.byref(args))
+    if n == 0:
+        raise LowramError(ERR_ARG, last_error() or "invalid arguments")
+    return n
+
+
+def fit_launch(args, stream=None):
+    rc = lib().lowram_fit_predictor(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def fit_predictor(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, *, workspace=None, stream=None):
+    """n_steps of gradient descent on the nonlinear branch of every (layer, KV
+    head) predictor; updates w1, b1, w2, b2 in place and returns the losses
+    [L, Hkv, n_steps + 1]."""
+    Lr, T, hkv, d = v.shape
+    losses = torch.empty(Lr, hkv, n_steps + 1, dtype=torch.float32, device=v.device)
+    args = make_fit_args(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, losses=losses)
+    L = lib()
+    _run(L.lowram_fit_predictor, args, L.lowram_fit_workspace_size, v.device, workspace, stream)
+    return losses

@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblowram.so")
 
 SOURCES = ["api.cpp", "decode_common.hip", "decode_generic.hip", "decode_mfma.hip", "rank.hip", "prefill_mfma.hip",
-           "xkv.hip"]
+           "xkv.hip", "fit.hip"]
 # Packed fp32 instructions are switched off for all device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-x", "hip", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

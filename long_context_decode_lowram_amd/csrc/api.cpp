@@ -195,6 +195,74 @@ int plan_xkv(const lowram_xkv_args* a, XkvPlan* pl) {
     return LOWRAM_OK;
 }
 
+struct PinvPlan { PinvParams p; size_t off[10]; size_t total; };
+
+int plan_pinv(const lowram_pinv_args* a, PinvPlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_maps < 1 || a->n_maps > 65535) return fail(LOWRAM_ERR_ARG, "n_maps (%d) must be in [1, 65535]", a->n_maps);
+    if (a->head_dim != kHeadDim) return fail(LOWRAM_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->hidden < a->head_dim || a->hidden > 65536)
+        return fail(LOWRAM_ERR_ARG, "hidden (%d) must be in [head_dim, 65536]", a->hidden);
+    PinvParams& p = pl->p;
+    p = PinvParams{};
+    p.n_maps = a->n_maps; p.hidden = a->hidden; p.d = a->head_dim;
+    int sp = (512 + a->n_maps - 1) / a->n_maps;
+    const int maxs = (a->hidden + 127) / 128;
+    p.splits = sp > maxs ? maxs : (sp < 1 ? 1 : sp);
+    const size_t P = a->n_maps, hd = (size_t)a->hidden * a->head_dim, dd = (size_t)a->head_dim * a->head_dim;
+    const size_t sz[10] = {P * hd * 8, P * hd * 8, P * dd * 8, P * dd * 8, P * dd * 8, P * dd * 8, P * dd * 8,
+                           P * p.splits * dd * 8, P * a->head_dim * 4, 0};
+    size_t off = 0;
+    for (int i = 0; i < 10; ++i) {
+        pl->off[i] = off;
+        off = up256(off + sz[i]);
+    }
+    pl->total = off;
+    return LOWRAM_OK;
+}
+
+struct FitPlan { FitParams p; size_t off[14]; size_t total; };
+
+int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_layers < 1 || a->n_kv_heads < 1 || a->ctx_len < 1)
+        return fail(LOWRAM_ERR_ARG, "n_layers, n_kv_heads and ctx_len must be >= 1");
+    if (a->head_dim != kHeadDim) return fail(LOWRAM_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", a->head_dim);
+    if (a->mlp_hidden < 128 || a->mlp_hidden % 128 != 0 || a->mlp_hidden > 1024)
+        return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 128 in [128, 1024] (got %d)", a->mlp_hidden);
+    if (a->n_steps < 0 || a->n_steps > 100000) return fail(LOWRAM_ERR_ARG, "n_steps (%d) must be in [0, 100000]", a->n_steps);
+    if (!(a->lr == a->lr) || a->lr > 3.0e38f || a->lr < -3.0e38f) return fail(LOWRAM_ERR_ARG, "lr must be finite");
+    if ((int64_t)a->ctx_len * a->n_kv_heads * a->head_dim * 2 >= (int64_t(1) << 31))
+        return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * n_kv_heads * head_dim * 2 must stay below 2^31");
+    if ((int64_t)a->n_layers * a->n_kv_heads > 65535) return fail(LOWRAM_ERR_ARG, "n_layers * n_kv_heads above 65535");
+    FitParams& p = pl->p;
+    p = FitParams{};
+    p.n_layers = a->n_layers; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads; p.hidden = a->mlp_hidden;
+    p.n_steps = a->n_steps; p.lr = a->lr;
+    p.n_probs = a->n_layers * a->n_kv_heads;
+    p.m_tiles = (a->ctx_len + 255) / 256;
+    const int tiles = p.n_probs * (a->mlp_hidden / 128);
+    int nc = (2048 + tiles - 1) / tiles;
+    const int maxc = (a->ctx_len + 31) / 32;
+    nc = nc < 1 ? 1 : (nc > 64 ? 64 : nc);
+    nc = nc > maxc ? maxc : nc;
+    p.chunk_len = ((a->ctx_len + nc - 1) / nc + 31) / 32 * 32;
+    p.n_chunks = (a->ctx_len + p.chunk_len - 1) / p.chunk_len;
+    const size_t P = p.n_probs, T = a->ctx_len, H = a->mlp_hidden, d = a->head_dim;
+    const size_t sz[14] = {P * T * H * 2, P * T * H * 2, P * T * d * 2, P * T * H * 2,        // zb hb gb dzb
+                           P * H * d * 2, P * H * d * 2, P * H * d * 2,                      // w1b w2b w2tb
+                           P * p.n_chunks * H * d * 4, P * p.n_chunks * H * d * 4,          // pw1 pw2
+                           P * p.m_tiles * d * 4, P * p.m_tiles * H * 4, P * p.m_tiles * 4,  // cs_g cs_dz loss_p
+                           0, 0};
+    size_t off = 0;
+    for (int i = 0; i < 14; ++i) {
+        pl->off[i] = off;
+        off = up256(off + sz[i]);
+    }
+    pl->total = off;
+    return LOWRAM_OK;
+}
+
 int hip_fail(hipError_t e, const char* what) {
     return fail(LOWRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -418,6 +486,78 @@ int lowram_xkv_factorize(const lowram_xkv_args* a, void* stream) {
         return hip_fail(e, "event record");
     if ((e = launch_xkv_factor(p, s)) != hipSuccess) return hip_fail(e, "xkv iteration launch");
     return LOWRAM_OK;
+}
+
+size_t lowram_pinv_workspace_size(const lowram_pinv_args* a) {
+    g_err[0] = 0;
+    PinvPlan pl;
+    return plan_pinv(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_pinv_value_map(const lowram_pinv_args* a, void* stream) {
+    g_err[0] = 0;
+    PinvPlan pl;
+    int rc = plan_pinv(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (!a->w_k || !a->w_v || !a->w_lin) return fail(LOWRAM_ERR_ARG, "w_k, w_v and w_lin must be non-NULL");
+    const void* v16[] = {a->w_k, a->w_v, a->w_lin, a->w_lin64, a->workspace};
+    for (const void* q : v16)
+        if (misaligned(q, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", q);
+    if (!a->workspace || a->workspace_bytes < pl.total)
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+    char* ws = static_cast<char*>(a->workspace);
+    PinvParams p = pl.p;
+    p.w_k = static_cast<const __bf16*>(a->w_k);
+    p.w_v = static_cast<const __bf16*>(a->w_v);
+    p.w_lin = static_cast<__bf16*>(a->w_lin);
+    p.w_lin64 = a->w_lin64;
+    auto dbl = [&](int i) { return reinterpret_cast<double*>(ws + pl.off[i]); };
+    p.wk64 = dbl(0); p.wv64 = dbl(1); p.g = dbl(2); p.bm = dbl(3); p.rinv = dbl(4); p.t1 = dbl(5); p.x = dbl(6);
+    p.g_parts = dbl(7);
+    p.dead = reinterpret_cast<int32_t*>(ws + pl.off[8]);
+    hipError_t e = launch_pinv(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWRAM_OK : hip_fail(e, "pinv launch");
+}
+
+size_t lowram_fit_workspace_size(const lowram_fit_args* a) {
+    g_err[0] = 0;
+    FitPlan pl;
+    return plan_fit(a, &pl) == LOWRAM_OK ? pl.total : 0;
+}
+
+int lowram_fit_predictor(const lowram_fit_args* a, void* stream) {
+    g_err[0] = 0;
+    FitPlan pl;
+    int rc = plan_fit(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (!a->keys || !a->v || !a->w_lin || !a->w1 || !a->b1 || !a->w2 || !a->b2)
+        return fail(LOWRAM_ERR_ARG, "keys, v, w_lin, w1, b1, w2 and b2 must be non-NULL");
+    const void* v16[] = {a->keys, a->v, a->w_lin, a->w1, a->b1, a->w2, a->b2, a->workspace};
+    for (const void* q : v16)
+        if (misaligned(q, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", q);
+    if (misaligned(a->losses, 4)) return fail(LOWRAM_ERR_ARG, "losses must be 4-byte aligned");
+    if (!a->workspace || a->workspace_bytes < pl.total)
+        return fail(LOWRAM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", pl.total, a->workspace ? a->workspace_bytes : 0);
+    char* ws = static_cast<char*>(a->workspace);
+    FitParams p = pl.p;
+    p.keys = static_cast<const __bf16*>(a->keys);
+    p.v = static_cast<const __bf16*>(a->v);
+    p.w_lin = static_cast<const __bf16*>(a->w_lin);
+    p.w1 = a->w1; p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.losses = a->losses;
+    p.zb = reinterpret_cast<__bf16*>(ws + pl.off[0]);
+    p.hb = reinterpret_cast<__bf16*>(ws + pl.off[1]);
+    p.gb = reinterpret_cast<__bf16*>(ws + pl.off[2]);
+    p.dzb = reinterpret_cast<__bf16*>(ws + pl.off[3]);
+    p.w1b = reinterpret_cast<__bf16*>(ws + pl.off[4]);
+    p.w2b = reinterpret_cast<__bf16*>(ws + pl.off[5]);
+    p.w2tb = reinterpret_cast<__bf16*>(ws + pl.off[6]);
+    p.pw1 = reinterpret_cast<float*>(ws + pl.off[7]);
+    p.pw2 = reinterpret_cast<float*>(ws + pl.off[8]);
+    p.cs_g = reinterpret_cast<float*>(ws + pl.off[9]);
+    p.cs_dz = reinterpret_cast<float*>(ws + pl.off[10]);
+    p.loss_p = reinterpret_cast<float*>(ws + pl.off[11]);
+    hipError_t e = launch_fit(p, a->ev_main_begin, a->ev_main_end, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWRAM_OK : hip_fail(e, "fit launch");
 }
 
 }  // extern "C"

@@ -78,4 +78,45 @@ size_t xkv_partials_floats(const XkvParams& p);   // per problem
 hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s);     // chunk partials of C^T C
 hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s);   // M, iterations, A and B_l
 
+// Test-time fit of the predictor's nonlinear branch by gradient descent, for
+// P = n_layers * n_kv problems (one per layer and KV head).
+struct FitParams {
+    int n_layers, ctx_len, n_kv, hidden, n_steps;
+    int n_probs;                  // n_layers * n_kv
+    int m_tiles;                  // 256-token tiles
+    int n_chunks, chunk_len;      // token chunks of the weight-gradient products
+    float lr;
+    const __bf16* keys;           // [L, T, Hkv*d]
+    const __bf16* v;              // [L, T, Hkv, d]
+    const __bf16* w_lin;          // [L, Hkv, d, d]
+    float* w1; float* b1; float* w2; float* b2;   // [P, h, d], [P, h], [P, d, h], [P, d]
+    float* losses;                // [P, n_steps + 1] or null
+    // workspace, per problem
+    __bf16* zb;                   // [P, T, h]  pre-activations
+    __bf16* hb;                   // [P, T, h]  gelu of them
+    __bf16* gb;                   // [P, T, d]  (2 / T)(v_hat - v)
+    __bf16* dzb;                  // [P, T, h]  gradient at the pre-activations
+    __bf16* w1b; __bf16* w2b; __bf16* w2tb;       // bf16 copies: [P, h, d], [P, d, h], [P, h, d]
+    float* pw1;                   // [P, n_chunks, d, h]  partial dW1, stored [i][u]
+    float* pw2;                   // [P, n_chunks, h, d]  partial dW2, stored [u][o]
+    float* cs_g;                  // [P, m_tiles, d]      column sums of g
+    float* cs_dz;                 // [P, m_tiles, h]      column sums of dz
+    float* loss_p;                // [P, m_tiles]         sums of squared errors
+};
+hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s);
+
+// W_lin = pinv(W_K) W_V per problem, from bf16 projections (binary64 inside).
+struct PinvParams {
+    int n_maps, hidden, d;
+    const __bf16* w_k; const __bf16* w_v;   // [P, hidden, d]
+    __bf16* w_lin;                          // [P, d, d] output-major
+    double* w_lin64;                        // [P, d, d] output-major, or null
+    double* wk64; double* wv64;             // [P, hidden, d]
+    double* g; double* bm; double* rinv; double* t1; double* x;   // [P, d, d]
+    double* g_parts;                        // [P, splits, d, d]
+    int32_t* dead;                          // [P, d]
+    int splits;
+};
+hipError_t launch_pinv(const PinvParams& p, hipStream_t s);
+
 }  // namespace lowram

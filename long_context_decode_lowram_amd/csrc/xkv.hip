@@ -684,4 +684,65 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------- pseudoinverse start
+// explainer, Slim Attention paragraph: the predictor's linear map starts at
+// the best linear guess the projections allow, W_lin = pinv(W_K) W_V (row
+// vectors: k = x W_K, v = x W_V). For W_K of full column rank,
+// pinv(W_K) = (W_K^T W_K)^-1 W_K^T, so with G = W_K^T W_K = L L^T and
+// B = W_K^T W_V: W_lin = L^-T (L^-T)^T B, in binary64 on the same products,
+// Cholesky and triangular solve as the factorisation above.
+__global__ __launch_bounds__(256) void xkv_cvt_kernel(const __bf16* src, double* dst, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[i]);
+}
+
+// w_lin[q][o][i] = W_lin[i][o] (output-major), bf16 by one rounding, and binary64.
+__global__ __launch_bounds__(256) void pinv_out_kernel(PinvParams p) {
+    const int q = blockIdx.y;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.d * p.d) return;
+    const int o = e / p.d, i = e - o * p.d;
+    const double v = p.x[((int64_t)q * p.d + i) * p.d + o];
+    reinterpret_cast<uint16_t*>(p.w_lin)[(int64_t)q * p.d * p.d + e] = f64_to_bf16_bits(v);
+    if (p.w_lin64) p.w_lin64[(int64_t)q * p.d * p.d + e] = v;
+}
+
+hipError_t launch_pinv(const PinvParams& p, hipStream_t s) {
+    const int d = p.d, P = p.n_maps;
+    const int64_t hd = (int64_t)p.hidden * d, dd = (int64_t)d * d;
+    const int64_t nel = hd * P;
+    hipLaunchKernelGGL(xkv_cvt_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s, p.w_k, p.wk64, nel);
+    hipLaunchKernelGGL(xkv_cvt_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, s, p.w_v, p.wv64, nel);
+    auto gram = [&](const double* b, double* out) {     // out = W_K^T b over the hidden axis, split
+        GemmArgs g{};
+        g.m = d; g.n = d; g.k = p.hidden; g.kc = (p.hidden + p.splits - 1) / p.splits; g.splits = p.splits;
+        g.A = p.wk64; g.lda = d; g.sA = hd;
+        g.B = b; g.ldb = d; g.sB = hd;
+        g.C = p.g_parts; g.ldc = d; g.sC = dd * p.splits; g.c_split = dd;
+        const dim3 grid((unsigned)((d + kGm - 1) / kGm), (unsigned)((d + kGm - 1) / kGm), (unsigned)(P * p.splits));
+        hipLaunchKernelGGL((xkv_gemm_f64_kernel<true, false>), grid, dim3(256), 0, s, g);
+        hipLaunchKernelGGL(xkv_sum_splits_kernel, dim3((unsigned)((dd + 255) / 256), (unsigned)P), dim3(256), 0, s,
+                           p.g_parts, out, dd, p.splits);
+    };
+    gram(p.wk64, p.g);
+    gram(p.wv64, p.bm);
+    hipLaunchKernelGGL(xkv_chol_kernel, dim3((unsigned)P), dim3(1024), 0, s, p.g, d, p.dead);
+    hipLaunchKernelGGL(xkv_trsm_kernel, dim3((unsigned)((d + kTrRows - 1) / kTrRows), (unsigned)P), dim3(256), 0, s,
+                       (const double*)nullptr, p.rinv, p.g, p.dead, d, d);
+    auto small = [&](bool ta, const double* a, const double* b, double* out) {
+        GemmArgs g{};
+        g.m = d; g.n = d; g.k = d; g.kc = d; g.splits = 1;
+        g.A = a; g.lda = d; g.sA = dd;
+        g.B = b; g.ldb = d; g.sB = dd;
+        g.C = out; g.ldc = d; g.sC = dd; g.c_split = 0;
+        const dim3 grid((unsigned)((d + kGm - 1) / kGm), (unsigned)((d + kGm - 1) / kGm), (unsigned)P);
+        if (ta) hipLaunchKernelGGL((xkv_gemm_f64_kernel<true, false>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((xkv_gemm_f64_kernel<false, false>), grid, dim3(256), 0, s, g);
+    };
+    small(true, p.rinv, p.bm, p.t1);      // (L^-T)^T B
+    small(false, p.rinv, p.t1, p.x);      // L^-T ((L^-T)^T B)
+    hipLaunchKernelGGL(pinv_out_kernel, dim3((unsigned)((dd + 255) / 256), (unsigned)P), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace lowram

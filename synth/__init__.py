@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "PrefillConfig", "PREFILL_CONFIGS",
            "make_generator", "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
-           "gen_prefill_inputs", "block_ptr_from_idx", "XkvConfig", "XKV_CONFIGS", "gen_xkv_inputs"]
+           "gen_prefill_inputs", "block_ptr_from_idx", "XkvConfig", "XKV_CONFIGS", "gen_xkv_inputs",
+           "FitConfig", "FIT_CONFIGS", "gen_fit_inputs", "gen_pinv_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -392,3 +393,62 @@ def gen_xkv_inputs(xc, device, batch=None):
     g = make_generator(device, xc.seed, "xkv-omega", xc.name)
     omega = torch.randn(xc.n, xc.rank, generator=g, device=device, dtype=torch.float64)
     return {"keys": keys, "omega": omega}
+
+
+@dataclasses.dataclass(frozen=True)
+class FitConfig:
+    """The predictor fit: L layers x Hkv heads of T tokens, hidden width h,
+    n_steps of gradient descent at rate lr."""
+    name: str
+    n_layers: int
+    ctx_len: int
+    n_kv_heads: int
+    hidden: int
+    n_steps: int
+    lr: float = 0.05
+    head_dim: int = 128
+    seed: int = 8
+
+
+FIT_CONFIGS = {c.name: c for c in (
+    FitConfig("f_small_ragged", 2, 1000, 2, 128, 3),
+    FitConfig("f_mid", 2, 8192, 8, 256, 2, lr=0.02),
+    # a 32-layer Llama-3.1-8B prefill at 131072 tokens, h = 256, the quick two-step fit
+    FitConfig("f_llama_131k", 32, 131072, 8, 256, 2, lr=0.02),
+)}
+
+
+def gen_fit_inputs(fc, device):
+    """keys [L, T, Hkv*d] bf16 standard normal; w_lin [L, Hkv, d, d] bf16
+    N(0, 1/sqrt(d)); true values v = k W_lin + gelu(k A) B + N(0, 0.05) with a
+    hidden branch A [d, h] ~ N(0, 1/sqrt(d)), B [h, d] ~ N(0, 1/sqrt(h)) per
+    head, so there is a nonlinear part to learn; the branch to fit starts at
+    w1 ~ N(0, 1/sqrt(d)), b1 = 0, w2 = 0, b2 = 0 (float32), so the predictor
+    starts at the linear map."""
+    g = make_generator(device, fc.seed, "fit", fc.name)
+    L, T, hkv, d, h = fc.n_layers, fc.ctx_len, fc.n_kv_heads, fc.head_dim, fc.hidden
+    keys = torch.empty(L, T, hkv * d, dtype=torch.bfloat16, device=device)
+    v = torch.empty(L, T, hkv, d, dtype=torch.bfloat16, device=device)
+    w_lin = (torch.randn(L, hkv, d, d, generator=g, device=device) / math.sqrt(d)).to(torch.bfloat16)
+    for l in range(L):
+        k = torch.randn(T, hkv * d, generator=g, device=device).to(torch.bfloat16)
+        keys[l] = k
+        kf = k.float().view(T, hkv, d)
+        for hh in range(hkv):
+            a = torch.randn(d, h, generator=g, device=device) / math.sqrt(d)
+            b = torch.randn(h, d, generator=g, device=device) / math.sqrt(h)
+            x = kf[:, hh, :].contiguous()
+            out = x @ w_lin[l, hh].float().t().contiguous() + torch.nn.functional.gelu(x @ a) @ b
+            out += 0.05 * torch.randn(T, d, generator=g, device=device)
+            v[l, :, hh, :] = out.to(torch.bfloat16)
+    w1 = torch.randn(L, hkv, h, d, generator=g, device=device) / math.sqrt(d)
+    return {"keys": keys, "v": v, "w_lin": w_lin, "w1": w1, "b1": torch.zeros(L, hkv, h, device=device),
+            "w2": torch.zeros(L, hkv, d, h, device=device), "b2": torch.zeros(L, hkv, d, device=device)}
+
+
+def gen_pinv_inputs(n_maps, hidden, device, seed=9, d=128):
+    """W_K, W_V [P, hidden, d] bf16 with N(0, 1/sqrt(hidden)) entries."""
+    g = make_generator(device, seed, "pinv", n_maps, hidden)
+    w_k = (torch.randn(n_maps, hidden, d, generator=g, device=device) / math.sqrt(hidden)).to(torch.bfloat16)
+    w_v = (torch.randn(n_maps, hidden, d, generator=g, device=device) / math.sqrt(hidden)).to(torch.bfloat16)
+    return w_k, w_v

@@ -258,3 +258,58 @@ def test_xkv_rank_above_width_rejected():
     a = valid_xkv()
     a.n_layers, a.width, a.rank = 1, 256, 320
     assert call_xkv(a) == B.ERR_UNSUPPORTED
+
+
+# ------------------------------------------------- pseudoinverse and fit
+def valid_pinv():
+    a = B.PinvArgs()
+    a.n_maps, a.hidden, a.head_dim = 4, 4096, 128
+    for n in ("w_k", "w_v", "w_lin"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def valid_fit():
+    a = B.FitArgs()
+    a.n_layers, a.ctx_len, a.n_kv_heads, a.head_dim, a.mlp_hidden, a.n_steps, a.lr = 2, 1000, 8, 128, 256, 2, 0.05
+    for n in ("keys", "v", "w_lin", "w1", "b1", "w2", "b2"):
+        setattr(a, n, FAKE)
+    return a
+
+
+def test_pinv_and_fit_layouts_and_workspace():
+    text = open(HEADER).read()
+    for struct, cls in (("lowram_pinv_args", B.PinvArgs), ("lowram_fit_args", B.FitArgs)):
+        body = text[text.index(f"typedef struct {struct}"):text.index(f"}} {struct};")]
+        fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+        assert fields == [f[0] for f in cls._fields_]
+    a = valid_pinv()
+    assert L.lib().lowram_pinv_workspace_size(ctypes.byref(a)) >= 2 * 4 * 4096 * 128 * 8
+    assert L.lib().lowram_pinv_value_map(ctypes.byref(a), None) == B.ERR_WORKSPACE
+    f = valid_fit()
+    assert L.lib().lowram_fit_workspace_size(ctypes.byref(f)) >= 3 * 16 * 1000 * 256 * 2
+    assert L.lib().lowram_fit_predictor(ctypes.byref(f), None) == B.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("w_k", None, B.ERR_ARG), ("w_lin", None, B.ERR_ARG), ("n_maps", 0, B.ERR_ARG),
+    ("head_dim", 64, B.ERR_UNSUPPORTED), ("hidden", 100, B.ERR_ARG), ("w_lin64", FAKE + 8, B.ERR_ARG),
+])
+def test_pinv_rejects(field, value, status):
+    a = valid_pinv()
+    setattr(a, field, value)
+    assert L.lib().lowram_pinv_value_map(ctypes.byref(a), None) == status
+    assert L.last_error() != ""
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("keys", None, B.ERR_ARG), ("b2", None, B.ERR_ARG), ("n_layers", 0, B.ERR_ARG), ("ctx_len", 0, B.ERR_ARG),
+    ("head_dim", 64, B.ERR_UNSUPPORTED), ("mlp_hidden", 192, B.ERR_UNSUPPORTED), ("mlp_hidden", 2048, B.ERR_UNSUPPORTED),
+    ("n_steps", -1, B.ERR_ARG), ("lr", float("nan"), B.ERR_ARG), ("lr", float("inf"), B.ERR_ARG),
+    ("ctx_len", 1 << 21, B.ERR_UNSUPPORTED), ("losses", FAKE + 2, B.ERR_ARG),
+])
+def test_fit_rejects(field, value, status):
+    a = valid_fit()
+    setattr(a, field, value)
+    assert L.lib().lowram_fit_predictor(ctypes.byref(a), None) == status
+    assert L.last_error() != ""
