@@ -240,7 +240,7 @@ int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
     p.n_layers = a->n_layers; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads; p.hidden = a->mlp_hidden;
     p.n_steps = a->n_steps; p.lr = a->lr;
     p.n_probs = a->n_layers * a->n_kv_heads;
-    p.m_tiles = (a->ctx_len + 255) / 256;
+    p.m_tiles = (a->ctx_len + 127) / 128;
     const int tiles = p.n_probs * (a->mlp_hidden / 128);
     int nc = (2048 + tiles - 1) / tiles;
     const int maxc = (a->ctx_len + 31) / 32;
@@ -249,7 +249,7 @@ int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
     p.chunk_len = ((a->ctx_len + nc - 1) / nc + 31) / 32 * 32;
     p.n_chunks = (a->ctx_len + p.chunk_len - 1) / p.chunk_len;
     const size_t P = p.n_probs, T = a->ctx_len, H = a->mlp_hidden, d = a->head_dim;
-    const size_t sz[14] = {P * T * H * 2, P * T * H * 2, P * T * d * 2, P * T * H * 2,        // zb hb gb dzb
+    const size_t sz[14] = {0, P * T * H * 2, P * T * d * 2, P * T * H * 2,                    // (unused) hb gb dzb
                            P * H * d * 2, P * H * d * 2, P * H * d * 2,                      // w1b w2b w2tb
                            P * p.n_chunks * H * d * 4, P * p.n_chunks * H * d * 4,          // pw1 pw2
                            P * p.m_tiles * d * 4, P * p.m_tiles * H * 4, P * p.m_tiles * 4,  // cs_g cs_dz loss_p
@@ -544,7 +544,6 @@ int lowram_fit_predictor(const lowram_fit_args* a, void* stream) {
     p.v = static_cast<const __bf16*>(a->v);
     p.w_lin = static_cast<const __bf16*>(a->w_lin);
     p.w1 = a->w1; p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.losses = a->losses;
-    p.zb = reinterpret_cast<__bf16*>(ws + pl.off[0]);
     p.hb = reinterpret_cast<__bf16*>(ws + pl.off[1]);
     p.gb = reinterpret_cast<__bf16*>(ws + pl.off[2]);
     p.dzb = reinterpret_cast<__bf16*>(ws + pl.off[3]);

@@ -6,9 +6,10 @@
 // per context at prefill. Loss L = (1 / T) sum_t ||v_hat_t - v_t||^2, plain
 // gradient descent on W1, b1, W2, b2 (W_lin fixed). Per step and problem
 // (layer, KV head), with weights stored output-major:
-//   Z = K W1^T + b1, H = gelu(Z)                       fit_nt_kernel<kEpiZ>
+//   H = gelu(K W1^T + b1)                              fit_nt_kernel<kEpiZ>
 //   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           fit_nt_kernel<kEpiG>   (+ loss, sum_t G)
-//   dZ = (G W2) * gelu'(Z)                             fit_nt_kernel<kEpiDz>  (+ sum_t dZ)
+//   dZ = (G W2) * gelu'(K W1^T + b1)                   fit_nt_kernel<kEpiDz>  (+ sum_t dZ; the
+//                                                      pre-activations are recomputed, not stored)
 //   dW2 = G^T H, dW1 = dZ^T K                          fit_tn_kernel (token chunks)
 //   theta -= lr dL/dtheta                              fit_update_kernel
 // Products on bf16 MFMA with fp32 sums; the parameters are fp32 masters with
@@ -22,12 +23,12 @@
 
 namespace lowram {
 
-constexpr int kFM = 256;                 // tokens per tile (MFMA B operand rows)
+constexpr int kFM = 128;                 // tokens per tile (MFMA B operand rows)
 constexpr int kFN = 128;                 // outputs per tile (MFMA A operand rows)
 constexpr int kFK = 64;                  // contraction step
 constexpr int kFRowB = kFK * 2;          // 128-byte LDS rows
 constexpr int kFOp0 = kFN * kFRowB;      // 16 KB
-constexpr int kFStage = (kFN + kFM) * kFRowB;   // 48 KB
+constexpr int kFStage = (kFN + kFM) * kFRowB;   // 32 KB
 constexpr int kFThreads = 512;
 enum : int { kEpiZ = 0, kEpiG = 1, kEpiDz = 2 };
 
@@ -35,9 +36,17 @@ __device__ __forceinline__ uint32_t fslot(int row, int piece) {
     return (uint32_t)(row * kFRowB + ((piece ^ (row & 7)) << 4));
 }
 
-__device__ __forceinline__ float gelu_f(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// GELU and its derivative from the normal tail fit (normal_tail): with
+// a = |z|, gelu(z) = max(z, 0) - a Q(a) and gelu'(z) = Phi(z) + z phi(z),
+// Phi(z) = 1 - Q(a) for z >= 0, Q(a) below; phi(z) = 2^(-z^2 / (2 ln 2)) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_f(float z) {
+    const float a = fabsf(z);
+    return fmaxf(z, 0.0f) - a * normal_tail(a);
+}
 __device__ __forceinline__ float gelu_grad_f(float z) {
-    return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
+    const float q = normal_tail(fabsf(z));
+    const float phi = __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z) * 0.39894228040143268f;
+    return (z >= 0.0f ? 1.0f - q : q) + z * phi;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -54,13 +63,13 @@ struct NtSeg {
     int kdim;
 };
 
-// NT product over up to two segments for a 256-token x 128-output tile of
-// problem blockIdx.y, then the fused epilogue. Grid (m_tiles * n_tiles, P).
-// Eight waves: wave w covers outputs 64 (w & 1) .. and tokens 64 (w >> 1) ..;
-// lane (l16, g4) ends with outputs n .. n + 3 (n = 4 g4 + 16 nt) of token l16
-// + 16 tt of its block.
+// NT product over up to two segments for a 128-token x 128-output tile of
+// problem blockIdx.y, then the fused epilogue. Grid (m_tiles * n_tiles, P);
+// 64 KB of LDS, so two workgroups share a CU. Eight waves: wave w covers
+// outputs 64 (w & 1) .. and tokens 32 (w >> 1) ..; lane (l16, g4) ends with
+// outputs n .. n + 3 (n = 4 g4 + 16 nt) of token l16 + 16 tt of its block.
 template <int EPI>
-__global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
+__global__ __launch_bounds__(kFThreads, 2) void fit_nt_kernel(FitParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char st0[kFStage];
     __shared__ __attribute__((aligned(16))) unsigned char st1[kFStage];
     __shared__ float red_cs[4][256];
@@ -71,16 +80,24 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
     const int d = kHeadDim, H = p.hidden, T = p.ctx_len;
     const int N = EPI == kEpiG ? d : H;
     const int n_tiles = N / kFN;
-    const int mt = blockIdx.x / n_tiles, ntile = blockIdx.x - mt * n_tiles;
+    // The output tiles of one token tile sit 8 blocks apart, so that they run
+    // on the same XCD (blocks go round-robin over the 8) and share its L2
+    // copy of the token rows. Blocks past the last token tile exit.
+    const int grp = blockIdx.x / (8 * n_tiles), rem = blockIdx.x - grp * 8 * n_tiles;
+    const int ntile = rem >> 3, mt = grp * 8 + (rem & 7);
+    if (mt >= p.m_tiles) return;
     const int t0 = mt * kFM, n0 = ntile * kFN;
     const int ldkv = p.n_kv * d;
     const __bf16* kq = p.keys + (int64_t)l * T * ldkv + h * d;
     const int64_t th = (int64_t)q * T * H, td = (int64_t)q * T * d;
 
+    // Segments of the contraction; EPI_G sums two into one accumulator,
+    // EPI_DZ runs two separate products (pre-activations, then G W2).
     NtSeg seg[2];
     int n_seg = 1;
+    const NtSeg zseg = NtSeg{kq, ldkv, p.w1b + (int64_t)q * H * d, d, d};
     if (EPI == kEpiZ) {
-        seg[0] = NtSeg{kq, ldkv, p.w1b + (int64_t)q * H * d, d, d};
+        seg[0] = zseg;
     } else if (EPI == kEpiG) {
         seg[0] = NtSeg{kq, ldkv, p.w_lin + (int64_t)q * d * d, d, d};
         seg[1] = NtSeg{p.hb + th, H, p.w2b + (int64_t)q * d * H, H, H};
@@ -88,18 +105,16 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
     } else {
         seg[0] = NtSeg{p.gb + td, d, p.w2tb + (int64_t)q * H * d, d, d};
     }
-    const int steps0 = seg[0].kdim / kFK;
-    const int n_steps = steps0 + (n_seg == 2 ? seg[1].kdim / kFK : 0);
 
-    // Direct copies: op0 (128 output rows) by waves' 2 copies each, op1 (256
-    // token rows, zeros past T) by 4 each; lane i lands in row 8 c + i / 8,
+    // Direct copies: op0 (128 output rows) and op1 (128 token rows, zeros
+    // past T) by 2 copies per wave each; lane i lands in row 8 c + i / 8,
     // slot i % 8, and fetches piece (i % 8) ^ (row % 8).
     const int dma_row = lane >> 3;
     const uint32_t dma_piece = (uint32_t)(((lane & 7) ^ dma_row) * 16);
-    auto dma = [&](int s, unsigned char* stage) {
+    auto dma = [&](const NtSeg* sgs, int steps0, int s, unsigned char* stage) {
         const int sg = s < steps0 ? 0 : 1;
         const int k0 = (s - (sg ? steps0 : 0)) * kFK;
-        const NtSeg& g = seg[sg];
+        const NtSeg& g = sgs[sg];
         const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(g.b + (int64_t)n0 * g.ldb, (uint32_t)(kFN * g.ldb * 2));
         const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.a + (int64_t)t0 * g.lda,
                                                       (uint32_t)((int64_t)max(0, T - t0) * g.lda * 2));
@@ -109,45 +124,56 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
             dma16(rb, stage + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * g.ldb + k0) * 2) + dma_piece, 0u);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int r0 = (w * 4 + c) * 8;
+        for (int c = 0; c < 2; ++c) {
+            const int r0 = (w * 2 + c) * 8;
             dma16(ra, stage + kFOp0 + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * g.lda + k0) * 2) + dma_piece, 0u);
         }
     };
 
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int wn = (w & 1) * 64, wt = (w >> 1) * 64;
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto mma = [&](const unsigned char* stage) {
+    const int wn = (w & 1) * 64, wt = (w >> 1) * 32;
+    auto mma = [&](const unsigned char* stage, f32x4 (&acc)[4][2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 af[4], bf[4];
+            bf16x8 af[4], bf[2];
 #pragma unroll
             for (int a = 0; a < 4; ++a) af[a] = lds16(stage, fslot(wn + a * 16 + l16, ks * 4 + g4));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bf[b] = lds16(stage + kFOp0, fslot(wt + b * 16 + l16, ks * 4 + g4));
+            for (int b = 0; b < 2; ++b) bf[b] = lds16(stage + kFOp0, fslot(wt + b * 16 + l16, ks * 4 + g4));
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = mfma(af[a], bf[b], acc[a][b]);
+                for (int b = 0; b < 2; ++b) acc[a][b] = mfma(af[a], bf[b], acc[a][b]);
         }
     };
-    dma(0, st0);
-    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+    // acc = sum over the segments' contraction, copies one 64-wide step ahead
+    // into two static stage buffers.
+    auto contract = [&](const NtSeg* sgs, int ns, f32x4 (&acc)[4][2]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int steps0 = sgs[0].kdim / kFK;
+        const int n_steps = steps0 + (ns == 2 ? sgs[1].kdim / kFK : 0);
+        dma(sgs, steps0, 0, st0);
+        auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+            wait_vmcnt<0>();
+            barrier_lds();
+            if (s + 1 < n_steps) dma(sgs, steps0, s + 1, nxt);
+            mma(cur, acc);
+        };
+        for (int s = 0; s < n_steps; s += 2) {
+            step(s, st0, st1);
+            if (s + 1 < n_steps) step(s + 1, st1, st0);
+        }
         wait_vmcnt<0>();
-        barrier_lds();
-        if (s + 1 < n_steps) dma(s + 1, nxt);
-        mma(cur);
     };
-    for (int s = 0; s < n_steps; s += 2) {
-        step(s, st0, st1);
-        if (s + 1 < n_steps) step(s + 1, st1, st0);
+    f32x4 acc[4][2], accz[4][2];
+    if (EPI == kEpiDz) {
+        contract(&zseg, 1, accz);
+        barrier_lds();       // every wave is done with the stage buffers
     }
-    wait_vmcnt<0>();
+    contract(seg, n_seg, acc);
 
     // Epilogue.
     float cs[4][4];
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
     float loss = 0.f;
     const float gscale = 2.0f / (float)T;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < 2; ++b) {
         const int t = t0 + wt + b * 16 + l16;
         if (t >= T) continue;
 #pragma unroll
@@ -167,16 +193,11 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
             const f32x4 x = acc[a][b];
             if (EPI == kEpiZ) {
                 const float* bb = p.b1 + (int64_t)q * H + n;
-                float z[4];
+                float hv[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) z[v] = x[v] + bb[v];
-                const uint32_t zw0 = pack_bf16x2(z[0], z[1]), zw1 = pack_bf16x2(z[2], z[3]);
-                *reinterpret_cast<u32x2*>(p.zb + th + (int64_t)t * H + n) = u32x2{zw0, zw1};
-                // gelu of the stored (rounded) pre-activation, the value the
-                // backward pass differentiates at
+                for (int v = 0; v < 4; ++v) hv[v] = gelu_f(x[v] + bb[v]);
                 *reinterpret_cast<u32x2*>(p.hb + th + (int64_t)t * H + n) =
-                    u32x2{pack_bf16x2(gelu_f(bf16_lo(zw0)), gelu_f(bf16_hi(zw0))),
-                          pack_bf16x2(gelu_f(bf16_lo(zw1)), gelu_f(bf16_hi(zw1)))};
+                    u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
             } else if (EPI == kEpiG) {
                 const float* bb = p.b2 + (int64_t)q * d + n;
                 const u32x2 vv = *reinterpret_cast<const u32x2*>(p.v + ((int64_t)l * T + t) * ldkv + h * d + n);
@@ -191,12 +212,12 @@ __global__ __launch_bounds__(kFThreads, 1) void fit_nt_kernel(FitParams p) {
                 }
                 *reinterpret_cast<u32x2*>(p.gb + td + (int64_t)t * d + n) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
             } else {
-                const u32x2 zz = *reinterpret_cast<const u32x2*>(p.zb + th + (int64_t)t * H + n);
-                const float zv[4] = {bf16_lo(zz[0]), bf16_hi(zz[0]), bf16_lo(zz[1]), bf16_hi(zz[1])};
+                const float* bb = p.b1 + (int64_t)q * H + n;
+                const f32x4 zx = accz[a][b];
                 float dz[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    dz[v] = x[v] * gelu_grad_f(zv[v]);
+                    dz[v] = x[v] * gelu_grad_f(zx[v] + bb[v]);
                     cs[a][v] += dz[v];
                 }
                 *reinterpret_cast<u32x2*>(p.dzb + th + (int64_t)t * H + n) = u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
@@ -425,7 +446,8 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
 
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s) {
     const unsigned P = (unsigned)p.n_probs;
-    const dim3 gz((unsigned)(p.m_tiles * (p.hidden / kFN)), P), gg((unsigned)p.m_tiles, P);
+    const unsigned mt8 = (unsigned)((p.m_tiles + 7) / 8 * 8);
+    const dim3 gz(mt8 * (unsigned)(p.hidden / kFN), P), gg(mt8, P);
     const dim3 t2((unsigned)(p.n_chunks * (kHeadDim / 128) * (p.hidden / 128)), P);
     hipError_t e;
     hipLaunchKernelGGL(fit_update_kernel, dim3(P), dim3(256), 0, s, p, 0, 2);

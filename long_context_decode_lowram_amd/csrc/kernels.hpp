@@ -83,7 +83,7 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s);   // M, iterati
 struct FitParams {
     int n_layers, ctx_len, n_kv, hidden, n_steps;
     int n_probs;                  // n_layers * n_kv
-    int m_tiles;                  // 256-token tiles
+    int m_tiles;                  // 128-token tiles
     int n_chunks, chunk_len;      // token chunks of the weight-gradient products
     float lr;
     const __bf16* keys;           // [L, T, Hkv*d]
@@ -92,8 +92,7 @@ struct FitParams {
     float* w1; float* b1; float* w2; float* b2;   // [P, h, d], [P, h], [P, d, h], [P, d]
     float* losses;                // [P, n_steps + 1] or null
     // workspace, per problem
-    __bf16* zb;                   // [P, T, h]  pre-activations
-    __bf16* hb;                   // [P, T, h]  gelu of them
+    __bf16* hb;                   // [P, T, h]  gelu(K W1^T + b1)
     __bf16* gb;                   // [P, T, d]  (2 / T)(v_hat - v)
     __bf16* dzb;                  // [P, T, h]  gradient at the pre-activations
     __bf16* w1b; __bf16* w2b; __bf16* w2tb;       // bf16 copies: [P, h, d], [P, d, h], [P, h, d]

@@ -62,6 +62,19 @@ __device__ __forceinline__ bf16x8 lds16(const void* base, uint32_t off) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(base) + off));
 }
 
+// The normal tail Q(a) = 1 - Phi(a) for a in [0, 6] (clamped), the fit that
+// gelu_tail16 below uses: log2 Q(a) is a degree-4 polynomial in a.
+__device__ __forceinline__ float normal_tail(float a) {
+    constexpr float c0 = -1.0004796981811523f, c1 = -1.1473716497421265f, c2 = -0.4680161774158478f,
+                    c3 = -0.04407823458313942f, c4 = 0.003866035956889391f;
+    a = __builtin_amdgcn_fmed3f(a, 0.0f, 6.0f);
+    float p = fmaf(c4, a, c3);
+    p = fmaf(p, a, c2);
+    p = fmaf(p, a, c1);
+    p = fmaf(p, a, c0);
+    return __builtin_amdgcn_exp2f(p);
+}
+
 // GELU(x) = x Phi(x) = max(x, 0) - |x| Q(|x|) with the normal tail
 // Q(a) = 1 - Phi(a). log2 Q on [0, 6] is a degree-4 polynomial in a (a
 // weighted near-minimax fit; gelu_tail_fit.py derives the constants and

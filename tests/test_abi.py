@@ -287,7 +287,7 @@ def test_pinv_and_fit_layouts_and_workspace():
     assert L.lib().lowram_pinv_workspace_size(ctypes.byref(a)) >= 2 * 4 * 4096 * 128 * 8
     assert L.lib().lowram_pinv_value_map(ctypes.byref(a), None) == B.ERR_WORKSPACE
     f = valid_fit()
-    assert L.lib().lowram_fit_workspace_size(ctypes.byref(f)) >= 3 * 16 * 1000 * 256 * 2
+    assert L.lib().lowram_fit_workspace_size(ctypes.byref(f)) >= 2 * 16 * 1000 * 256 * 2
     assert L.lib().lowram_fit_predictor(ctypes.byref(f), None) == B.ERR_WORKSPACE
 
 
