@@ -62,3 +62,86 @@ def test_c1_rank_then_decode_four_layers():
         err = rel_err(out.cpu().numpy(), ref)
         print(f"layer {layer}: rel_err={err:.2e}", flush=True)
         assert err <= 1e-4
+
+
+def _exact_attention(q, keys, vals, group):
+    """Plain softmax attention in float64: q [Hq, d], keys/vals [T, Hkv, d]."""
+    out = np.zeros_like(q)
+    for j in range(q.shape[0]):
+        k = keys[:, j // group]
+        s = k @ q[j] / np.sqrt(q.shape[1])
+        p = np.exp(s - s.max())
+        out[j] = (p / p.sum()) @ vals[:, j // group]
+    return out
+
+
+def test_compress_fit_rank_decode_whole_method():
+    """The whole method through the library, on keys and values projected from
+    a hidden state with a decaying spectrum (two layers of one group, 2 KV
+    heads, 8 query heads, T = 2048): cross-layer key factors, pseudoinverse
+    start, 20 fit steps (rate 0.02) on the rebuilt keys, fused prefill ranking with 2-bit
+    residuals, decode. The decode output matches the oracle on the factors and
+    store the library produced, the fit lowers the loss, and the residuals
+    bring the output closer to exact attention over the true keys and values."""
+    import long_context_decode_lowram_amd as L
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(11)
+    T, Dm, hkv, d, hq, G, r, hid, k_res = 2048, 512, 2, 128, 8, 2, 128, 128, 256
+    s = torch.exp(-torch.arange(Dm, device=dev, dtype=torch.float32) / 40.0) + 0.05
+    x = torch.randn(T, Dm, generator=g, device=dev) * s
+    x = x / x.pow(2).mean().sqrt()
+    w_k = torch.randn(G, Dm, hkv * d, generator=g, device=dev) / np.sqrt(Dm)
+    w_v = torch.randn(G, Dm, hkv * d, generator=g, device=dev) / np.sqrt(Dm)
+    keys = torch.stack([(x @ w_k[l]) for l in range(G)]).to(torch.bfloat16)            # [G, T, Hkv*d]
+    vals = torch.stack([(x @ w_v[l]) for l in range(G)]).to(torch.bfloat16).view(G, T, hkv, d)
+
+    # 1. cross-layer key factors
+    omega = torch.randn(G * hkv * d, r, generator=g, device=dev, dtype=torch.float64)
+    xf = L.xkv_factorize(keys.contiguous(), omega, 3)
+    a, b_l = xf["a"], xf["b_l"].view(G, hkv * d, r)
+    # 2. pseudoinverse start per (layer, head)
+    wk_h = torch.stack([w_k[l][:, h * d:(h + 1) * d] for l in range(G) for h in range(hkv)]).to(torch.bfloat16)
+    wv_h = torch.stack([w_v[l][:, h * d:(h + 1) * d] for l in range(G) for h in range(hkv)]).to(torch.bfloat16)
+    w_lin, _ = L.pinv_value_map(wk_h.contiguous(), wv_h.contiguous())
+    w_lin = w_lin.view(G, hkv, d, d)
+    # 3. fit on the rebuilt keys
+    k_rec = torch.stack([(a.float() @ b_l[l].float().t().contiguous()) for l in range(G)]).to(torch.bfloat16)
+    w1 = (torch.randn(G, hkv, hid, d, generator=g, device=dev) / np.sqrt(d)).contiguous()
+    b1 = torch.zeros(G, hkv, hid, device=dev)
+    w2 = torch.zeros(G, hkv, d, hid, device=dev)
+    b2 = torch.zeros(G, hkv, d, device=dev)
+    losses = L.fit_predictor(k_rec.contiguous(), vals.contiguous(), w_lin.contiguous(), w1, b1, w2, b2, 20, 0.02)
+    torch.cuda.synchronize()
+    assert bool((losses[..., -1] < losses[..., 0]).all()), losses
+    bf = lambda t: t.to(torch.bfloat16).contiguous()  # noqa: E731
+    # 4. fused prefill ranking, 2-bit residuals
+    pr = L.prefill_rank(a[None].contiguous(), b_l.contiguous(), w_lin.contiguous(), bf(w1), bf(w2), vals.contiguous(),
+                        k_res, "i2", group=G, b1=bf(b1), b2=bf(b2))
+    torch.cuda.synchronize()
+    # 5. decode one query per layer, with and without the residuals
+    q = torch.randn(1, hq, d, generator=g, device=dev).to(torch.bfloat16)
+    for l in range(G):
+        args = (q, a[None].contiguous(), b_l[l][None].contiguous(), w_lin[l][None].contiguous(), bf(w1[l][None]),
+                bf(w2[l][None]))
+        kw = dict(b1=bf(b1[l][None]), b2=bf(b2[l][None]))
+        out = L.decode_step(*args, pr["idx"][l][None].contiguous(), pr["val"][l][None].contiguous(),
+                            pr["ptr"][l][None].contiguous(), res_scale=pr["scale"][l][None].contiguous(), **kw)
+        nb = -(-T // 64)
+        empty_idx = torch.zeros(1, hkv, 0, dtype=torch.int32, device=dev)
+        out0 = L.decode_step(*args, empty_idx, torch.zeros(1, hkv, 0, d // 4, dtype=torch.uint8, device=dev),
+                             torch.zeros(1, hkv, nb + 1, dtype=torch.int32, device=dev), **kw)
+        torch.cuda.synchronize()
+        ref, _ = oracle.decode_step(dict(
+            q=np64(q), a=np64(a[None]), bl=np64(b_l[l][None]), w_lin=np64(w_lin[l][None]), w1=np64(bf(w1[l][None])),
+            w2=np64(bf(w2[l][None])), b1=np64(bf(b1[l][None])), b2=np64(bf(b2[l][None])),
+            res_idx=pr["idx"][l][None].cpu().numpy(), res_val=pr["val"][l][None].cpu().numpy(),
+            res_scale=pr["scale"][l][None].cpu().numpy(), block=64))
+        err = rel_err(out.float().cpu().numpy(), ref)
+        exact = _exact_attention(np64(q[0]), np64(keys[l]).reshape(T, hkv, d), np64(vals[l]), hq // hkv)
+        e_res = rel_err(out.float().cpu().numpy()[0], exact)
+        e_none = rel_err(out0.float().cpu().numpy()[0], exact)
+        print(f"layer {l}: parity {err:.2e}; vs exact attention: {e_none:.3f} without residuals, "
+              f"{e_res:.3f} with 2-bit residuals; fit loss {losses[l, 0, 0].item():.3f} -> {losses[l, 0, -1].item():.3f}",
+              flush=True)
+        assert err <= 2e-2
+        assert e_res < e_none
