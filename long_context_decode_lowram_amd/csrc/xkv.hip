@@ -69,6 +69,24 @@ __device__ __forceinline__ void xkv_tile(int k, int nt, int& ti, int& tj) {
     tj = i + k;
 }
 
+// k-th upper tile (I <= J) when the tiles are walked 4 x 4 blocks at a time
+// (block rows in order, block columns from the diagonal on, row-major inside).
+__device__ __forceinline__ void xkv_tile_blocked(int k, int nt, int& ti, int& tj) {
+    const int nb = (nt + 3) / 4;
+    for (int bi = 0; bi < nb; ++bi)
+        for (int bj = bi; bj < nb; ++bj)
+            for (int i = 4 * bi; i < min(nt, 4 * bi + 4); ++i)
+                for (int j = max(i, 4 * bj); j < min(nt, 4 * bj + 4); ++j) {
+                    if (k == 0) {
+                        ti = i;
+                        tj = j;
+                        return;
+                    }
+                    --k;
+                }
+    ti = tj = 0;
+}
+
 // ---------------------------------------------------------------- Gram
 // Block (b, problem): token chunk b / n_upper, tile b % n_upper (chunk-major,
 // so the workgroups resident together share one chunk of C). The stored
@@ -136,10 +154,17 @@ __global__ __launch_bounds__(kGramThreads, 1) void xkv_gram_kernel(XkvParams p) 
     __shared__ __attribute__((aligned(16))) unsigned char st2[kGStage];
     __shared__ __attribute__((aligned(16))) unsigned char st3[kGStage];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int chunk = blockIdx.x / p.n_upper;
-    const int tile = blockIdx.x - chunk * p.n_upper;
+    // Blocks go round-robin over the 8 XCDs; XCD x takes the contiguous run
+    // of positions x * per .. x * per + per - 1, in an order that walks the
+    // upper tiles 4 x 4 blocks at a time, so the workgroups resident on one
+    // XCD share few column slices in its L2.
+    const int total = p.n_chunks * p.n_upper, per = (total + 7) / 8;
+    const int pos = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (pos >= total) return;
+    const int chunk = pos / p.n_upper;
     int ti, tj;
-    xkv_tile(tile, p.nt, ti, tj);
+    xkv_tile_blocked(pos - chunk * p.n_upper, p.nt, ti, tj);
+    const int tile = ti * p.nt - ti * (ti - 1) / 2 + (tj - ti);     // row-major upper index
     const int t_begin = chunk * p.chunk_len;
     const int t_end = min(p.ctx_len, t_begin + p.chunk_len);
     const int n_steps = (t_end - t_begin + kGK - 1) / kGK;
@@ -606,8 +631,8 @@ __global__ __launch_bounds__(kXThreads, 1) void xkv_a_kernel(XkvParams p) {
 size_t xkv_partials_floats(const XkvParams& p) { return (size_t)p.n_chunks * p.n_upper * kXT * kXT; }
 
 hipError_t launch_xkv_gram(const XkvParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(xkv_gram_kernel, dim3((unsigned)(p.n_chunks * p.n_upper), (unsigned)p.n_batch),
-                       dim3(kGramThreads), 0, s, p);
+    const unsigned per = (unsigned)((p.n_chunks * p.n_upper + 7) / 8);
+    hipLaunchKernelGGL(xkv_gram_kernel, dim3(8 * per, (unsigned)p.n_batch), dim3(kGramThreads), 0, s, p);
     return hipGetLastError();
 }
 
