@@ -65,7 +65,9 @@ int plan_decode(const lowram_decode_args* a, DecodePlan* pl) {
     pl->n_split = (pl->n_cand + pl->bps - 1) / pl->bps;
     if (pl->n_split < 1) pl->n_split = 1;
     pl->part_stride = (2 + a->mlp_hidden + kHeadDim + 3) & ~3;
-    const size_t smem = sizeof(float) * ((size_t)pl->n_split + a->win_len + a->mlp_hidden + 3 * kHeadDim + 8);
+    DecodeParams sm{};
+    sm.n_split = pl->n_split; sm.win_len = a->win_len; sm.hidden = a->mlp_hidden;
+    const size_t smem = combine_smem_bytes(sm);
     if (smem > 65536) return fail(LOWRAM_ERR_UNSUPPORTED, "too many splits plus window tokens for the combine");
 
     const size_t B = a->batch;

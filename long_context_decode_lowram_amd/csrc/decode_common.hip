@@ -61,26 +61,91 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 // after rescaling every record to the common max; W2 and b2 are linear and
 // the weights p sum to L, so applying them after the weighted sum gives the
 // predictor's value for every token exactly (up to rounding).
+constexpr int kCombWaves = 8;
+constexpr int kCombThreads = kCombWaves * 64;
+
 template <int ACT>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int h = j / p.group, H = p.hidden, S = p.part_stride;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int h = j / p.group, H = p.hidden, S = p.part_stride, nf = H + kHeadDim;
     const int nsplit = min(p.n_split, (p.att_count[b] + p.blocks_per_split - 1) / p.blocks_per_split);
     const int nw = p.win_len;
     const float* P = p.partials + ((int64_t)b * p.n_q + j) * p.n_split * (int64_t)S;
     extern __shared__ float sm[];
-    float* es = sm;                       // [n_split]
-    float* sw = es + p.n_split;           // [win_len]
+    float* sw = sm;                       // [win_len]
     float* oc = sw + nw;                  // [H + 128]
-    float* qs = oc + H + kHeadDim;        // [128]
-    float* red = qs + kHeadDim;           // [8 + 128]: block reductions, then the second half-sums
+    float* qs = oc + nf;                  // [128]
+    float* red = qs + kHeadDim;           // [8 + 3 * 128]: block reductions, then the W2 quarter sums
+    float* part = red + 8 + 3 * kHeadDim; // [8][H + 128]: the waves' record sums
+    float* wml = part + kCombWaves * nf;  // [8][2]: each wave's max and weight sum
 
+    // out[f] takes four threads, a quarter of the W2 row each; the first 256
+    // bytes of that quarter are loaded now, before anything they wait on.
+    const int f_out = tid & (kHeadDim - 1), quarter = tid >> 7;
+    const int64_t w2row = (((int64_t)b * p.n_kv + h) * kHeadDim + f_out) * H;
+    const int i0 = quarter * (H / 4), n_c = (H / 4) / 8;       // 16-byte pieces of the quarter
+    const bool w2_vec = ACT == DT_BF16 && H % 32 == 0;
+    const uint4* w2v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.w2) + w2row + i0);
+    uint4 w2pre[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w2pre[c] = (w2_vec && c < n_c) ? w2v[c] : make_uint4(0u, 0u, 0u, 0u);
+
+    // Records: wave wv merges the splits wv, wv+8, ... eight at a time, with
+    // a running max (every sum is rescaled to it as it grows), so the loads of
+    // a batch's maxima, weight sums and O rows are in flight together. Lane
+    // takes the features lane + 64 i, six at a time: each load of the wave
+    // reads 256 consecutive bytes of one record.
+    for (int f0 = 0; f0 < nf; f0 += 64 * 6) {
+        float mrun = -INFINITY, lrun = 0.f;
+        float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s0 = wv; s0 < nsplit; s0 += kCombWaves * 8) {
+            float mb[8], lb[8], v[8][6];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sp = s0 + kCombWaves * u;
+                const bool ok = sp < nsplit;
+                const float* rec = P + (int64_t)(ok ? sp : 0) * S;
+                mb[u] = ok ? rec[0] : -INFINITY;
+                lb[u] = ok ? rec[1] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const int fi = f0 + lane + 64 * i;
+                    v[u][i] = (ok && fi < nf) ? rec[2 + fi] : 0.f;
+                }
+            }
+            float mnew = mrun;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mnew = fmaxf(mnew, mb[u]);
+            const float r = mrun == -INFINITY ? 0.f : expf(mrun - mnew);
+            lrun *= r;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) acc[i] *= r;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float e = mb[u] == -INFINITY ? 0.f : expf(mb[u] - mnew);
+                lrun += e * lb[u];
+#pragma unroll
+                for (int i = 0; i < 6; ++i) acc[i] += e * v[u][i];
+            }
+            mrun = mnew;
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int fi = f0 + lane + 64 * i;
+            if (fi < nf) part[wv * nf + fi] = acc[i];
+        }
+        if (lane == 0 && f0 == 0) {
+            wml[2 * wv] = mrun;
+            wml[2 * wv + 1] = lrun;
+        }
+    }
+
+    // Window tokens: exact keys and values, scored here.
     for (int f = tid; f < kHeadDim; f += blockDim.x)
         qs[f] = ld<ACT>(p.q, ((int64_t)b * p.n_q + j) * kHeadDim + f);
     __syncthreads();
-
     float mx = -INFINITY;
-    for (int s = tid; s < nsplit; s += blockDim.x) mx = fmaxf(mx, P[(int64_t)s * S]);
     for (int u = tid; u < nw; u += blockDim.x) {
         const int64_t row = (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim;
         float acc = 0.f;
@@ -89,62 +154,64 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
         sw[u] = acc;
         mx = fmaxf(mx, acc);
     }
-    const float M = block_reduce(mx, red, true);
+    float M = block_reduce(mx, red, true);     // its barriers also publish part and wml
+    for (int w8 = 0; w8 < kCombWaves; ++w8) M = fmaxf(M, wml[2 * w8]);
 
     const int64_t out_row = ((int64_t)b * p.n_q + j) * kHeadDim;
     if (M == -INFINITY) {   // nothing attended for this sequence
         for (int f = tid; f < kHeadDim; f += blockDim.x) st<ACT>(p.out, out_row + f, 0.f);
     } else {
-        float lt = 0.f, lw = 0.f;
-        for (int s = tid; s < nsplit; s += blockDim.x) {
-            const float m = P[(int64_t)s * S];
-            const float e = (m == -INFINITY) ? 0.f : expf(m - M);
-            es[s] = e;
-            lt += e * P[(int64_t)s * S + 1];
+        float scl[kCombWaves], Lt = 0.f;
+#pragma unroll
+        for (int w8 = 0; w8 < kCombWaves; ++w8) {
+            scl[w8] = wml[2 * w8] == -INFINITY ? 0.f : expf(wml[2 * w8] - M);
+            Lt += scl[w8] * wml[2 * w8 + 1];
         }
+        float lw = 0.f;
         for (int u = tid; u < nw; u += blockDim.x) {
             const float e = expf(sw[u] - M);
             sw[u] = e;
             lw += e;
         }
-        const float Lt = block_reduce(lt, red, false);
         const float Lw = block_reduce(lw, red, false);
-        for (int f = tid; f < H + kHeadDim; f += blockDim.x) {
-            float acc = 0.f;
-            for (int s = 0; s < nsplit; ++s) acc += es[s] * P[(int64_t)s * S + 2 + f];
-            oc[f] = acc;
+        for (int f = tid; f < nf; f += blockDim.x) {
+            float v = 0.f;
+#pragma unroll
+            for (int w8 = 0; w8 < kCombWaves; ++w8) v += scl[w8] * part[w8 * nf + f];
+            oc[f] = v;
         }
         __syncthreads();
-        // out[f] = (sum_i O_G[i] W2[f][i] + O_V[f] + L b2[f] + window) / (L + L_w):
-        // two threads per output feature, each half of the W2 row in 16-byte loads.
+        // out[f] = (sum_i O_G[i] W2[f][i] + O_V[f] + L b2[f] + window) / (L + L_w).
         const float inv = 1.0f / (Lt + Lw);
-        const int f = tid & (kHeadDim - 1), half = tid >> 7;      // blockDim.x == 256
-        const int64_t w2row = (((int64_t)b * p.n_kv + h) * kHeadDim + f) * H;
-        const int i0 = half * (H / 2), i1 = i0 + H / 2;
+        const int f = f_out;
         float y = 0.f;
-        if (ACT == DT_BF16) {
-            const uint4* wv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.w2) + w2row + i0);
-            for (int c = 0; c < (i1 - i0) / 8; ++c) {
-                const uint4 u = wv[c];
+        if (w2_vec) {
+            auto piece = [&](int c, const uint4 u) {
                 const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int i = i0 + 8 * c + 2 * k;
                     y += oc[i] * __uint_as_float(wd[k] << 16) + oc[i + 1] * __uint_as_float(wd[k] & 0xffff0000u);
                 }
-            }
+            };
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (c < n_c) piece(c, w2pre[c]);
+            for (int c = 8; c < n_c; ++c) piece(c, w2v[c]);
         } else {
+            const int i1 = quarter == 3 ? H : i0 + H / 4;
             for (int i = i0; i < i1; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
         }
-        if (half == 1) {
+        if (quarter == 3) {
             y += oc[H + f];
             if (p.b2) y += Lt * ld<ACT>(p.b2, ((int64_t)b * p.n_kv + h) * kHeadDim + f);
             for (int u = 0; u < nw; ++u)
                 y += sw[u] * ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f);
-            red[8 + f] = y;
         }
+        if (quarter > 0) red[8 + (quarter - 1) * kHeadDim + f] = y;
         __syncthreads();
-        if (half == 0) st<ACT>(p.out, out_row + f, (y + red[8 + f]) * inv);
+        if (quarter == 0)
+            st<ACT>(p.out, out_row + f, (((y + red[8 + f]) + red[8 + kHeadDim + f]) + red[8 + 2 * kHeadDim + f]) * inv);
     }
     if (p.stats != nullptr && j % p.group == 0 && tid == 0) {
         int tok = 0, res = 0;
@@ -159,15 +226,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
 }
 
 size_t combine_smem_bytes(const DecodeParams& p) {
-    return sizeof(float) * ((size_t)p.n_split + p.win_len + p.hidden + 3 * kHeadDim + 8);
+    return sizeof(float) * ((size_t)p.win_len + (kCombWaves + 1) * ((size_t)p.hidden + kHeadDim) + 4 * kHeadDim + 8 +
+                            2 * kCombWaves);
 }
 
 hipError_t launch_combine(const DecodeParams& p, int act, hipStream_t s) {
     const size_t smem = combine_smem_bytes(p);
     if (act == DT_F32)
-        hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(p.n_q, p.batch), dim3(256), smem, s, p);
+        hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(p.n_q, p.batch), dim3(kCombThreads), smem, s, p);
     else
-        hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(p.n_q, p.batch), dim3(256), smem, s, p);
+        hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(p.n_q, p.batch), dim3(kCombThreads), smem, s, p);
     return hipGetLastError();
 }
 

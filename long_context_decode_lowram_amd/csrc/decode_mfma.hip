@@ -27,6 +27,8 @@
 //      split merge: sum_t p_t (g_t W2 + b2) = (sum_t p_t g_t) W2 + l b2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "mfma_util.hpp"
 
@@ -514,19 +516,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
     }
     __syncthreads();
-    for (int fc = 0; fc < n_fchunks; ++fc) {
+    // One feature chunk. GP: a chunk of W1 (GELU, bias) or of W_lin; a
+    // compile-time flag, so no branch splits a tile's MFMAs from the GELU of
+    // the tile before it and the two interleave.
+    auto fchunk = [&](int fc, auto gp_const) {
+        constexpr bool GP = decltype(gp_const)::value;
         u32x4 pre[4];
         stage_w(min(fc + 1, n_fchunks - 1), pre);   // unconditional; the last chunk reloads itself
         const __bf16* sw = (fc & 1) ? stg1 : stg0;
         const int f0 = fc * kFc;
-        const bool gpart = f0 < H;
         // Z for one 16-feature tile; on the W1 part the accumulator starts at the bias.
         auto ztile = [&](int ft, f32x4 (&z)[4]) {
             bf16x8 wf[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 wf[s] = lds16(sw, (uint32_t)((ft * 16 + l16) * 256 + (((4 * s + g4) ^ l16) * 16)));
-            const float bb = gpart ? b1s[f0 + ft * 16 + l16] : 0.f;
+            const float bb = GP ? b1s[f0 + ft * 16 + l16] : 0.f;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 z[tt] = f32x4{bb, bb, bb, bb};
@@ -539,13 +544,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft) {
             if (ft + 1 < 4) ztile(ft + 1, zn);        // the next tile's MFMAs overlap this tile's GELU
-            if (gpart) gelu_tail16(zc);
+            if constexpr (GP) gelu_tail16(zc);
             o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(zc[2 * u], zc[2 * u + 1]), o[ft]);
             if (ft + 1 < 4) {
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) zc[tt] = zn[tt];
+            }
+            if constexpr (GP) {
+                // Interleave: the next tile's 16 MFMAs each followed by a share
+                // of this tile's GELU, so the matrix pipe and the vector ALU
+                // work side by side.
+                if (ft + 1 < 4) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
         }
         float (*const os)[kMaxG][kFc] = (fc & 1) ? oslot1 : oslot0;
@@ -563,13 +583,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         for (int e = tid; e < G * kFc; e += kThreads) {
             const int j = e / kFc, fl = e % kFc;
             float v = os[0][j][fl] + os[1][j][fl] + os[2][j][fl] + os[3][j][fl];
-            if (!gpart) {        // the residual rows belong to the k W_lin features
+            if constexpr (!GP) {        // the residual rows belong to the k W_lin features
                 const int f = f0 - H + fl;
                 v += resS[0][j][f] + resS[1][j][f] + resS[2][j][f] + resS[3][j][f];
             }
             rec0[j * rec_step + 2 + f0 + fl] = v;
         }
-    }
+    };
+    for (int fc = 0; fc < H / kFc; ++fc) fchunk(fc, std::true_type{});
+    for (int fc = H / kFc; fc < n_fchunks; ++fc) fchunk(fc, std::false_type{});
 
     // ---- 5. record header and counts
     if (tid < G) {
