@@ -510,19 +510,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // barrier the query rows and the weights are dead, and their space holds
     // the two per-wave O buffers of the feature loop.
     for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
-    {
-        u32x4 pre[4];
-        stage_w(0, pre);
-        store_w(0, pre);         // stage buffers are free: every wave passed the last main-loop barrier
-    }
+    // Weight chunks go global -> registers -> LDS, loaded two chunks ahead:
+    // chunk fc stores chunk fc+1 from one register set (loaded at the start
+    // of chunk fc-1) and loads chunk fc+2 into the other; the two sets swap
+    // roles from chunk to chunk, so no copy waits on a load in flight.
+    u32x4 preA[4], preB[4];
+    stage_w(0, preA);
+    store_w(0, preA);            // stage buffers are free: every wave passed the last main-loop barrier
+    stage_w(min(1, n_fchunks - 1), preA);
     __syncthreads();
     // One feature chunk. GP: a chunk of W1 (GELU, bias) or of W_lin; a
     // compile-time flag, so no branch splits a tile's MFMAs from the GELU of
     // the tile before it and the two interleave.
-    auto fchunk = [&](int fc, auto gp_const) {
+    auto fchunk = [&](int fc, auto gp_const, u32x4 (&cur)[4], u32x4 (&nxt)[4]) {
         constexpr bool GP = decltype(gp_const)::value;
-        u32x4 pre[4];
-        stage_w(min(fc + 1, n_fchunks - 1), pre);   // unconditional; the last chunk reloads itself
+        stage_w(min(fc + 2, n_fchunks - 1), nxt);    // unconditional; the last chunks reload the last
         const __bf16* sw = (fc & 1) ? stg1 : stg0;
         const int f0 = fc * kFc;
         // Z for one 16-feature tile; on the W1 part the accumulator starts at the bias.
@@ -576,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 const int j = 4 * g4 + i;
                 if (j < G) os[w][j][ft * 16 + l16] = active ? o[ft][i] : 0.f;
             }
-        store_w((fc + 1) & 1, pre);     // the other buffer: nobody reads it in this chunk
+        store_w((fc + 1) & 1, cur);     // the other buffer: nobody reads it in this chunk
         __syncthreads();
         // Sum the four waves' O in fixed order. The next write of this buffer
         // comes two chunks later, after every wave has passed the next barrier.
@@ -590,8 +592,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             rec0[j * rec_step + 2 + f0 + fl] = v;
         }
     };
-    for (int fc = 0; fc < H / kFc; ++fc) fchunk(fc, std::true_type{});
-    for (int fc = H / kFc; fc < n_fchunks; ++fc) fchunk(fc, std::false_type{});
+    const int n_g = H / kFc;
+    for (int fc = 0; fc < n_g; fc += 2) {
+        fchunk(fc, std::true_type{}, preA, preB);
+        if (fc + 1 < n_g) fchunk(fc + 1, std::true_type{}, preB, preA);
+    }
+    auto wlin = [&](u32x4 (&r0)[4], u32x4 (&r1)[4]) {
+        for (int fc = n_g; fc < n_fchunks; fc += 2) {
+            fchunk(fc, std::false_type{}, r0, r1);
+            if (fc + 1 < n_fchunks) fchunk(fc + 1, std::false_type{}, r1, r0);
+        }
+    };
+    if (n_g % 2 == 0) wlin(preA, preB);
+    else wlin(preB, preA);
 
     // ---- 5. record header and counts
     if (tid < G) {
