@@ -317,8 +317,14 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     p.counts = reinterpret_cast<int32_t*>(ws + pl.off_counts);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_assemble(p, s);
-    if (e != hipSuccess) return hip_fail(e, "assemble launch");
+    // Without eviction flags the kernels read the selection in place; the
+    // compaction pass runs only when some selected blocks may be dropped.
+    p.att_direct = a->keep == nullptr;
+    hipError_t e = hipSuccess;
+    if (!p.att_direct) {
+        e = launch_assemble(p, s);
+        if (e != hipSuccess) return hip_fail(e, "assemble launch");
+    }
     if (a->ev_main_begin) {
         e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_begin), s);
         if (e != hipSuccess) return hip_fail(e, "event record");

@@ -107,6 +107,22 @@ struct DecodeParams {
     float* partials;       // [B, Hq, n_split, part_stride]
     int32_t* counts;       // [B, Hkv, n_split, 2]
     int n_sel;
+    int att_direct;        // no eviction flags: the attended blocks are sel (or all blocks) as given
 };
+
+// Attended block i of sequence b, or -1 for an entry outside the cache. With
+// eviction flags the assembly kernel has compacted the kept blocks into
+// att_list; without them the list is the selection itself (every block when
+// there is none), read in place.
+__device__ __forceinline__ int attended_block(const DecodeParams& p, int b, int i) {
+    if (p.att_direct) {
+        const int blk = p.sel ? p.sel[(int64_t)b * p.n_sel + i] : i;
+        return (blk >= 0 && blk < p.n_blocks) ? blk : -1;
+    }
+    return p.att_list[(int64_t)b * p.n_blocks + i];
+}
+__device__ __forceinline__ int attended_count(const DecodeParams& p, int b) {
+    return p.att_direct ? (p.sel ? p.n_sel : p.n_blocks) : p.att_count[b];
+}
 
 }  // namespace lowram

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int h = j / p.group, H = p.hidden, S = p.part_stride, nf = H + kHeadDim;
-    const int nsplit = min(p.n_split, (p.att_count[b] + p.blocks_per_split - 1) / p.blocks_per_split);
+    const int nsplit = min(p.n_split, (attended_count(p, b) + p.blocks_per_split - 1) / p.blocks_per_split);
     const int nw = p.win_len;
     const float* P = p.partials + ((int64_t)b * p.n_q + j) * p.n_split * (int64_t)S;
     extern __shared__ float sm[];

@@ -26,13 +26,13 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
     };
     int32_t* cnt_rec = p.counts + (((int64_t)b * p.n_kv + h) * p.n_split + i) * 2;
 
-    if (i >= p.att_count[b]) {
+    const int blk = i < attended_count(p, b) ? attended_block(p, b, i) : -1;
+    if (blk < 0) {
         for (int jj = 0; jj < G; ++jj)
             for (int f = tid; f < S; f += kThreads) rec(jj)[f] = (f == 0) ? -INFINITY : 0.f;
         if (tid == 0) { cnt_rec[0] = 0; cnt_rec[1] = 0; }
         return;
     }
-    const int blk = p.att_list[(int64_t)b * p.n_blocks + i];
     const int t0 = blk * kBlock;
     const int nt = min(kBlock, p.ctx_len - t0);
 

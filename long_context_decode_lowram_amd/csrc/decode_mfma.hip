@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int h = slot % p.n_kv;
     const int split = (slot / p.n_kv) * kXcd + xcd;
     if (split >= p.n_split) return;
-    const int n_att = p.att_count[b];
+    const int n_att = attended_count(p, b);
     if (split * kWaves >= n_att) return;         // beyond this sequence's attended blocks
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -139,8 +139,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                   "epilogue arrays overflow sa");
 
     const int bi = split * kWaves + w;                 // this wave's attended-block index
-    const bool active = bi < n_att;
-    const int blk = active ? p.att_list[(int64_t)b * p.n_blocks + bi] : 0;
+    const int blk_or_none = bi < n_att ? attended_block(p, b, bi) : -1;
+    const bool active = blk_or_none >= 0;
+    const int blk = active ? blk_or_none : 0;
     const int t0 = blk * kBlock;
     const int nt = active ? min(kBlock, p.ctx_len - t0) : 0;
 
