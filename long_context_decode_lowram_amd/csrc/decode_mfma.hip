@@ -48,6 +48,9 @@ constexpr int kXcd = 8;                   // XCDs on MI355X; workgroups go round
 constexpr int kABytes = kBlock * kRowBytes;   // one wave's A rows of a rank chunk: 8 KB
 static_assert(128 * kRowBytes == kStage * 2, "a stage buffer holds one B_l chunk or one weight chunk");
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+
 // Two 4-element halves (n .. n+3 and n+16 .. n+19) of a bf16 LDS row.
 __device__ __forceinline__ bf16x8 lds_pair(const __bf16* row, int n) {
     const u32x2 lo = *reinterpret_cast<const u32x2*>(row + n);
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     __shared__ __attribute__((aligned(16))) unsigned char sa[kWaves * kABytes];
     __shared__ __attribute__((aligned(16))) unsigned char sres[kWaves * 4096];
     __bf16* const qs = reinterpret_cast<__bf16*>(sa);                                  // [16][kQRow]
-    float (*const pl)[kMaxG][kBlock] = reinterpret_cast<float (*)[kMaxG][kBlock]>(sa + 4352);   // softmax weights
+    float (*const pl)[kMaxG][kBlock + 1] = reinterpret_cast<float (*)[kMaxG][kBlock + 1]>(sa + 4352);   // softmax weights, rows padded
     // per-wave O of a feature chunk, two buffers; they reuse the space of qs
     // and pl, which are dead by the feature loop
     float (*const oslot0)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa);
@@ -135,7 +138,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     float (*const lw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(sa + 24960);         // per-wave weight sum
     int* const cnt_tok = reinterpret_cast<int*>(sa + 25088);
     int* const cnt_res = reinterpret_cast<int*>(sa + 25104);
-    static_assert(25120 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736,
+    static_assert(25120 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736 &&
+                      4352 + kWaves * kMaxG * (kBlock + 1) * 4 <= 20736,
                   "epilogue arrays overflow sa");
 
     const int bi = split * kWaves + w;                 // this wave's attended-block index
@@ -168,7 +172,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(
             static_cast<const unsigned char*>(p.res_val) + (res_row + q0) * (int64_t)kResRowB, (uint32_t)(n * kResRowB));
 #pragma unroll
-        for (int q = 0; q < kResPieces; ++q) dma16(rr, rs_w + q * 1024, (uint32_t)(q * 1024 + lane * 16), 0u);
+        for (int q = 0; q < kResPieces; ++q) {
+            uint32_t src = (uint32_t)(q * 1024 + lane * 16);
+            if constexpr (RDT == DT_BF16) {
+                // 256-byte rows; 32-byte piece pair c of row r sits at pair
+                // c ^ (r & 7), so the transposing reads below are free of bank
+                // conflicts: lane i fills row 4q + i/16, slot i%16.
+                const int r = 4 * q + (lane >> 4), slot = lane & 15;
+                src = (uint32_t)(r * 256 + (((((slot >> 1) ^ (r & 7)) << 1) | (slot & 1)) * 16));
+            }
+            dma16(rr, rs_w + q * 1024, src, 0u);
+        }
     };
     // Token (relative to the block) and int8 scale of residual row q0 + lane.
     auto res_meta = [&](int q0, int& tok, float& scl) {
@@ -449,48 +463,86 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
     for (int ft = 0; ft < 8; ++ft) rv[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     int applied = 0;
-    for (int q0 = lo; q0 < hi; q0 += kResRows) {
-        if (q0 != lo) {
-            wait_lgkmcnt0();               // this wave's reads of the previous rows are done
-            dma_res(q0);
-        }
-        const int n = min(kResRows, hi - q0);
-        int tok = tok0;
-        float scl = scl0;
-        if (q0 != lo) res_meta(q0, tok, scl);
-        wait_vmcnt<0>();
-        // Four rows per step, all their LDS reads first. Rows past n read the
-        // zeros the copy left there; rows outside the block get weight zero.
-        for (int r0 = 0; r0 < n; r0 += 4) {
-            float pw[4][4], v[4][8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = r0 + u;
-                const int t = __builtin_amdgcn_readlane(tok, r);
-                const bool ok = r < n && t >= 0 && t < nt;
-                applied += ok ? 1 : 0;
-                const int tc = ok ? t : 0;
-                const float wr = res_scaled(RDT) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), r)) : 1.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = 4 * g4 + i;
-                    pw[u][i] = (ok && j < G) ? pl[w][j][tc] * wr : 0.f;
-                }
-#pragma unroll
-                for (int ft = 0; ft < 8; ++ft) {
-                    const int f = ft * 16 + l16;
-                    if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
-                    else if (RDT == DT_BF16) v[u][ft] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rs_w + r * kResRowB + f * 2));
-                    else if (RDT == DT_I8) v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
-                    else v[u][ft] = static_cast<float>((rs_w[r * kResRowB + (f >> 2)] >> (2 * (f & 3))) & 3u) - 1.5f;
-                }
+    if constexpr (RDT == DT_BF16) {
+        // sum_r P[j][t_r] R[r][f] on MFMA 16x16x16 (bf16 operands, fp32 sums),
+        // 16 rows a batch. A operand: lane (l16, g4) holds the weights of query
+        // head l16 for rows 4 g4 .. 4 g4 + 3 (token of row r from lane r); B
+        // operand: the transposing LDS read gives lane (l16, g4) feature
+        // 16 ft + l16 of those four rows. The result lands as rv[ft][i] =
+        // feature 16 ft + l16 of query head 4 g4 + i. Rows past n are the
+        // zeros the copy left and get weight zero, as do rows outside the block.
+        static_assert(kResRows == 16, "one MFMA k-step per batch of bf16 rows");
+        for (int q0 = lo; q0 < hi; q0 += kResRows) {
+            if (q0 != lo) {
+                wait_lgkmcnt0();               // this wave's reads of the previous rows are done
+                dma_res(q0);
             }
+            const int n = min(kResRows, hi - q0);
+            int tok = tok0;
+            float scl_unused = 1.f;
+            if (q0 != lo) res_meta(q0, tok, scl_unused);
+            applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
+            s16x4 pa;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g4 + i;
+                const int t = __shfl(tok, r, kWave);
+                const bool ok = r < n && t >= 0 && t < nt && l16 < G;
+                pa[i] = __builtin_bit_cast(short, (__bf16)(ok ? pl[w][l16][t] : 0.f));
+            }
+            wait_vmcnt<0>();
+            const int rr = 4 * g4 + (l16 >> 2);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int ft = 0; ft < 8; ++ft) rv[ft][i] += pw[u][i] * v[u][ft];
+            for (int ft = 0; ft < 8; ++ft) {
+                const uint32_t off = (uint32_t)(rr * 256 + ((((ft ^ (rr & 7)) << 1) | ((l16 & 3) >> 1)) * 16) + 8 * (l16 & 1));
+                const s16x4 pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(rs_w + off));
+                rv[ft] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, pb, rv[ft], 0, 0, 0);
+            }
+        }
+    } else {
+        for (int q0 = lo; q0 < hi; q0 += kResRows) {
+            if (q0 != lo) {
+                wait_lgkmcnt0();               // this wave's reads of the previous rows are done
+                dma_res(q0);
+            }
+            const int n = min(kResRows, hi - q0);
+            int tok = tok0;
+            float scl = scl0;
+            if (q0 != lo) res_meta(q0, tok, scl);
+            wait_vmcnt<0>();
+            // Four rows per step, all their LDS reads first. Rows past n read the
+            // zeros the copy left there; rows outside the block get weight zero.
+            for (int r0 = 0; r0 < n; r0 += 4) {
+                float pw[4][4], v[4][8];
+    #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = r0 + u;
+                    const int t = __builtin_amdgcn_readlane(tok, r);
+                    const bool ok = r < n && t >= 0 && t < nt;
+                    applied += ok ? 1 : 0;
+                    const int tc = ok ? t : 0;
+                    const float wr = res_scaled(RDT) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl), r)) : 1.f;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 4 * g4 + i;
+                        pw[u][i] = (ok && j < G) ? pl[w][j][tc] * wr : 0.f;
+                    }
+    #pragma unroll
+                    for (int ft = 0; ft < 8; ++ft) {
+                        const int f = ft * 16 + l16;
+                        if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
+                        else if (RDT == DT_BF16) v[u][ft] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rs_w + r * kResRowB + f * 2));
+                        else if (RDT == DT_I8) v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
+                        else v[u][ft] = static_cast<float>((rs_w[r * kResRowB + (f >> 2)] >> (2 * (f & 3))) & 3u) - 1.5f;
+                    }
+                }
+    #pragma unroll
+                for (int u = 0; u < 4; ++u)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+    #pragma unroll
+                        for (int ft = 0; ft < 8; ++ft) rv[ft][i] += pw[u][i] * v[u][ft];
+            }
         }
     }
     // Park the residual sums in this wave's quarter of sres (its rows are
