@@ -20,8 +20,12 @@
 //      S^T = K . Q^T  (query heads of this KV head padded to 16 columns),
 //      Z   = K . [W1 | W_lin]^T  in chunks of 64 features.
 //   3. Softmax weights against the workgroup-wide max; gelu(Z_W1 + b1) in
-//      fp32; O = P . [gelu | K W_lin]  (P in registers as the A operand).
-//   4. Residual rows of the block add P[t] * R to the K W_lin part.
+//      fp32; O = P . [gelu | K W_lin]  (P in registers as the A operand). The
+//      W1 chunks and the W_lin chunks run as separate passes, so each tile's
+//      MFMAs interleave with the previous tile's GELU; weight chunks are
+//      loaded two chunks ahead.
+//   4. Residual rows of the block add P[t] * R to the K W_lin part (bf16 rows
+//      on MFMA 16x16x16 through transposing LDS reads; other codes per row).
 //   5. The four waves' O are summed in fixed order into one partial record
 //      (m, l, O_G[h], O_V[d]); the combine kernel applies W2 and b2 after the
 //      split merge: sum_t p_t (g_t W2 + b2) = (sum_t p_t g_t) W2 + l b2.
@@ -215,16 +219,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     uint32_t bl_off[4];         // B_l: this wave fills rows 32w .. 32w+31 of the head's 128
 #pragma unroll
     for (int q = 0; q < 4; ++q) bl_off[q] = (uint32_t)((w * 32 + q * 8 + dma_row) * R * 2) + dma_piece;
+    // Copies past the last chunk go to a resource of size zero: they read
+    // zeros and touch no memory, so every chunk issues the same copies.
+    const __amdgpu_buffer_rsrc_t rnone = buffer_rsrc(p.b_l, 0u);
     auto dma_bl = [&](int c, __bf16* buf) {
+        const __amdgpu_buffer_rsrc_t rbs = c < n_chunks ? rb : rnone;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            dma16(rb, reinterpret_cast<unsigned char*>(buf) + (w * 32 + q * 8) * kRowBytes, bl_off[q], (uint32_t)(c * kRowBytes));
+            dma16(rbs, reinterpret_cast<unsigned char*>(buf) + (w * 32 + q * 8) * kRowBytes, bl_off[q], (uint32_t)(c * kRowBytes));
     };
     unsigned char* const sa_w = sa + w * kABytes;     // this wave's A rows (bf16 factor)
     auto dma_a = [&](int c) {
+        const __amdgpu_buffer_rsrc_t ras = c < n_chunks ? ra : rnone;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            dma16(ra, sa_w + q * 8 * kRowBytes, (uint32_t)((q * 8 + dma_row) * R * 2) + dma_piece, (uint32_t)(c * kRowBytes));
+            dma16(ras, sa_w + q * 8 * kRowBytes, (uint32_t)((q * 8 + dma_row) * R * 2) + dma_piece, (uint32_t)(c * kRowBytes));
     };
 
     // MFMA operand reads: lane (l16, g4) takes row l16 of a 16-row tile at
@@ -275,12 +284,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
 
+    // MFMA steps s0 .. s1-1 of one rank chunk (B_l tile st % 8, k-step st / 8),
+    // each B_l fragment read two steps ahead; the first two are read by the caller.
+    auto mma_part = [&](const __bf16* sb, const bf16x8 (&a8)[2][4], bf16x8 (&bq)[3], auto s0c, auto s1c) {
+        constexpr int s0 = decltype(s0c)::value, s1 = decltype(s1c)::value;
+        auto rd = [&](int st) { return lds16(sb, rd_off[st >> 3] + (st & 7) * 16 * kRowBytes); };
+#pragma unroll
+        for (int st = s0; st < s1; ++st) {
+            if (st + 2 < 16) bq[(st + 2) % 3] = rd(st + 2);
+            const int kk = st >> 3, nt_ = st & 7;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bq[st % 3], a8[kk][tt], acc[nt_][tt]);
+        }
+        if (s0 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int st = s0; st < s1; ++st) {
+            if (st + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+    };
+
     if constexpr (ADT == DT_BF16) {
         // Per chunk c: read this wave's A fragments of c (copied during the
-        // previous chunk), start the copies of chunk c+1 (B_l into the other
-        // stage buffer, A into the now consumed region), run the MFMAs, then
-        // wait for the B_l copy only (the A copy stays in flight) and meet at
-        // the barrier.
+        // previous chunk), start the B_l copy of chunk c+1 into the other stage
+        // buffer, run four MFMA steps, then (the A reads are done by then)
+        // start the A copy of chunk c+1 into the consumed region and run the
+        // other twelve steps; wait for the B_l copy only (the A copy stays in
+        // flight) and meet at the barrier.
         dma_bl(0, stg0);
         dma_a(0);
         wait_vmcnt<8>();
@@ -292,12 +322,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = lds16(sa_w, rd_off[kk] + tt * 16 * kRowBytes);
-            wait_lgkmcnt0();
-            if (c + 1 < n_chunks) {
-                dma_bl(c + 1, nxt);
-                dma_a(c + 1);
-            }
-            mma_chunk(cur, a8);
+            dma_bl(c + 1, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 bq[3];
+            bq[0] = lds16(cur, rd_off[0]);
+            bq[1] = lds16(cur, rd_off[0] + 16 * kRowBytes);
+            mma_part(cur, a8, bq, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkmcnt<2>();   // LDS reads complete in order: with two B_l reads issued since, the A reads are done
+            dma_a(c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(cur, a8, bq, std::integral_constant<int, 4>{}, std::integral_constant<int, 16>{});
             wait_vmcnt<8>();
             barrier_lds();
         };
