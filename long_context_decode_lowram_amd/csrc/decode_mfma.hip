@@ -455,8 +455,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
     for (int u = 0; u < 2; ++u) pf[u] = pack8(sc[2 * u], sc[2 * u + 1]);
 
-    // ---- 3/4. feature chunks of [W1 | W_lin]: Z = K W^T, gelu on the W1 part, O = P Z
-    const int n_fchunks = (H + kHeadDim) / kFc;
+    // ---- 3/4. feature chunks of W1: Z = K W1^T + b1, gelu, O_G = P gelu(Z)
+    const int n_fchunks = H / kFc;
     const __bf16* w1 = static_cast<const __bf16*>(p.w1) + ((int64_t)b * p.n_kv + h) * H * (int64_t)kHeadDim;
     const __bf16* wl = static_cast<const __bf16*>(p.w_lin) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)kHeadDim;
     const __bf16* b1 = p.b1 ? static_cast<const __bf16*>(p.b1) + ((int64_t)b * p.n_kv + h) * H : nullptr;
@@ -468,8 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         for (int q = 0; q < 4; ++q) {
             const int e = tid + kThreads * q, row = e >> 4, col = (e & 15) * 8;
             const int f = fc * kFc + row;
-            const __bf16* src = f < H ? w1 + (int64_t)f * kHeadDim : wl + (int64_t)(f - H) * kHeadDim;
-            reg[q] = *reinterpret_cast<const u32x4*>(src + col);
+            reg[q] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)f * kHeadDim + col);
         }
     };
     // Weight chunks in LDS: 256-byte rows (one feature) of sixteen 16-byte
@@ -581,8 +580,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         }
     }
     // Park the residual sums in this wave's quarter of sres (its rows are
-    // consumed): resS[w][j][f] for f in 0..127, added in the cross-wave sum of
-    // the K W_lin chunks, so no registers hold them through the feature loop.
+    // consumed): resS[w][j][f] for f in 0..127, added to the value part below.
     float (*const resS)[kMaxG][kHeadDim] = reinterpret_cast<float (*)[kMaxG][kHeadDim]>(sres);
     static_assert(kWaves * kMaxG * kHeadDim * 4 <= kWaves * 4096, "residual sums overflow sres");
     wait_lgkmcnt0();
@@ -594,24 +592,128 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             for (int ft = 0; ft < 8; ++ft) resS[w][j][ft * 16 + l16] = rv[ft][i];
         }
     }
-    // The pre-pass above read only this wave's own softmax weights; after this
-    // barrier the query rows and the weights are dead, and their space holds
-    // the two per-wave O buffers of the feature loop.
-    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
     // Weight chunks go global -> registers -> LDS, loaded two chunks ahead:
     // chunk fc stores chunk fc+1 from one register set (loaded at the start
     // of chunk fc-1) and loads chunk fc+2 into the other; the two sets swap
-    // roles from chunk to chunk, so no copy waits on a load in flight.
+    // roles from chunk to chunk, so no copy waits on a load in flight. Chunk
+    // 0's loads start here, ahead of the value part.
     u32x4 preA[4], preB[4];
     stage_w(0, preA);
-    store_w(0, preA);            // stage buffers are free: every wave passed the last main-loop barrier
+
+    // ---- 4b. The value part by linearity: sum_t p_t (k_t W_lin^T) =
+    // (sum_t p_t k_t) W_lin^T. Each wave forms P K (query heads x 128
+    // features) on MFMA; the contraction runs over tokens, which K holds across
+    // lanes, so K goes through LDS once (this wave's 8 KB of a stage buffer,
+    // 32 token rows of 256 bytes, 32-byte pair c of row r at pair c ^ (r & 7))
+    // and comes back through the transposing read. The four waves' P K are
+    // summed in fixed order, rounded to bf16 and multiplied by W_lin^T (two
+    // 16-feature output tiles per wave); the residual sums are added and the
+    // result is the record's value part.
+    {
+        // W_lin rows of this wave's output tiles: lane (l16, g4) of tile e,
+        // k-step ks holds W_lin[16 (2w + e) + l16][32 ks + 8 g4 .. + 7].
+        u32x4 wlf[2][4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                wlf[e][ks] = *reinterpret_cast<const u32x4*>(wl + (int64_t)(16 * (2 * w + e) + l16) * kHeadDim + 32 * ks + 8 * g4);
+        unsigned char* const kt_w = reinterpret_cast<unsigned char*>(w < 2 ? stg0 : stg1) + (w & 1) * 8192;
+        f32x4 pk[8];
+#pragma unroll
+        for (int ft = 0; ft < 8; ++ft) pk[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {          // tokens 32 u .. 32 u + 31 (token tiles 2u, 2u + 1)
+            // kf[tt][s] holds, for token 16 tt + l16, features 32 s + 4 g4 + (0..3)
+            // (bytes 8 g4 of pair 2 s) and 32 s + 16 + 4 g4 + (0..3) (pair 2 s + 1).
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int rr = 16 * e + l16;
+#pragma unroll
+                for (int sg = 0; sg < 4; ++sg) {
+                    const u32x4 v = __builtin_bit_cast(u32x4, kf[2 * u + e][sg]);
+                    *reinterpret_cast<u32x2*>(kt_w + rr * 256 + (((2 * sg) ^ (rr & 7)) * 32) + 8 * g4) = u32x2{v[0], v[1]};
+                    *reinterpret_cast<u32x2*>(kt_w + rr * 256 + (((2 * sg + 1) ^ (rr & 7)) * 32) + 8 * g4) = u32x2{v[2], v[3]};
+                }
+            }
+            // B operand of tile ft: lane (l16, g4) takes feature 16 ft + l16 of
+            // token rows 4 g4 + (0..3) and 16 + 4 g4 + (0..3), the k-slot order
+            // of pf[u]; lanes 4 r' + c name row 4 g4 + r' at columns 16 ft + 4 c.
+            const int r1 = 4 * g4 + (l16 >> 2), r2 = r1 + 16;
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t)(kt_w + r1 * 256 + ((ft ^ (r1 & 7)) * 32) + 8 * (l16 & 3)));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t)(kt_w + r2 * 256 + ((ft ^ (r2 & 7)) * 32) + 8 * (l16 & 3)));
+                u32x4 bv;
+                bv[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+                bv[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+                bv[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+                bv[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+                pk[ft] = mfma(pf[u], as_bf16x8(bv), pk[ft]);
+            }
+            wait_lgkmcnt0();                   // this wave's reads are done before the next rows overwrite them
+        }
+        // P K of each wave, pk_w[j][f], in that wave's own 8 KB (its K rows are
+        // read), so only one barrier orders the four waves' sums.
+        auto pks = [&](int ww) {
+            return reinterpret_cast<float (*)[kHeadDim]>(reinterpret_cast<unsigned char*>(ww < 2 ? stg0 : stg1) + (ww & 1) * 8192);
+        };
+        static_assert(kMaxG * kHeadDim * 4 <= 8192, "P K sums overflow a wave's space");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = 4 * g4 + i;
+            if (j < G) {
+#pragma unroll
+                for (int ft = 0; ft < 8; ++ft) pks(w)[j][ft * 16 + l16] = pk[ft][i];
+            }
+        }
+        barrier_lds();
+        // A operand: (sum over waves of P K)[j = l16][32 ks + 8 g4 .. + 7] in bf16.
+        bf16x8 pa[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float sum[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sum[i] = 0.f;
+            if (l16 < G) {
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const float* src = &pks(ww)[l16][32 * ks + 8 * g4];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) sum[i] += src[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pa[ks][i] = (__bf16)sum[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            f32x4 ov = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) ov = mfma(pa[ks], as_bf16x8(wlf[e][ks]), ov);
+            const int f = 16 * (2 * w + e) + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * g4 + i;
+                if (j < G)
+                    rec0[j * rec_step + 2 + H + f] =
+                        ov[i] + (((resS[0][j][f] + resS[1][j][f]) + resS[2][j][f]) + resS[3][j][f]);
+            }
+        }
+    }
+    // Past the value part's barrier every wave is done with the query rows and
+    // softmax weights; their space holds the two per-wave O buffers of the
+    // feature loop.
+    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
+    barrier_lds();               // every wave has read the P K sums in the stage buffers
+    store_w(0, preA);
     stage_w(min(1, n_fchunks - 1), preA);
     __syncthreads();
-    // One feature chunk. GP: a chunk of W1 (GELU, bias) or of W_lin; a
-    // compile-time flag, so no branch splits a tile's MFMAs from the GELU of
-    // the tile before it and the two interleave.
-    auto fchunk = [&](int fc, auto gp_const, u32x4 (&cur)[4], u32x4 (&nxt)[4]) {
-        constexpr bool GP = decltype(gp_const)::value;
+    // One feature chunk of W1. No branch splits a tile's MFMAs from the GELU
+    // of the tile before it, so the two interleave.
+    auto fchunk = [&](int fc, u32x4 (&cur)[4], u32x4 (&nxt)[4]) {
         stage_w(min(fc + 2, n_fchunks - 1), nxt);    // unconditional; the last chunks reload the last
         const __bf16* sw = (fc & 1) ? stg1 : stg0;
         const int f0 = fc * kFc;
@@ -621,7 +723,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 wf[s] = lds16(sw, (uint32_t)((ft * 16 + l16) * 256 + (((4 * s + g4) ^ l16) * 16)));
-            const float bb = GP ? b1s[f0 + ft * 16 + l16] : 0.f;
+            const float bb = b1s[f0 + ft * 16 + l16];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 z[tt] = f32x4{bb, bb, bb, bb};
@@ -634,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
         for (int ft = 0; ft < 4; ++ft) {
             if (ft + 1 < 4) ztile(ft + 1, zn);        // the next tile's MFMAs overlap this tile's GELU
-            if constexpr (GP) gelu_tail16(zc);
+            gelu_tail16(zc);
             o[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 2; ++u) o[ft] = mfma(pf[u], pack8(zc[2 * u], zc[2 * u + 1]), o[ft]);
@@ -642,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) zc[tt] = zn[tt];
             }
-            if constexpr (GP) {
+            {
                 // Interleave: the next tile's 16 MFMAs each followed by a share
                 // of this tile's GELU, so the matrix pipe and the vector ALU
                 // work side by side.
@@ -673,26 +775,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         for (int e = tid; e < G * kFc; e += kThreads) {
             const int j = e / kFc, fl = e % kFc;
             float v = os[0][j][fl] + os[1][j][fl] + os[2][j][fl] + os[3][j][fl];
-            if constexpr (!GP) {        // the residual rows belong to the k W_lin features
-                const int f = f0 - H + fl;
-                v += resS[0][j][f] + resS[1][j][f] + resS[2][j][f] + resS[3][j][f];
-            }
             rec0[j * rec_step + 2 + f0 + fl] = v;
         }
     };
     const int n_g = H / kFc;
     for (int fc = 0; fc < n_g; fc += 2) {
-        fchunk(fc, std::true_type{}, preA, preB);
-        if (fc + 1 < n_g) fchunk(fc + 1, std::true_type{}, preB, preA);
+        fchunk(fc, preA, preB);
+        if (fc + 1 < n_g) fchunk(fc + 1, preB, preA);
     }
-    auto wlin = [&](u32x4 (&r0)[4], u32x4 (&r1)[4]) {
-        for (int fc = n_g; fc < n_fchunks; fc += 2) {
-            fchunk(fc, std::false_type{}, r0, r1);
-            if (fc + 1 < n_fchunks) fchunk(fc + 1, std::false_type{}, r1, r0);
-        }
-    };
-    if (n_g % 2 == 0) wlin(preA, preB);
-    else wlin(preB, preA);
 
     // ---- 5. record header and counts
     if (tid < G) {
