@@ -384,16 +384,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         ascl[tt] = ADT == DT_I8 && tl < nt ? p.a_scale[a_row0 + tl] : 1.f;
     }
 
-    // Tokens past the block's end contribute nothing: their K columns are set
-    // to zero whatever the factor rows there held.
+    // Tokens past the block's end contribute nothing: their factor rows were
+    // read through a resource that ends at the block, as zeros, so their K
+    // columns are zero already. int8 A: the per-row scale multiplies its column.
+    if constexpr (ADT == DT_I8) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int tl = tt * 16 + l16;
-        const float s = tl < nt ? ascl[tt] : 0.f;
+        for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-        for (int nt_ = 0; nt_ < 8; ++nt_)
+            for (int nt_ = 0; nt_ < 8; ++nt_)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[nt_][tt][i] = tl < nt ? acc[nt_][tt][i] * s : 0.f;
+                for (int i = 0; i < 4; ++i) acc[nt_][tt][i] *= ascl[tt];
+        }
     }
 
     // ---- stage the query rows of this head (rows >= G zero); sa is free now
