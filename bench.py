@@ -96,9 +96,10 @@ def work_per_call(cfg, n_att, n_res_att, win):
     Bytes: every attended A row once (int8 rows add their scale), every
     residual row applied (value, index, int8 scale), the layer factor, the
     predictor, q and out, the window rows. FLOPs: key rebuild 2*r*Hkv*d,
-    predictor 2*Hkv*d*(d + h) per token (the W2 product is applied after the
-    attention-weighted sum, a linear rewrite), scores 2*Hq*d and weighted sums
-    2*Hq*(d + h) per token."""
+    K W1 2*Hkv*d*h per token, scores 2*Hq*d and weighted sums 2*Hq*(d + h)
+    per token (P [K | gelu]), and W_lin once per group of four blocks
+    2*Hq*d*d: the linear parts W_lin, W2 and b2 are applied after the
+    attention-weighted sum, an exact rewrite of the per-token predictor."""
     d, hkv, hq, r, h = cfg.head_dim, cfg.n_kv_heads, cfg.n_q_heads, cfg.rank, cfg.mlp_hidden
     ea = {"f32": 4, "bf16": 2, "i8": 1}[cfg.a_dtype]
     ew = {"f32": 4, "bf16": 2}[cfg.act]
@@ -107,7 +108,7 @@ def work_per_call(cfg, n_att, n_res_att, win):
         byts += na * (r * ea + (4 if cfg.a_dtype == "i8" else 0))
         byts += nr * residual_row_bytes(cfg)
         byts += (r * hkv * d + hkv * (d * d + 2 * d * h)) * ew + 2 * hq * d * ew + win * 2 * hkv * d * ew
-        flops += 2 * na * hkv * d * (r + d + h) + 2 * na * hq * d + 2 * na * hq * (d + h)
+        flops += 2 * na * hkv * d * (r + h) + 2 * na * hq * d + 2 * na * hq * (d + h) + 2 * hq * d * d * -(-na // (4 * cfg.block))
         flops_direct += 2 * na * r * hkv * d + 2 * na * hkv * (d * d + 2 * d * h) + 4 * (na + win) * hq * d
     return byts, flops, flops_direct
 
