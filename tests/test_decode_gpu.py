@@ -46,6 +46,18 @@ def test_small_configs(name, generic):
     check(case, cfg, generic=generic)
 
 
+@pytest.mark.parametrize("res", ["bf16", "i8"])
+@pytest.mark.parametrize("gqa", [1, 2, 3, 8])
+def test_gqa_group_sizes(gqa, res):
+    """One to eight query heads per KV head. The fused kernel pads the group to
+    16 rows in its score, residual and value products; bf16 residual rows take
+    the matrix-core path, int8 rows the per-row one."""
+    base = C2 if res == "bf16" else C5
+    cfg = base.replace(ctx_len=64 * 24 + 11, batch=2, n_kv_heads=2, n_q_heads=2 * gqa)
+    case = make_case(cfg, layer=1, biases=True)
+    check(case, cfg, generic=False)
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
 def test_peaked_attention(generic):
     """Query rescaled so logits have a spread of about 4: a score-path bug
@@ -67,6 +79,22 @@ def test_no_residuals_and_every_token_a_residual(generic):
         check(case, cfg, generic=generic)
         set_residuals(case, cfg, torch.arange(cfg.ctx_len, dtype=torch.int32).expand(bsz, 8, -1))
         check(case, cfg, generic=generic)
+
+
+@pytest.mark.parametrize("res", ["bf16", "i8"])
+def test_residual_rows_per_block_around_batch_sizes(res):
+    """Blocks holding 1, 15, 16, 17, 33 and 64 residual rows, every block
+    attended: the bf16 path sums rows 16 at a time on the matrix cores, the
+    other codes copy 32 rows at a time."""
+    base = C2 if res == "bf16" else C5
+    cfg = base.replace(ctx_len=64 * 8, batch=2, sel_den=1, evict_half=False, res_dtype=res)
+    case = make_case(cfg, layer=0)
+    rows = []
+    for blk, n in enumerate([1, 15, 16, 17, 33, 64, 0, 2]):
+        rows += list(range(blk * 64 + (64 - n) // 2, blk * 64 + (64 - n) // 2 + n))
+    idx = torch.tensor(rows, dtype=torch.int32).expand(2, 8, -1)
+    set_residuals(case, cfg, idx)
+    check(case, cfg, generic=False)
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
