@@ -28,6 +28,8 @@
 // every weight fragment is one plain 16-byte piece of a weight row.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "mfma_util.hpp"
 
@@ -111,13 +113,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
 #pragma unroll
     for (int q = 0; q < 4; ++q) bl_off[q] = (uint32_t)(perm32(w * 32 + q * 8 + dma_row) * R * 2) + piece;
     unsigned char* const sa_w = ((w >> 1) ? buf3 : buf2) + (w & 1) * (kBlock * kPRow);
+    // Copies past the last chunk go to a resource of size zero: they read
+    // zeros and touch no memory, so every chunk issues the same copies.
+    const __amdgpu_buffer_rsrc_t rnone = buffer_rsrc(p.b_l, 0u);
     auto dma_bl = [&](int c, unsigned char* dst) {
+        const __amdgpu_buffer_rsrc_t r = c < n_chunks ? rb : rnone;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dma16(rb, dst + (w * 32 + q * 8) * kPRow, bl_off[q], (uint32_t)(c * kPRow));
+        for (int q = 0; q < 4; ++q) dma16(r, dst + (w * 32 + q * 8) * kPRow, bl_off[q], (uint32_t)(c * kPRow));
     };
     auto dma_a = [&](int c) {
+        const __amdgpu_buffer_rsrc_t r = c < n_chunks ? ra : rnone;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dma16(ra, sa_w + q * 8 * kPRow, a_off[q], (uint32_t)(c * kPRow));
+        for (int q = 0; q < 8; ++q) dma16(r, sa_w + q * 8 * kPRow, a_off[q], (uint32_t)(c * kPRow));
     };
     const int xs = g4 ^ (l16 & 7);
     const uint32_t rd_off[2] = {(uint32_t)(l16 * kPRow + xs * 16), (uint32_t)(l16 * kPRow + (xs ^ 4) * 16)};
@@ -127,25 +134,24 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto mma_chunk = [&](const unsigned char* sb, const bf16x8 (&a8)[2][4]) {
+    // MFMA steps s0 .. s1-1 of one rank chunk (B_l tile st % 8, k-step st / 8),
+    // each B_l fragment read two steps ahead; the first two are read by the caller.
+    auto mma_part = [&](const unsigned char* sb, const bf16x8 (&a8)[2][4], bf16x8 (&bq)[3], auto s0c, auto s1c) {
+        constexpr int s0 = decltype(s0c)::value, s1 = decltype(s1c)::value;
         auto rd = [&](int st) { return lds16(sb, rd_off[st >> 3] + (st & 7) * 16 * kPRow); };
-        bf16x8 bq[3];
-        bq[0] = rd(0);
-        bq[1] = rd(1);
 #pragma unroll
-        for (int st = 0; st < 16; ++st) {
+        for (int st = s0; st < s1; ++st) {
             if (st + 2 < 16) bq[(st + 2) % 3] = rd(st + 2);
             const int kk = st >> 3, nt_ = st & 7;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) acc[nt_][tt] = mfma(bq[st % 3], a8[kk][tt], acc[nt_][tt]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (s0 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int st = 0; st < 14; ++st) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int st = s0; st < s1; ++st) {
+            if (st + 2 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
     dma_bl(0, buf0);
     dma_a(0);
@@ -158,12 +164,21 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = lds16(sa_w, rd_off[kk] + tt * 16 * kPRow);
-        wait_lgkmcnt0();
-        if (c + 1 < n_chunks) {
-            dma_bl(c + 1, nxt);
-            dma_a(c + 1);
-        }
-        mma_chunk(cur, a8);
+        // The next chunk's B_l copy starts now (the other buffer); its A copy,
+        // into the region just read, four MFMA steps in, once the A reads are
+        // done (LDS reads complete in order: with two B_l reads issued since,
+        // they are).
+        dma_bl(c + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 bq[3];
+        bq[0] = lds16(cur, rd_off[0]);
+        bq[1] = lds16(cur, rd_off[0] + 16 * kPRow);
+        mma_part(cur, a8, bq, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt<2>();
+        dma_a(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_part(cur, a8, bq, std::integral_constant<int, 4>{}, std::integral_constant<int, 16>{});
         wait_vmcnt<8>();
         barrier_lds();
     };
