@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     }
 
     __shared__ __attribute__((aligned(16))) unsigned char buf0[kBuf], buf1[kBuf], buf2[kBuf], buf3[kBuf];
+    // This wave's 64 rows of V (256-byte rows; 16-byte piece p of row r at
+    // slot p ^ (r & 15)), copied after the keys so they land during the
+    // predictor steps. 128 KB of LDS in all: one workgroup per CU.
+    __shared__ __attribute__((aligned(16))) unsigned char sv[kPw * kBlock * 256];
 
     // ---- 1. K^T = B_l(head)^T . A^T over the rank, 64 columns per chunk
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(
@@ -301,6 +305,22 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
         barrier_lds();                      // every wave is done with this step's buffers
         if (j + 2 < n_steps) dma_step(j + 2, s0, s1);
     };
+    const int64_t vrow_stride = (int64_t)p.n_kv * kHeadDim;     // elements between tokens of V
+    const __bf16* vl = static_cast<const __bf16*>(p.v) + ((int64_t)l * T * p.n_kv + h) * kHeadDim;
+    unsigned char* const sv_w = sv + w * (kBlock * 256);
+    {
+        // Instruction q fills rows 4q .. 4q+3: lane i row 4q + i/16, slot i%16,
+        // fetching piece (i%16) ^ (row & 15); rows without a token read zeros.
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vl, (uint32_t)((int64_t)T * vrow_stride * 2));
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int row = 4 * q + (lane >> 4);
+            const int t = __shfl(my_tok, row, kWave);
+            const uint32_t pc = (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
+            dma16(rv, sv_w + q * 1024, t >= 0 ? (uint32_t)((int64_t)t * vrow_stride * 2) + pc : kOob, 0u);
+        }
+    }
+    // The V copies are older than the first step's: its wait covers them too.
     dma_step(0, buf0, buf1);
     if (n_steps > 1) dma_step(1, buf2, buf3);
     for (int j = 0; j < n_steps; j += 2) {  // static buffers: even steps in buf0/buf1
@@ -309,8 +329,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     }
 
     // ---- 3. per token: error (pass 1) or residual (pass 2)
-    const int64_t vrow_stride = (int64_t)p.n_kv * kHeadDim;     // elements between tokens of V
-    const __bf16* vl = static_cast<const __bf16*>(p.v) + ((int64_t)l * T * p.n_kv + h) * kHeadDim;
+    // V elements 16 ot + 4 g4 .. + 3 of row r: bytes 32 ot + 8 g4 of the row,
+    // piece 2 ot + g4 / 2 at its swizzled slot.
+    auto v4 = [&](int r, int ot) {
+        const int pc = 2 * ot + (g4 >> 1);
+        return *reinterpret_cast<const u32x2*>(sv_w + r * 256 + ((pc ^ (r & 15)) << 4) + 8 * (g4 & 1));
+    };
     if (MODE == 0) {
         // d^2 in binary64 by every lane for its 32 values, into this wave's
         // 16 KB LDS tile [16 tokens][128] (32-byte column c = 4ot + g of row
@@ -320,10 +344,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int t = __shfl(my_tok, tt * 16 + l16, kWave);
-            const __bf16* vr = vl + (int64_t)(t < 0 ? 0 : t) * vrow_stride;
 #pragma unroll
             for (int ot = 0; ot < 8; ++ot) {
-                const u32x2 vv = *reinterpret_cast<const u32x2*>(vr + ot * 16 + 4 * g4);
+                const u32x2 vv = v4(tt * 16 + l16, ot);
                 double d2[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -360,11 +383,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
             const int row = tt * 16 + l16;
             const int t = __shfl(my_tok, row, kWave);
             const int s = (grp * kPw + w) * kBlock + row;              // slot in the residual store
-            const __bf16* vr = vl + (int64_t)(t < 0 ? 0 : t) * vrow_stride;
             double rr[8][4];
 #pragma unroll
             for (int ot = 0; ot < 8; ++ot) {
-                const u32x2 vv = *reinterpret_cast<const u32x2*>(vr + ot * 16 + 4 * g4);
+                const u32x2 vv = v4(row, ot);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t word = vv[i >> 1];
