@@ -102,7 +102,8 @@ typedef struct lowram_decode_args {
     const void    *res_val;     /* [B, Hkv, k, d] (I2: [B, Hkv, k, d/4] bytes; NULL if k == 0) */
     const float   *res_scale;   /* [B, Hkv, k] I8 / I2 residuals only, else NULL    */
     const int32_t *res_blk_ptr; /* [B, Hkv, nb+1] slots of block i: [p[i], p[i+1])  */
-    const int32_t *sel;         /* [B, n_sel] ascending block indices, or NULL      */
+    const int32_t *sel;         /* [B, n_sel] ascending block indices, or NULL;
+                                   entries outside [0, nb) are padding and skipped */
     const uint8_t *keep;        /* [B, nb] 1 = kept, 0 = evicted, or NULL           */
     const void    *win_k;       /* [B, win_cap, Hkv*d] or NULL when win_len == 0    */
     const void    *win_v;       /* [B, win_cap, Hkv*d]                              */

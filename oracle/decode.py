@@ -80,9 +80,11 @@ def attended_blocks(n_tokens, block, sel=None, keep=None):
     explainer, prefill/decode paragraph: only the chunks the current query
     selects are rebuilt; paper page, Abstract: a selected subset per step and
     composition with eviction. Blocks are [i*block, min((i+1)*block, T)).
+    Selection entries outside [0, nb) are padding (a row of a batch that
+    selects fewer blocks than the widest row) and name no block.
     """
     nb = -(-n_tokens // block)
-    cand = range(nb) if sel is None else [int(i) for i in sel]
+    cand = range(nb) if sel is None else [int(i) for i in sel if 0 <= int(i) < nb]
     return [i for i in cand if keep is None or bool(keep[i])]
 
 

@@ -128,6 +128,23 @@ def test_single_block_all_blocks_last_partial_block(generic):
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+@pytest.mark.parametrize("with_keep", [False, True], ids=["direct", "compacted"])
+def test_ragged_selection_rows_padded(generic, with_keep):
+    """Rows of one batch that select different numbers of blocks, padded with
+    -1 and with an out-of-range index; one row is padding only."""
+    cfg = SMALL["bf16_sel"].replace(batch=3)
+    nb = cfg.nb
+    case = make_case(cfg, layer=7)
+    case["sel"] = torch.tensor([[0, 3, 7, nb - 1, -1, -1],
+                                [-1, -1, -1, -1, -1, -1],
+                                [2, 5, nb, -1, 9, -7]], dtype=torch.int32)
+    case["keep"] = torch.ones(3, nb, dtype=torch.uint8) if with_keep else None
+    case["win_len"] = 0
+    out, stats = check(case, cfg, generic=generic)
+    assert not out[1].float().abs().sum().item() and stats[1].abs().sum().item() == 0
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
 def test_window_lengths(generic):
     cfg = SMALL["bf16_r1024_sel"]
     case = make_case(cfg, layer=4)

@@ -336,6 +336,13 @@ def test_selection_invariants():
     np.testing.assert_allclose(a1, a2, rtol=1e-13, atol=1e-14)
     a3, _ = oracle.decode_batch_element(*args, keep=np.array([1, 0, 1, 0, 1], np.uint8), **kw)
     np.testing.assert_allclose(a1, a3, rtol=0, atol=0)
+    # Padding entries (outside [0, nb)) in a selection row name no block.
+    a4, s4 = oracle.decode_batch_element(*args, sel=[-1, 0, 2, 4, 5, 99], **kw)
+    _, s1 = oracle.decode_batch_element(*args, sel=[0, 2, 4], **kw)
+    np.testing.assert_array_equal(a1, a4)
+    assert s4.tolist() == s1.tolist()
+    a5, s5 = oracle.decode_batch_element(*args, sel=[-1, -1], **kw)
+    assert not a5.any() and not s5.any()
 
 
 def test_split_softmax_merge_equals_single_pass():
