@@ -12,8 +12,9 @@
 //      (bf16 factor) is copied global -> LDS by direct loads one chunk ahead,
 //      into unpadded rows with an XOR swizzle; no registers hold data in
 //      flight, so the next chunk's loads are issued before this chunk's
-//      MFMAs. int8 A rows come straight into registers (exact in bf16) and
-//      their per-row scale multiplies the accumulator column.
+//      MFMAs. int8 A rows take the same copies into two alternating
+//      buffers, are widened to bf16 (exact) after the LDS read, and their
+//      per-row scale multiplies the accumulator column.
 //   2. The accumulators, rounded to bf16, are used in place as the A operand
 //      of the next products (the k-slot order of an MFMA is free as long as
 //      both operands agree, which removes any transpose):
@@ -25,7 +26,8 @@
 //      MFMAs interleave with the previous tile's GELU; weight chunks are
 //      loaded two chunks ahead.
 //   4. Residual rows of the block add P[t] * R to the K W_lin part (bf16 rows
-//      on MFMA 16x16x16 through transposing LDS reads; other codes per row).
+//      on MFMA 16x16x16, int8 rows on MFMA 16x16x32 with the row scale in the
+//      weight, both through transposing LDS reads; fp32 and 2-bit rows per row).
 //   5. The four waves' O are summed in fixed order into one partial record
 //      (m, l, O_G[h], O_V[d]); the combine kernel applies W2 and b2 after the
 //      split merge: sum_t p_t (g_t W2 + b2) = (sum_t p_t g_t) W2 + l b2.
@@ -54,6 +56,8 @@ static_assert(128 * kRowBytes == kStage * 2, "a stage buffer holds one B_l chunk
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2* lds_i32x2_t;
 
 // Two 4-element halves (n .. n+3 and n+16 .. n+19) of a bf16 LDS row.
 __device__ __forceinline__ bf16x8 lds_pair(const __bf16* row, int n) {
@@ -82,26 +86,6 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(u32x2 v) {
 // conflicts on gfx950 (measured: as fast as contiguous reads, where padded
 // 144-byte rows take 1.7x as long).
 __device__ __forceinline__ int swz(int r) { return r & 7; }
-
-// One A-row fragment (8 rank columns of one token) at byte offset `off` of
-// the wave's block, kept raw until the MFMA uses it (bf16 as is, int8 codes
-// widened then); rows past the block's end read as zero.
-template <int ADT> struct AFrag;
-template <> struct AFrag<DT_BF16> {
-    u32x4 v;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    }
-    __device__ __forceinline__ bf16x8 get() const { return as_bf16x8(v); }
-};
-template <> struct AFrag<DT_I8> {
-    u32x2 v;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    }
-    __device__ __forceinline__ bf16x8 get() const { return i8x8_to_bf16(v); }
-};
-
 
 }  // namespace
 
@@ -184,6 +168,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 // conflicts: lane i fills row 4q + i/16, slot i%16.
                 const int r = 4 * q + (lane >> 4), slot = lane & 15;
                 src = (uint32_t)(r * 256 + (((((slot >> 1) ^ (r & 7)) << 1) | (slot & 1)) * 16));
+            } else if constexpr (RDT == DT_I8) {
+                // 128-byte rows; 16-byte piece c of row r sits in slot
+                // c ^ (r & 7): lane i fills row 8q + i/8, slot i%8.
+                const int r = 8 * q + (lane >> 3), slot = lane & 7;
+                src = (uint32_t)(r * 128 + ((slot ^ (r & 7)) * 16));
             }
             dma16(rr, rs_w + q * 1024, src, 0u);
         }
@@ -241,16 +230,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int xs = g4 ^ swz(l16);
     const uint32_t rd_off[2] = {(uint32_t)(l16 * kRowBytes + xs * 16), (uint32_t)(l16 * kRowBytes + (xs ^ 4) * 16)};
 
-    using Frag = AFrag<ADT>;
-    uint32_t a_off[4];          // int8 factor: A fragments straight into registers
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) a_off[tt] = (uint32_t)(((tt * 16 + l16) * R + g4 * 8) * EA);
-    auto load_a = [&](int c, Frag (&af)[2][4]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) af[kk][tt].load(ra, a_off[tt] + (c * kKc + kk * 32) * EA);
-    };
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -341,28 +320,57 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             if (c + 1 < n_chunks) chunk(c + 1, stg1, stg0);
         }
     } else {
-        // int8 factor: A fragments ping-pong in registers, one chunk ahead.
+        // int8 factor: this wave's 64-byte A rows of a rank chunk are copied
+        // global -> LDS like the bf16 rows, into two 4 KB buffers that
+        // alternate by chunk, so the copy of chunk c+1 starts with the chunk's
+        // B_l copy. 16-byte piece c of row r sits in slot c ^ ((r >> 2) & 3),
+        // which keeps the 8-byte fragment reads of 16 consecutive rows free of
+        // bank conflicts. The codes are widened exactly to bf16 after the read.
+        constexpr int kA8Bytes = kBlock * kKc;
+        static_assert(2 * kA8Bytes <= kABytes, "two int8 A buffers per wave");
+        uint32_t a8_src[4];     // instruction q fills rows 16q .. 16q+15: lane i takes row 16q + i/4, slot i%4
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            a8_src[q] = (uint32_t)((16 * q + (lane >> 2)) * R + (((lane & 3) ^ g4) * 16));
+        auto dma_a8 = [&](int c) {
+            const __amdgpu_buffer_rsrc_t ras = c < n_chunks ? ra : rnone;
+            unsigned char* const dst = sa_w + (c & 1) * kA8Bytes;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dma16(ras, dst + q * 1024, a8_src[q], (uint32_t)(c * kKc));
+        };
+        // Fragment (kk, tt): row 16 tt + l16, rank columns 32 kk + 8 g4 .. +7,
+        // i.e. piece 2 kk + g4 / 2, half g4 % 2.
+        uint32_t a8_rd[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            a8_rd[kk] = (uint32_t)(l16 * kKc + (((2 * kk + (g4 >> 1)) ^ (l16 >> 2)) * 16) + 8 * (g4 & 1));
         dma_bl(0, stg0);
-        Frag afA[2][4], afB[2][4];
-        load_a(0, afA);
-        wait_vmcnt<8>();
+        dma_a8(0);
+        wait_vmcnt<4>();       // the residual copy and B_l chunk 0 (issued first) have landed
         barrier_lds();
-        auto chunk = [&](int c, const __bf16* cur, __bf16* nxt, const Frag (&fc)[2][4], Frag (&fn)[2][4]) {
-            const int cn = min(c + 1, n_chunks - 1);   // unconditional; the last chunk reloads itself
-            dma_bl(cn, nxt);
-            load_a(cn, fn);
+        auto chunk = [&](int c, const __bf16* cur, __bf16* nxt) {
+            wait_vmcnt<0>();   // this wave's A rows of chunk c (the only copy in flight)
+            const unsigned char* const ab = sa_w + (c & 1) * kA8Bytes;
+            u32x2 raw[2][4];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    raw[kk][tt] = *reinterpret_cast<const u32x2*>(ab + a8_rd[kk] + tt * 16 * kKc);
+            dma_bl(c + 1, nxt);
+            dma_a8(c + 1);
             bf16x8 a8[2][4];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = fc[kk][tt].get();
+                for (int tt = 0; tt < 4; ++tt) a8[kk][tt] = i8x8_to_bf16(raw[kk][tt]);
             mma_chunk(cur, a8);
-            wait_vmcnt<8>();
+            wait_vmcnt<4>();   // B_l of chunk c+1 (issued before the A copy) has landed
             barrier_lds();
         };
         for (int c = 0; c < n_chunks; c += 2) {
-            chunk(c, stg0, stg1, afA, afB);
-            if (c + 1 < n_chunks) chunk(c + 1, stg1, stg0, afB, afA);
+            chunk(c, stg0, stg1);
+            if (c + 1 < n_chunks) chunk(c + 1, stg1, stg0);
         }
     }
 
@@ -534,7 +542,44 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 rv[ft] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, pb, rv[ft], 0, 0, 0);
             }
         }
+    } else if constexpr (RDT == DT_I8) {
+        // The same product for int8 rows on MFMA 16x16x32, 32 rows a batch,
+        // the row scale folded into the weight: A operand lane (l16, g4)
+        // holds P[l16][t_r] * s_r for rows r = 8 g4 .. 8 g4 + 7; the
+        // transposing byte read gives lane (l16, g4) feature 16 ft + l16 of
+        // those eight rows, widened exactly to bf16.
+        static_assert(kResRows == 32, "one MFMA k-step per batch of int8 rows");
+        for (int q0 = lo; q0 < hi; q0 += kResRows) {
+            if (q0 != lo) {
+                wait_lgkmcnt0();               // this wave's reads of the previous rows are done
+                dma_res(q0);
+            }
+            const int n = min(kResRows, hi - q0);
+            int tok = tok0;
+            float scl = scl0;
+            if (q0 != lo) res_meta(q0, tok, scl);
+            applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
+            bf16x8 pa;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * g4 + i;
+                const int t = __shfl(tok, r, kWave);
+                const float sr = __shfl(scl, r, kWave);
+                const bool ok = r < n && t >= 0 && t < nt && l16 < G;
+                pa[i] = (__bf16)(ok ? pl[w][l16][t] * sr : 0.f);
+            }
+            wait_vmcnt<0>();
+            const int rr = 8 * g4 + (l16 >> 1);
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) {
+                const uint32_t off = (uint32_t)(rr * 128 + ((ft ^ (rr & 7)) * 16) + 8 * (l16 & 1));
+                const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t)(rs_w + off));
+                rv[ft] = mfma(pa, i8x8_to_bf16(u32x2{(unsigned)raw[0], (unsigned)raw[1]}), rv[ft]);
+            }
+        }
     } else {
+        // fp32 and 2-bit rows: per row, on the vector ALUs.
+        static_assert(RDT == DT_F32 || RDT == DT_I2, "bf16 and int8 rows take the MFMA paths");
         for (int q0 = lo; q0 < hi; q0 += kResRows) {
             if (q0 != lo) {
                 wait_lgkmcnt0();               // this wave's reads of the previous rows are done
@@ -566,8 +611,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                     for (int ft = 0; ft < 8; ++ft) {
                         const int f = ft * 16 + l16;
                         if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
-                        else if (RDT == DT_BF16) v[u][ft] = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(rs_w + r * kResRowB + f * 2));
-                        else if (RDT == DT_I8) v[u][ft] = static_cast<float>(*reinterpret_cast<const int8_t*>(rs_w + r * kResRowB + f));
                         else v[u][ft] = static_cast<float>((rs_w[r * kResRowB + (f >> 2)] >> (2 * (f & 3))) & 3u) - 1.5f;
                     }
                 }

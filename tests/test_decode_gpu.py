@@ -84,8 +84,8 @@ def test_no_residuals_and_every_token_a_residual(generic):
 @pytest.mark.parametrize("res", ["bf16", "i8"])
 def test_residual_rows_per_block_around_batch_sizes(res):
     """Blocks holding 1, 15, 16, 17, 33 and 64 residual rows, every block
-    attended: the bf16 path sums rows 16 at a time on the matrix cores, the
-    other codes copy 32 rows at a time."""
+    attended: the fused kernel sums bf16 rows 16 at a time and int8 rows 32 at
+    a time on the matrix cores."""
     base = C2 if res == "bf16" else C5
     cfg = base.replace(ctx_len=64 * 8, batch=2, sel_den=1, evict_half=False, res_dtype=res)
     case = make_case(cfg, layer=0)
@@ -98,11 +98,12 @@ def test_residual_rows_per_block_around_batch_sizes(res):
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
-@pytest.mark.parametrize("name", ["i2_keep", "f32_i2"])
-def test_two_bit_residuals_carry_the_output(name, generic):
-    """Every token holds a 2-bit residual of about the values' size, so the
-    output moves by far more than the tolerance if a code is decoded from the
-    wrong bits, with the wrong level offset or without its scale."""
+@pytest.mark.parametrize("name", ["i2_keep", "f32_i2", "i8_keep"])
+def test_quantised_residuals_carry_the_output(name, generic):
+    """Every token holds a 2-bit or int8 residual of about the values' size,
+    so the output moves by far more than the tolerance if a code is decoded
+    from the wrong bits or row, with the wrong level offset or without its
+    scale."""
     cfg = SMALL[name]
     case = make_case(cfg, layer=7)
     bsz = case["q"].shape[0]
