@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 const int r = 8 * q + (lane >> 3), slot = lane & 7;
                 src = (uint32_t)(r * 128 + ((slot ^ (r & 7)) * 16));
             }
-            dma16(rr, rs_w + q * 1024, src, 0u);
+            dma16<kNonTemporal>(rr, rs_w + q * 1024, src, 0u);
         }
     };
     // Token (relative to the block) and int8 scale of residual row q0 + lane.

@@ -59,8 +59,11 @@ __device__ __forceinline__ void barrier_lds() {
 // Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // lds + 16 i (in lane order), read from byte voff + soff of the buffer;
 // reads past the buffer's end produce zeros.
+// POLICY is the load's cache-policy field; kNonTemporal marks data read once.
+constexpr int kNonTemporal = 2;
+template <int POLICY = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, POLICY);
 }
 
 // Read of one 16-byte LDS piece at byte offset `off` of `base`.

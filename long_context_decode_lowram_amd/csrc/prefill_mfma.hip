@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
             const int row = 4 * q + (lane >> 4);
             const int t = __shfl(my_tok, row, kWave);
             const uint32_t pc = (uint32_t)(((lane & 15) ^ (row & 15)) * 16);
-            dma16(rv, sv_w + q * 1024, t >= 0 ? (uint32_t)((int64_t)t * vrow_stride * 2) + pc : kOob, 0u);
+            dma16<kNonTemporal>(rv, sv_w + q * 1024, t >= 0 ? (uint32_t)((int64_t)t * vrow_stride * 2) + pc : kOob, 0u);
         }
     }
     // The V copies are older than the first step's: its wait covers them too.
