@@ -26,8 +26,9 @@
 //      MFMAs interleave with the previous tile's GELU; weight chunks are
 //      loaded two chunks ahead.
 //   4. Residual rows of the block add P[t] * R to the K W_lin part (bf16 rows
-//      on MFMA 16x16x16, int8 rows on MFMA 16x16x32 with the row scale in the
-//      weight, both through transposing LDS reads; fp32 and 2-bit rows per row).
+//      on MFMA 16x16x16, int8 and 2-bit rows on MFMA 16x16x32 with the row
+//      scale in the weight, all through transposing LDS reads; fp32 rows per
+//      row).
 //   5. The four waves' O are summed in fixed order into one partial record
 //      (m, l, O_G[h], O_V[d]); the combine kernel applies W2 and b2 after the
 //      split merge: sum_t p_t (g_t W2 + b2) = (sum_t p_t g_t) W2 + l b2.
@@ -173,6 +174,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 // c ^ (r & 7): lane i fills row 8q + i/8, slot i%8.
                 const int r = 8 * q + (lane >> 3), slot = lane & 7;
                 src = (uint32_t)(r * 128 + ((slot ^ (r & 7)) * 16));
+            } else if constexpr (RDT == DT_I2) {
+                // 32-byte rows; 16-byte half c of row r sits in slot
+                // c ^ ((r >> 3) & 1): lane i fills row 32q + i/2, slot i%2.
+                const int r = 32 * q + (lane >> 1), slot = lane & 1;
+                src = (uint32_t)(r * 32 + ((slot ^ ((r >> 3) & 1)) * 16));
             }
             dma16<kNonTemporal>(rr, rs_w + q * 1024, src, 0u);
         }
@@ -577,9 +583,69 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
                 rv[ft] = mfma(pa, i8x8_to_bf16(u32x2{(unsigned)raw[0], (unsigned)raw[1]}), rv[ft]);
             }
         }
+    } else if constexpr (RDT == DT_I2) {
+        // 2-bit rows on MFMA 16x16x32: 64 rows a batch, 32 a k-step. The
+        // byte-transposing read gives lane (l16, g4) byte column 16 bt + l16
+        // of rows 8 g4 .. 8 g4 + 7; that byte holds the codes of features
+        // 4 (16 bt + l16) + c, c = 0..3, in bits 2c. One byte permute per two
+        // codes q makes the bf16 bit patterns 0x4300 | q, i.e. the values
+        // 128 + q exactly. The level is q - 1.5, so the weighted sum is
+        // sum_r w_r (128 + q_r) + sum_r w_r (-128) + sum_r w_r (-1.5), the two
+        // constant terms taken on the same MFMA (-128 and -1.5 are exact in
+        // bf16) and added once at the end. The weight w_r = P[j][t_r] s_r as
+        // for int8. Output tile 4 bt + c holds feature 4 (16 bt + l16) + c.
+        static_assert(kResRows == 64, "two MFMA k-steps per batch of 2-bit rows");
+        bf16x8 cm128, cm15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { cm128[i] = (__bf16)(-128.f); cm15[i] = (__bf16)(-1.5f); }
+        f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = lo; q0 < hi; q0 += kResRows) {
+            if (q0 != lo) {
+                wait_lgkmcnt0();               // this wave's reads of the previous rows are done
+                dma_res(q0);
+            }
+            const int n = min(kResRows, hi - q0);
+            int tok = tok0;
+            float scl = scl0;
+            if (q0 != lo) res_meta(q0, tok, scl);
+            applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
+            wait_vmcnt<0>();
+            for (int ks = 0; ks * 32 < n; ++ks) {
+                bf16x8 pa;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 32 * ks + 8 * g4 + i;
+                    const int t = __shfl(tok, r, kWave);
+                    const float sr = __shfl(scl, r, kWave);
+                    const bool ok = r < n && t >= 0 && t < nt && l16 < G;
+                    pa[i] = (__bf16)(ok ? pl[w][l16][t] * sr : 0.f);
+                }
+                corr = mfma(pa, cm128, corr);
+                corr = mfma(pa, cm15, corr);
+                const int rr = 32 * ks + 8 * g4 + (l16 >> 1);
+#pragma unroll
+                for (int bt = 0; bt < 2; ++bt) {
+                    const uint32_t off = (uint32_t)(rr * 32 + ((bt ^ (g4 & 1)) * 16) + 8 * (l16 & 1));
+                    const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t)(rs_w + off));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t x0 = ((uint32_t)raw[0] >> (2 * c)) & 0x03030303u;
+                        const uint32_t x1 = ((uint32_t)raw[1] >> (2 * c)) & 0x03030303u;
+                        u32x4 bv;
+                        bv[0] = __builtin_amdgcn_perm(0x43434343u, x0, 0x04010400u);
+                        bv[1] = __builtin_amdgcn_perm(0x43434343u, x0, 0x04030402u);
+                        bv[2] = __builtin_amdgcn_perm(0x43434343u, x1, 0x04010400u);
+                        bv[3] = __builtin_amdgcn_perm(0x43434343u, x1, 0x04030402u);
+                        rv[4 * bt + c] = mfma(pa, as_bf16x8(bv), rv[4 * bt + c]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ft = 0; ft < 8; ++ft) rv[ft] += corr;
     } else {
-        // fp32 and 2-bit rows: per row, on the vector ALUs.
-        static_assert(RDT == DT_F32 || RDT == DT_I2, "bf16 and int8 rows take the MFMA paths");
+        // fp32 rows: per row, on the vector ALUs.
+        static_assert(RDT == DT_F32, "bf16, int8 and 2-bit rows take the MFMA paths");
         for (int q0 = lo; q0 < hi; q0 += kResRows) {
             if (q0 != lo) {
                 wait_lgkmcnt0();               // this wave's reads of the previous rows are done
@@ -610,8 +676,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     #pragma unroll
                     for (int ft = 0; ft < 8; ++ft) {
                         const int f = ft * 16 + l16;
-                        if (RDT == DT_F32) v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
-                        else v[u][ft] = static_cast<float>((rs_w[r * kResRowB + (f >> 2)] >> (2 * (f & 3))) & 3u) - 1.5f;
+                        v[u][ft] = *reinterpret_cast<const float*>(rs_w + r * kResRowB + f * 4);
                     }
                 }
     #pragma unroll
@@ -633,7 +698,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
         const int j = 4 * g4 + i;
         if (j < G) {
 #pragma unroll
-            for (int ft = 0; ft < 8; ++ft) resS[w][j][ft * 16 + l16] = rv[ft][i];
+            for (int ft = 0; ft < 8; ++ft)   // 2-bit rows: tile ft holds feature 4 (16 (ft / 4) + l16) + ft % 4
+                resS[w][j][RDT == DT_I2 ? 64 * (ft >> 2) + 4 * l16 + (ft & 3) : ft * 16 + l16] = rv[ft][i];
         }
     }
     // Weight chunks go global -> registers -> LDS, loaded two chunks ahead:

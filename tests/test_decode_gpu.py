@@ -81,11 +81,11 @@ def test_no_residuals_and_every_token_a_residual(generic):
         check(case, cfg, generic=generic)
 
 
-@pytest.mark.parametrize("res", ["bf16", "i8"])
+@pytest.mark.parametrize("res", ["bf16", "i8", "i2"])
 def test_residual_rows_per_block_around_batch_sizes(res):
     """Blocks holding 1, 15, 16, 17, 33 and 64 residual rows, every block
-    attended: the fused kernel sums bf16 rows 16 at a time and int8 rows 32 at
-    a time on the matrix cores."""
+    attended: the fused kernel sums bf16 rows 16 at a time, int8 rows 32 at a
+    time and 2-bit rows 64 at a time (two steps of 32) on the matrix cores."""
     base = C2 if res == "bf16" else C5
     cfg = base.replace(ctx_len=64 * 8, batch=2, sel_den=1, evict_half=False, res_dtype=res)
     case = make_case(cfg, layer=0)
