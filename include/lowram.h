@@ -122,7 +122,9 @@ typedef struct lowram_decode_args {
  * A sequence with nothing to attend (its blocks all evicted and no window)
  * gets a zero output row and zero stats; LOWRAM_ERR_EMPTY is returned only
  * when the host can see that every sequence is empty (ctx_len == 0 or
- * n_sel == 0, and win_len == 0). */
+ * n_sel == 0, and win_len == 0). The call only launches kernels (and
+ * records the optional events), so it may be captured into a HIP graph;
+ * replays read the argument buffers as they are at replay time. */
 int lowram_decode_step(const lowram_decode_args *args, void *stream);
 
 /* Bytes of workspace lowram_decode_step needs for these shapes; 0 when the
