@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--generic", action="store_true", help="force the fp32 SIMT kernel")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step as eager launches instead of replays of a HIP graph of it")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run each layer's combine on a second stream, beside the next layer's fused kernel")
     ap.add_argument("--res-dtype", choices=("f32", "bf16", "i8", "i2"), default=None,
                     help="store the workload's residuals in this encoding instead")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -63,11 +65,26 @@ class HipEvents:
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
 
     def create(self):
         e = ctypes.c_void_p()
         assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def create_sync(self):
+        """An event for ordering only (hipEventDisableTiming)."""
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 2) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream)) == 0
+
+    def wait(self, stream, e):
+        assert self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(e), 0) == 0
 
     def elapsed_ms(self, a, b):
         f = ctypes.c_float()
@@ -201,9 +218,13 @@ def main():
                                         b2=x["b2"], res_scale=x["res_scale"], sel=x["sel"], keep=x["keep"],
                                         win_k=wk, win_v=wv, win_len=win, generic=args.generic))
     ws_bytes = max(L.decode_workspace_size(c) for c in calls)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    for c in calls:
-        c.workspace, c.workspace_bytes = ws.data_ptr(), ws_bytes
+    # Two workspaces, alternating by layer: each layer's combine runs on a
+    # second stream and overlaps the next layer's fused kernel, which writes
+    # the other workspace; layer l+2 waits for layer l's combine.
+    overlap = args.overlap
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(2 if overlap else 1)]
+    for l, c in enumerate(calls):
+        c.workspace, c.workspace_bytes = wss[l % len(wss)].data_ptr(), ws_bytes
 
     counts = [attended_counts(x, cfg) for x in layers]
     step_bytes = step_flops = step_flops_direct = 0
@@ -215,14 +236,28 @@ def main():
     stream = torch.cuda.current_stream()
     n_ev = args.steps * cfg.n_layers
     evs = [(ev.create(), ev.create()) for _ in range(n_ev)]
+    cstream = torch.cuda.Stream() if overlap else None
+    ready = [ev.create_sync() for _ in calls] if overlap else []
+    done = [ev.create_sync() for _ in calls] if overlap else []
+    for l, c in enumerate(calls):
+        if overlap:
+            c.combine_stream, c.combine_ready = cstream.cuda_stream, ready[l]
 
     def step(timed_index=None, s=None):
+        ms_ = stream if s is None else s
         for l, c in enumerate(calls):
             if timed_index is not None:
                 c.ev_main_begin, c.ev_main_end = evs[timed_index * cfg.n_layers + l]
             else:
                 c.ev_main_begin = c.ev_main_end = None
-            L.decode_launch(c, stream if s is None else s)
+            if overlap and l >= 2:
+                ev.wait(ms_, done[l - 2])            # layer l-2's combine has released this workspace
+            L.decode_launch(c, ms_)
+            if overlap:
+                ev.record(done[l], cstream)
+        if overlap:
+            for l in range(max(0, len(calls) - 2), len(calls)):
+                ev.wait(ms_, done[l])                # join: the step ends with every combine
 
     for _ in range(args.warmup):
         step()
@@ -273,7 +308,8 @@ def main():
         "value": cached / (ms * 1e-3),
         "unit": "cached tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "timing": "HIP graph replays of the step" if not args.no_graph else "eager launches",
+        "timing": ("HIP graph replays of the step" if not args.no_graph else "eager launches") +
+                  ("; each layer's combine overlaps the next layer's fused kernel" if overlap else ""),
         "eager_ms_per_step": eager_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if cfg.act == "f32" else ("bf16+i8" if cfg.a_dtype == "i8" else "bf16"),

@@ -116,6 +116,10 @@ typedef struct lowram_decode_args {
 
     void          *ev_main_begin; /* optional hipEvent_t recorded right before and  */
     void          *ev_main_end;   /* after the fused reconstruct+attend kernel       */
+
+    void          *combine_stream; /* optional hipStream_t for the split-K combine,
+                                      or NULL (the combine follows on `stream`)      */
+    void          *combine_ready;  /* hipEvent_t, required with combine_stream      */
 } lowram_decode_args;
 
 /* Enqueue one layer's decode step. Returns LOWRAM_OK or a negative status.
@@ -124,7 +128,15 @@ typedef struct lowram_decode_args {
  * when the host can see that every sequence is empty (ctx_len == 0 or
  * n_sel == 0, and win_len == 0). The call only launches kernels (and
  * records the optional events), so it may be captured into a HIP graph;
- * replays read the argument buffers as they are at replay time. */
+ * replays read the argument buffers as they are at replay time.
+ *
+ * With combine_stream set, the call records combine_ready on `stream` after
+ * the fused kernel, makes combine_stream wait for it and runs the split-K
+ * combine (which reads the workspace and writes out and stats) there, so
+ * that it can overlap the caller's next work on `stream`. The caller then
+ * orders on combine_stream whatever reuses this workspace or reads out or
+ * stats (for example the next layer's call with the same workspace); a
+ * next call with another workspace may run on `stream` at once. */
 int lowram_decode_step(const lowram_decode_args *args, void *stream);
 
 /* Bytes of workspace lowram_decode_step needs for these shapes; 0 when the

@@ -32,7 +32,8 @@ class DecodeArgs(ctypes.Structure):
         (n, _p) for n in (
         "q", "a", "a_scale", "b_l", "w_lin", "w1", "b1", "w2", "b2", "res_idx", "res_val", "res_scale",
         "res_blk_ptr", "sel", "keep", "win_k", "win_v", "out", "stats", "workspace")] + [
-        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p)]
+        ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p),
+        ("combine_stream", _p), ("combine_ready", _p)]
 
 
 class RankArgs(ctypes.Structure):

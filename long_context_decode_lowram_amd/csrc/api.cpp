@@ -87,6 +87,7 @@ int check_decode_ptrs(const lowram_decode_args* a, const DecodePlan& pl) {
     if ((a->res_dtype == LOWRAM_I8 || a->res_dtype == LOWRAM_I2) && a->n_res > 0 && !a->res_scale)
         return fail(LOWRAM_ERR_ARG, "int8 and 2-bit residuals need res_scale");
     if (a->win_len > 0 && (!a->win_k || !a->win_v)) return fail(LOWRAM_ERR_ARG, "win_k and win_v must be non-NULL when win_len > 0");
+    if (a->combine_stream && !a->combine_ready) return fail(LOWRAM_ERR_ARG, "combine_stream needs combine_ready");
     const void* v16[] = {a->q, a->a, a->b_l, a->w_lin, a->w1, a->w2, a->res_val, a->win_k, a->win_v, a->out, a->workspace};
     for (const void* p : v16)
         if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
@@ -336,7 +337,15 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
         e = hipEventRecord(static_cast<hipEvent_t>(a->ev_main_end), s);
         if (e != hipSuccess) return hip_fail(e, "event record");
     }
-    e = launch_combine(p, a->act_dtype, s);
+    hipStream_t cs = s;
+    if (a->combine_stream) {
+        cs = static_cast<hipStream_t>(a->combine_stream);
+        e = hipEventRecord(static_cast<hipEvent_t>(a->combine_ready), s);
+        if (e != hipSuccess) return hip_fail(e, "event record");
+        e = hipStreamWaitEvent(cs, static_cast<hipEvent_t>(a->combine_ready), 0);
+        if (e != hipSuccess) return hip_fail(e, "stream wait");
+    }
+    e = launch_combine(p, a->act_dtype, cs);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return LOWRAM_OK;
 }

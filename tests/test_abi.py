@@ -102,6 +102,7 @@ def test_decode_valid_args_stop_at_workspace():
     ("res_dtype", B.I8, B.ERR_ARG),             # int8 residuals without res_scale
     ("res_dtype", B.I2, B.ERR_ARG),             # 2-bit residuals without res_scale
     ("res_dtype", 4, B.ERR_ARG),
+    ("combine_stream", FAKE, B.ERR_ARG),        # a combine stream without its event
 ])
 def test_decode_rejects(field, value, status):
     a = valid_decode()

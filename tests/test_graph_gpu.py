@@ -83,3 +83,86 @@ def test_graph_of_layer_calls_replays_the_eager_results():
         for (o, s), (eo, es) in zip(zip(outs, stats), eager):
             assert torch.equal(o, eo), f"replay {rep}: output differs"
             assert torch.equal(s, es), f"replay {rep}: stats differ"
+
+
+class _Ev:
+    """Ordering-only hipEvent_t handles and stream waits through the HIP runtime."""
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+
+    def create(self):
+        e = self.c.c_void_p()
+        assert self.lib.hipEventCreateWithFlags(self.c.byref(e), 2) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(self.c.c_void_p(e), self.c.c_void_p(stream.cuda_stream)) == 0
+
+    def wait(self, stream, e):
+        assert self.lib.hipStreamWaitEvent(self.c.c_void_p(stream.cuda_stream), self.c.c_void_p(e), 0) == 0
+
+
+def test_combine_on_a_second_stream_overlapping_the_next_call():
+    """Layer calls with the combine on a second stream and two workspaces
+    used in turn (call l+2 waits for call l's combine), eagerly and as a
+    graph replayed between eager work, give the single-stream outputs bit for
+    bit."""
+    cfgs = [C2.replace(ctx_len=64 * 40 + 9, batch=2, seed=s) for s in range(3)] + \
+           [C5.replace(ctx_len=64 * 48 + 5, batch=3), C2.replace(ctx_len=64 * 40 + 9, batch=2, res_dtype="i2")]
+    cases, calls, outs, stats, ws = _calls(cfgs)
+    for a in calls:
+        L.decode_launch(a)
+    torch.cuda.synchronize()
+    eager = [(o.clone(), s.clone()) for o, s in zip(outs, stats)]
+
+    ev = _Ev()
+    ws2 = torch.empty_like(ws)
+    cs = torch.cuda.Stream()
+    ready = [ev.create() for _ in calls]
+    done = [ev.create() for _ in calls]
+    for l, a in enumerate(calls):
+        a.workspace = (ws if l % 2 == 0 else ws2).data_ptr()
+        a.combine_stream, a.combine_ready = cs.cuda_stream, ready[l]
+
+    def step(main):
+        for l, a in enumerate(calls):
+            if l >= 2:
+                ev.wait(main, done[l - 2])
+            L.decode_launch(a, main)
+            ev.record(done[l], cs)
+        for l in range(len(calls) - 2, len(calls)):
+            ev.wait(main, done[l])
+
+    def clear():
+        for o, s in zip(outs, stats):
+            o.fill_(float("nan"))
+            s.fill_(-9)
+        torch.cuda.synchronize()
+
+    def check(what):
+        for (o, s), (eo, es) in zip(zip(outs, stats), eager):
+            assert torch.equal(o, eo), f"{what}: output differs"
+            assert torch.equal(s, es), f"{what}: stats differ"
+
+    clear()
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    check("eager, two streams")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(4):
+        clear()
+        g.replay()
+        x = torch.randn(1 << 20, device="cuda")
+        _ = (x * 2).sum()
+        torch.cuda.synchronize()
+        check(f"replay {rep}")
