@@ -179,3 +179,25 @@ def test_c1_full_config_four_layers():
     for layer in range(C1.n_layers):
         case = make_case(C1, layer=layer, biases=False)
         check(case, C1, generic=False)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_randomised_shapes_and_encodings(seed):
+    """Seeded draws over the step's options, several at once: A bf16 or int8;
+    residuals bf16, int8 or 2-bit at 0-50% of the tokens; 1, 2 or 4 KV heads
+    with 1-8 query heads each; ragged context; rank 64-512; hidden 64-256;
+    every block or a selection; eviction flags; a window. Seeds 6 and 7 force
+    the fp32 SIMT kernel on the same kind of draw."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    win_cap = int(rng.choice([0, 64]))
+    cfg = C2.replace(ctx_len=int(rng.integers(64 * 6, 64 * 40)), batch=int(rng.integers(1, 4)),
+                     n_kv_heads=hkv, n_q_heads=hkv * int(rng.choice([1, 2, 3, 4, 8])),
+                     rank=int(rng.choice([64, 128, 256, 512])), mlp_hidden=int(rng.choice([64, 128, 256])),
+                     sel_den=int(rng.choice([1, 2, 4])), evict_half=bool(rng.integers(0, 2)),
+                     a_dtype=str(rng.choice(["bf16", "i8"])), res_dtype=str(rng.choice(["bf16", "i8", "i2"])),
+                     res_frac=(int(rng.integers(0, 6)), 10), win_cap=win_cap, seed=seed)
+    print(cfg, flush=True)
+    case = make_case(cfg, layer=int(rng.integers(0, 4)),
+                     win_len=int(rng.integers(1, win_cap + 1)) if win_cap else 0)
+    check(case, cfg, generic=seed >= 6)
