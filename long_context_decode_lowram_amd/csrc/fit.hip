@@ -331,7 +331,9 @@ __global__ __launch_bounds__(256, 1) void fit_tn_kernel(FitParams p) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             dma16(ra, stage + (w * 8 + c * 4) * kTRowB, va[c], sa);
-            dma16(rb, stage + kTOp + (w * 8 + c * 4) * kTRowB, vb[c], sb);
+            // B (H or K rows) is read by one workgroup only: non-temporal.
+            // A (G or dZ rows) is shared by the two output tiles' workgroups.
+            dma16<kNonTemporal>(rb, stage + kTOp + (w * 8 + c * 4) * kTRowB, vb[c], sb);
         }
     };
     const int g = lane >> 4, i16 = lane & 15;
