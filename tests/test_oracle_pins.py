@@ -199,7 +199,7 @@ def _brute_decode(q, a, a_scale, bl, w_lin, w1, b1, w2, b2, idx, rv, rs, sel, ke
     n_kv = len(bl) // d
     g = n_q // n_kv
     nb = (n_tok + blk - 1) // blk
-    blocks = list(range(nb)) if sel is None else list(sel)
+    blocks = list(range(nb)) if sel is None else [i for i in sel if 0 <= i < nb]
     blocks = [i for i in blocks if keep is None or keep[i]]
     tau = [t for i in blocks for t in range(i * blk, min(i * blk + blk, n_tok))]
     out = [[0.0] * d for _ in range(n_q)]
@@ -320,6 +320,63 @@ def test_brute_force_two_bit_residuals():
         wk.tolist(), wv.tolist(), 64)
     np.testing.assert_allclose(got, np.array(ref), rtol=1e-11, atol=1e-12)
     assert gstats.tolist() == rstats
+
+
+@pytest.mark.parametrize("enc", ["float", "int8", "i2"])
+def test_decode_step_routes_every_sequence(enc):
+    """decode_step over a batch of three sequences, each with its own query,
+    factor A (and int8 row scales), B_l, predictor, residual set and scales,
+    padded selection row, eviction row and window rows, the window buffers
+    holding more rows than win_len. Every sequence must equal the scalar brute
+    force on that sequence's own data and exactly its first win_len window
+    rows (explainer, mechanism paragraph; prefill/decode paragraph: the recent
+    tokens are stored exactly)."""
+    rng = np.random.default_rng(11 + len(enc))
+    n_b, n_tok, win_cap, win_len = 3, 200, 6, 4
+    cases = [_tiny_case(rng, n_tok, int8_a=enc == "int8", int8_r=enc == "int8") for _ in range(n_b)]
+    n_kv, d = cases[0]["w_lin"].shape[:2]
+    k = cases[0]["idx"].shape[1]
+    if enc == "i2":
+        for c in cases:
+            c["rv"] = rng.integers(0, 256, (n_kv, k, d // 4)).astype(np.uint8)
+            c["rs"] = rng.uniform(0.05, 0.2, (n_kv, k)).astype(np.float32)
+    sels = [[0, 2, 3, -1], [1, 3, -1, -1], [0, 1, 2, 3]]
+    keeps = [np.array([1, 1, 1, 1], np.uint8), np.array([1, 1, 1, 1], np.uint8), np.array([1, 0, 1, 1], np.uint8)]
+    wk = rng.standard_normal((n_b, win_cap, n_kv * d))
+    wv = rng.standard_normal((n_b, win_cap, n_kv * d))
+    batch = {name: np.stack([c[src] for c in cases]) for name, src in
+             (("q", "q"), ("a", "a"), ("bl", "bl"), ("w_lin", "w_lin"), ("w1", "w1"), ("w2", "w2"),
+              ("b1", "b1"), ("b2", "b2"), ("res_idx", "idx"), ("res_val", "rv"))}
+    if enc == "int8":
+        batch["a_scale"] = np.stack([c["a_scale"] for c in cases])
+    if enc != "float":
+        batch["res_scale"] = np.stack([c["rs"] for c in cases])
+    batch.update(sel=np.array(sels, np.int32), keep=np.stack(keeps), win_k=wk, win_v=wv, win_len=win_len, block=64)
+    tl = lambda x: None if x is None else np.asarray(x, np.float64).tolist()  # noqa: E731
+
+    def rows(c):
+        # 2-bit codes read with plain bit operations: element o in bits
+        # 2(o mod 4) of byte o // 4, level q - 1.5.
+        if enc != "i2":
+            return tl(c["rv"])
+        return [[[((int(c["rv"][h, p, o // 4]) >> (2 * (o % 4))) & 3) - 1.5 for o in range(d)]
+                 for p in range(k)] for h in range(n_kv)]
+
+    def brute(b, n_win):
+        c = cases[b]
+        return _brute_decode(
+            tl(c["q"]), tl(c["a"]), tl(c["a_scale"]), tl(c["bl"]), tl(c["w_lin"]), tl(c["w1"]), tl(c["b1"]),
+            tl(c["w2"]), tl(c["b2"]), c["idx"].tolist(), rows(c), tl(c["rs"]), sels[b], list(keeps[b]),
+            wk[b, :n_win].tolist(), wv[b, :n_win].tolist(), 64)
+
+    for n_win in (win_len, 0):
+        batch["win_len"] = n_win
+        got, gstats = oracle.decode_step(batch)
+        assert got.shape == (n_b, cases[0]["q"].shape[0], d)
+        for b in range(n_b):
+            ref, rstats = brute(b, n_win)
+            np.testing.assert_allclose(got[b], np.array(ref), rtol=1e-11, atol=1e-12)
+            assert gstats[b].tolist() == rstats
 
 
 # ------------------------------------------------------------ invariants
