@@ -54,7 +54,18 @@ extern "C" {
 #define LOWRAM_I2   3
 
 /* Flags for lowram_decode_args.flags. */
-#define LOWRAM_FLAG_GENERIC 1  /* use the fp32 SIMT kernel even where the MFMA kernel applies */
+#define LOWRAM_FLAG_GENERIC  1  /* use the fp32 SIMT kernel even where the MFMA kernel applies */
+#define LOWRAM_FLAG_VALIDATE 2  /* check the device-side index data first; defects set bits of
+                                   *check_flags (LOWRAM_CHECK_*), the step still runs, guarded */
+
+/* Bits that the validate mode ORs into *check_flags. The library only sets
+ * bits: the caller clears the word (e.g. with a fill kernel) before the call
+ * and reads it once the stream has passed the call. */
+#define LOWRAM_CHECK_SEL_ORDER  1   /* sel: the in-range entries of a row are not strictly ascending */
+#define LOWRAM_CHECK_RES_RANGE  2   /* res_idx: an entry outside [0, ctx_len)                        */
+#define LOWRAM_CHECK_RES_ORDER  4   /* res_idx: a row is not strictly ascending                     */
+#define LOWRAM_CHECK_RES_PTR    8   /* res_blk_ptr: not the block CSR of res_idx                    */
+#define LOWRAM_CHECK_WIN_LEN   16   /* *win_len_dev outside [0, win_len]                            */
 
 /*
  * One layer's decode step for a batch (explainer, prefill/decode paragraph:
@@ -120,6 +131,14 @@ typedef struct lowram_decode_args {
     void          *combine_stream; /* optional hipStream_t for the split-K combine,
                                       or NULL (the combine follows on `stream`)      */
     void          *combine_ready;  /* hipEvent_t, required with combine_stream      */
+
+    const int32_t *win_len_dev;    /* optional: one int32 in device memory holding the
+                                      number of window tokens to attend, read when the
+                                      kernels run (so one captured graph serves a
+                                      growing window); win_len is then its upper bound
+                                      and values outside [0, win_len] are clamped.
+                                      NULL: win_len itself is attended.              */
+    uint32_t      *check_flags;    /* device word for LOWRAM_FLAG_VALIDATE, else NULL */
 } lowram_decode_args;
 
 /* Enqueue one layer's decode step. Returns LOWRAM_OK or a negative status.
@@ -142,6 +161,56 @@ int lowram_decode_step(const lowram_decode_args *args, void *stream);
 /* Bytes of workspace lowram_decode_step needs for these shapes; 0 when the
  * arguments are invalid (see lowram_last_error). */
 size_t lowram_decode_workspace_size(const lowram_decode_args *args);
+
+/*
+ * Validate mode (flags & LOWRAM_FLAG_VALIDATE, check_flags non-NULL). Before
+ * the step's kernels, one more kernel reads the device-side index data the
+ * host cannot see and ORs a LOWRAM_CHECK_* bit into *check_flags for every
+ * kind of defect it finds:
+ *   - a row of sel whose in-range entries are not strictly ascending
+ *     (padding entries outside [0, nb) are allowed anywhere);
+ *   - a res_idx entry outside [0, ctx_len), or a (b, h) row of res_idx that
+ *     is not strictly ascending;
+ *   - a res_blk_ptr row that is not the block CSR of its res_idx row
+ *     (ptr[0] = 0, ptr[nb] = n_res, non-decreasing, and every slot s lies in
+ *     [ptr[i], ptr[i+1]) for the block i = res_idx[s] / 64 of its token);
+ *   - *win_len_dev outside [0, win_len].
+ * The step itself runs as usual: its kernels are bounds-guarded and never
+ * read outside the documented shapes, so a defect gives a wrong output
+ * (e.g. residuals outside their block are skipped), not a fault. The check
+ * costs one pass over the indices (about 1 MB per call at 131072 tokens);
+ * the call neither synchronises nor reads the word back.
+ */
+
+/*
+ * Window append (explainer, prefill/decode paragraph: newly generated tokens
+ * are kept exactly, uncompressed). For each of n_layers recent-window
+ * buffers and each sequence b, writes the step's new key and value rows
+ *   win_k[l, b, pos_l, :] = new_k[l, b, :],  win_v[l, b, pos_l, :] = new_v[l, b, :]
+ * at pos_l = win_len_dev[l], then sets win_len_dev[l] = pos_l + 1, so a
+ * decode call that follows on the stream with that counter as its
+ * win_len_dev attends the token. A buffer that is full (pos_l outside
+ * [0, win_cap)) is left as it is, counter included. One launch, no
+ * allocation and no synchronisation: it may be captured into a HIP graph
+ * with the decode calls, and each replay appends at the counter's current
+ * value. Layer l's buffers win_k[l], win_v[l] are what its decode call
+ * takes as win_k, win_v.
+ * Shapes: new_k, new_v [n_layers, B, width] (width = n_kv_heads * head_dim,
+ * a multiple of 8) and win_k, win_v [n_layers, B, win_cap, width] in
+ * act_dtype; win_len_dev int32 [n_layers]. Pointers 16-byte aligned
+ * (win_len_dev 4).
+ */
+typedef struct lowram_window_args {
+    int32_t n_layers, batch, width, win_cap;
+    int32_t act_dtype;          /* F32 | BF16                                         */
+    const void *new_k;          /* [n_layers, B, width]                               */
+    const void *new_v;          /* [n_layers, B, width]                               */
+    void       *win_k;          /* [n_layers, B, win_cap, width]                      */
+    void       *win_v;          /* [n_layers, B, win_cap, width]                      */
+    int32_t    *win_len_dev;    /* [n_layers] in/out fill counts                      */
+} lowram_window_args;
+
+int lowram_window_append(const lowram_window_args *args, void *stream);
 
 /*
  * Prefill-side residual ranking (paper page, Abstract: residuals for the
@@ -202,7 +271,8 @@ size_t lowram_rank_workspace_size(const lowram_rank_args *args);
  * same instructions, so R uses bit-for-bit the V_hat that was ranked; pass a
  * v_hat buffer to receive that fp32 V_hat for every token.
  * Requirements: head_dim 128, block_size 64, rank % 64 == 0, mlp_hidden % 64
- * == 0, act_dtype BF16, T * rank * 2 < 2^31. All tensors caller-owned device
+ * == 0, act_dtype BF16, T * rank * 2 < 2^31 and T * n_kv_heads * head_dim * 2
+ * < 2^31 (32-bit buffer offsets into A and V). All tensors caller-owned device
  * memory, 16-byte aligned (err 8, index/scale 4).
  */
 typedef struct lowram_prefill_args {

@@ -10,16 +10,20 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowram.so")
+# LOWRAM_LIBRARY names another build of the same library (the host-sanitizer
+# build that the ABI tests run against); by default the in-tree one.
+_LIB_PATH = os.environ.get("LOWRAM_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblowram.so")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_WINDOW_FULL, ERR_EMPTY, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 F32, BF16, I8, I2 = 0, 1, 2, 3
-FLAG_GENERIC = 1
+FLAG_GENERIC, FLAG_VALIDATE = 1, 2
+CHECK_SEL_ORDER, CHECK_RES_RANGE, CHECK_RES_ORDER, CHECK_RES_PTR, CHECK_WIN_LEN = 1, 2, 4, 8, 16
 BLOCK = 64
 
 # uint8 tensors carry 2-bit codes packed four per byte (residual rows [.., d/4]).
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: I2}
 _RES_CODE = {"f32": F32, "bf16": BF16, "i8": I8, "i2": I2}
+_RES_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i2": torch.uint8}
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int32
@@ -33,7 +37,12 @@ class DecodeArgs(ctypes.Structure):
         "q", "a", "a_scale", "b_l", "w_lin", "w1", "b1", "w2", "b2", "res_idx", "res_val", "res_scale",
         "res_blk_ptr", "sel", "keep", "win_k", "win_v", "out", "stats", "workspace")] + [
         ("workspace_bytes", ctypes.c_size_t), ("ev_main_begin", _p), ("ev_main_end", _p),
-        ("combine_stream", _p), ("combine_ready", _p)]
+        ("combine_stream", _p), ("combine_ready", _p), ("win_len_dev", _p), ("check_flags", _p)]
+
+
+class WindowArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("n_layers", "batch", "width", "win_cap", "act_dtype")] + [
+        (n, _p) for n in ("new_k", "new_v", "win_k", "win_v", "win_len_dev")]
 
 
 class RankArgs(ctypes.Structure):
@@ -91,6 +100,8 @@ def lib():
         L.lowram_decode_step.restype = ctypes.c_int
         L.lowram_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.lowram_decode_workspace_size.restype = ctypes.c_size_t
+        L.lowram_window_append.argtypes = [ctypes.POINTER(WindowArgs), _p]
+        L.lowram_window_append.restype = ctypes.c_int
         L.lowram_rank_residuals.argtypes = [ctypes.POINTER(RankArgs), _p]
         L.lowram_rank_residuals.restype = ctypes.c_int
         L.lowram_rank_workspace_size.argtypes = [ctypes.POINTER(RankArgs)]
@@ -146,11 +157,115 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _want(name, t, shape, dtypes):
+    """Raise ValueError unless tensor ``t`` has exactly ``shape`` and one of ``dtypes``."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(x) for x in dtypes]}")
+
+
+def _same_gpu(named):
+    """Every tensor on the CUDA (HIP) device of the first one: the library
+    reads device pointers only, so a host tensor must never reach it."""
+    first = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}; liblowram takes device tensors only")
+        if first is None:
+            first = t.device
+        elif t.device != first:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {first}")
+
+
+_ACT = (torch.float32, torch.bfloat16)
+_I32 = (torch.int32,)
+
+
+def _check_decode(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, out, a_scale, b1, b2, res_scale,
+                  sel, keep, win_k, win_v, win_len, stats, win_len_dev, check_flags, workspace):
+    """Shapes, dtypes and device of every decode tensor against the shapes the
+    header documents, derived from (B, Hq, d) of q, (T, r) of a, Hkv from b_l,
+    h from w1, k from res_idx; raises ValueError before anything is launched."""
+    if q.dim() != 3 or a.dim() != 3 or b_l.dim() != 3 or w1.dim() != 4 or res_idx.dim() != 3:
+        raise ValueError("q, a, b_l must be 3-D, w1 4-D and res_idx 3-D")
+    B, Hq, d = q.shape
+    T, r = a.shape[1], a.shape[2]
+    if b_l.shape[1] % d:
+        raise ValueError(f"b_l: {b_l.shape[1]} rows is not a multiple of head_dim {d}")
+    hkv, h, k = b_l.shape[1] // d, w1.shape[2], res_idx.shape[2]
+    nb = -(-T // BLOCK)
+    act = q.dtype
+    if act not in _ACT:
+        raise ValueError(f"q: dtype {act}, expected float32 or bfloat16")
+    _want("a", a, (B, T, r), (torch.float32, torch.bfloat16, torch.int8))
+    if a.dtype == torch.int8:
+        _want("a_scale", a_scale, (B, T), (torch.float32,))
+    elif a_scale is not None:
+        raise ValueError("a_scale is for int8 A only")
+    _want("b_l", b_l, (B, hkv * d, r), (act,))
+    _want("w_lin", w_lin, (B, hkv, d, d), (act,))
+    _want("w1", w1, (B, hkv, h, d), (act,))
+    _want("w2", w2, (B, hkv, d, h), (act,))
+    if b1 is not None:
+        _want("b1", b1, (B, hkv, h), (act,))
+    if b2 is not None:
+        _want("b2", b2, (B, hkv, d), (act,))
+    _want("res_idx", res_idx, (B, hkv, k), _I32)
+    if res_val is None or res_val.dtype not in _DTYPE:
+        raise ValueError("res_val must be float32, bfloat16, int8 or uint8 (2-bit codes)")
+    _want("res_val", res_val, (B, hkv, k, d // 4 if res_val.dtype == torch.uint8 else d), (res_val.dtype,))
+    if res_val.dtype in (torch.int8, torch.uint8):
+        if k > 0 or res_scale is not None:
+            _want("res_scale", res_scale, (B, hkv, k), (torch.float32,))
+    elif res_scale is not None:
+        raise ValueError("res_scale is for int8 and 2-bit residuals only")
+    _want("res_blk_ptr", res_blk_ptr, (B, hkv, nb + 1), _I32)
+    if sel is not None:
+        if sel.dim() != 2 or sel.shape[0] != B or sel.dtype != torch.int32:
+            raise ValueError(f"sel: expected int32 [B={B}, n_sel], got {sel.dtype} {tuple(sel.shape)}")
+    if keep is not None:
+        _want("keep", keep, (B, nb), (torch.uint8,))
+    if win_k is not None or win_v is not None:
+        if win_k is None or win_k.dim() != 3:
+            raise ValueError("win_k: expected [B, win_cap, Hkv*d]")
+        _want("win_k", win_k, (B, win_k.shape[1], hkv * d), (act,))
+        _want("win_v", win_v, tuple(win_k.shape), (act,))
+    elif win_len:
+        raise ValueError("win_len > 0 needs win_k and win_v")
+    _want("out", out, (B, Hq, d), (act,))
+    if stats is not None:
+        _want("stats", stats, (B, hkv, 2), _I32)
+    if win_len_dev is not None:
+        _want("win_len_dev", win_len_dev, (1,), _I32)
+    if check_flags is not None:
+        _want("check_flags", check_flags, (1,), (torch.int32, torch.uint32) if hasattr(torch, "uint32") else _I32)
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    _same_gpu((("q", q), ("a", a), ("a_scale", a_scale), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1),
+               ("w2", w2), ("b1", b1), ("b2", b2), ("res_idx", res_idx), ("res_val", res_val),
+               ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("sel", sel), ("keep", keep),
+               ("win_k", win_k), ("win_v", win_v), ("out", out), ("stats", stats),
+               ("win_len_dev", win_len_dev), ("check_flags", check_flags), ("workspace", workspace)))
+
+
 def make_decode_args(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, out, *, a_scale=None,
                      b1=None, b2=None, res_scale=None, sel=None, keep=None, win_k=None, win_v=None,
-                     win_len=0, stats=None, workspace=None, generic=False, events=None):
+                     win_len=0, stats=None, workspace=None, generic=False, events=None, win_len_dev=None,
+                     validate=None):
     """Fill a DecodeArgs from tensors (shapes as documented in lowram.h).
-    ``workspace`` may be None to size it first with ``decode_workspace_size``."""
+    ``workspace`` may be None to size it first with ``decode_workspace_size``.
+    ``win_len_dev`` (int32 [1] on the device) makes the kernels read the window
+    length at run time, ``win_len`` then being its upper bound; ``validate``
+    (int32 [1] on the device, cleared by the caller) turns on the validate
+    mode, whose defect bits (CHECK_*) land there. Every tensor's shape, dtype
+    and device is checked first (ValueError)."""
+    _check_decode(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, out, a_scale, b1, b2, res_scale,
+                  sel, keep, win_k, win_v, win_len, stats, win_len_dev, validate, workspace)
     B, Hq, d = q.shape
     T, r = a.shape[1], a.shape[2]
     args = DecodeArgs()
@@ -164,11 +279,12 @@ def make_decode_args(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, ou
     args.act_dtype = _dt(q, "q")
     args.a_dtype = _dt(a, "a")
     args.res_dtype = _dt(res_val, "res_val")
-    args.flags = FLAG_GENERIC if generic else 0
+    args.flags = (FLAG_GENERIC if generic else 0) | (FLAG_VALIDATE if validate is not None else 0)
     for name, t in (("q", q), ("a", a), ("a_scale", a_scale), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1),
                     ("b1", b1), ("w2", w2), ("b2", b2), ("res_idx", res_idx), ("res_val", res_val),
                     ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr), ("sel", sel), ("keep", keep),
-                    ("win_k", win_k), ("win_v", win_v), ("out", out), ("stats", stats), ("workspace", workspace)):
+                    ("win_k", win_k), ("win_v", win_v), ("out", out), ("stats", stats), ("workspace", workspace),
+                    ("win_len_dev", win_len_dev), ("check_flags", validate)):
         setattr(args, name, _ptr(t))
     args.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is not None:
@@ -204,9 +320,65 @@ def decode_step(q, a, b_l, w_lin, w1, w2, res_idx, res_val, res_blk_ptr, *, out=
     return out
 
 
+def make_window_args(new_k, new_v, win_k, win_v, win_len_dev):
+    """Arguments of lowram_window_append: new_k, new_v [L, B, width];
+    win_k, win_v [L, B, win_cap, width] (layer l's buffers are what its decode
+    call takes); win_len_dev int32 [L] fill counts on the device."""
+    if win_k.dim() != 4:
+        raise ValueError("win_k: expected [n_layers, B, win_cap, width]")
+    Lw, B, cap, width = win_k.shape
+    if win_k.dtype not in _ACT:
+        raise ValueError(f"win_k: dtype {win_k.dtype}, expected float32 or bfloat16")
+    _want("win_v", win_v, (Lw, B, cap, width), (win_k.dtype,))
+    _want("new_k", new_k, (Lw, B, width), (win_k.dtype,))
+    _want("new_v", new_v, (Lw, B, width), (win_k.dtype,))
+    _want("win_len_dev", win_len_dev, (Lw,), _I32)
+    _same_gpu((("win_k", win_k), ("win_v", win_v), ("new_k", new_k), ("new_v", new_v),
+               ("win_len_dev", win_len_dev)))
+    args = WindowArgs()
+    args.n_layers, args.batch, args.width, args.win_cap = Lw, B, width, cap
+    args.act_dtype = _DTYPE[win_k.dtype]
+    for name, t in (("new_k", new_k), ("new_v", new_v), ("win_k", win_k), ("win_v", win_v),
+                    ("win_len_dev", win_len_dev)):
+        setattr(args, name, _ptr(t))
+    return args
+
+
+def window_launch(args, stream=None):
+    rc = lib().lowram_window_append(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def window_append(new_k, new_v, win_k, win_v, win_len_dev, *, stream=None):
+    """Append one exact key/value row per (layer, sequence) at each layer's
+    fill count and advance the counts (lowram_window_append)."""
+    window_launch(make_window_args(new_k, new_v, win_k, win_v, win_len_dev), stream)
+
+
 def make_rank_args(v, v_hat, n_res, res_dtype, res_idx, res_val, res_scale, res_blk_ptr, *, err=None,
                    workspace=None, events=None):
+    """Arguments of lowram_rank_residuals; shapes, dtypes and devices are
+    checked against v [Lr, T, Hkv, d] first (ValueError)."""
+    if v.dim() != 4:
+        raise ValueError("v: expected [Lr, T, Hkv, d]")
     Lr, T, Hkv, d = v.shape
+    if v.dtype not in _ACT:
+        raise ValueError(f"v: dtype {v.dtype}, expected float32 or bfloat16")
+    if res_dtype not in _RES_CODE:
+        raise ValueError(f"res_dtype must be one of {sorted(_RES_CODE)}")
+    nb = -(-T // BLOCK)
+    _want("v_hat", v_hat, tuple(v.shape), (v.dtype,))
+    if n_res > 0 or res_idx is not None:
+        _want("res_idx", res_idx, (Lr, Hkv, n_res), _I32)
+        _want("res_val", res_val, (Lr, Hkv, n_res, d // 4 if res_dtype == "i2" else d), (_RES_TORCH[res_dtype],))
+    if res_dtype in ("i8", "i2") and (n_res > 0 or res_scale is not None):
+        _want("res_scale", res_scale, (Lr, Hkv, n_res), (torch.float32,))
+    _want("res_blk_ptr", res_blk_ptr, (Lr, Hkv, nb + 1), _I32)
+    if err is not None:
+        _want("err", err, (Lr, Hkv, T), (torch.float64,))
+    _same_gpu((("v", v), ("v_hat", v_hat), ("res_idx", res_idx), ("res_val", res_val), ("res_scale", res_scale),
+               ("res_blk_ptr", res_blk_ptr), ("err", err), ("workspace", workspace)))
     args = RankArgs()
     args.n_slices, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, T, Hkv, d
     args.block_size, args.n_res = BLOCK, n_res
@@ -233,9 +405,6 @@ def rank_launch(args, stream=None):
     rc = lib().lowram_rank_residuals(ctypes.byref(args), _stream(stream))
     if rc != OK:
         raise LowramError(rc, last_error())
-
-
-_RES_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i2": torch.uint8}
 
 
 def _res_store(Lr, Hkv, n_res, d, res_dtype, dev):
@@ -271,8 +440,37 @@ def rank_residuals(v, v_hat, n_res, res_dtype, *, want_err=False, workspace=None
 def make_prefill_args(a, b_l, w_lin, w1, w2, v, n_res, res_dtype, res_idx, res_val, res_scale, res_blk_ptr, *,
                       group=4, b1=None, b2=None, err=None, v_hat=None, workspace=None, events=None):
     """Arguments of lowram_prefill_rank. a [ceil(Lr/group), T, r], b_l [Lr, Hkv*d, r],
-    w_lin [Lr, Hkv, d, d], w1 [Lr, Hkv, h, d], w2 [Lr, Hkv, d, h], v [Lr, T, Hkv, d]."""
+    w_lin [Lr, Hkv, d, d], w1 [Lr, Hkv, h, d], w2 [Lr, Hkv, d, h], v [Lr, T, Hkv, d],
+    all bf16; shapes, dtypes and devices are checked first (ValueError)."""
+    if v.dim() != 4 or a.dim() != 3 or w1.dim() != 4:
+        raise ValueError("v must be 4-D, a 3-D and w1 4-D")
     Lr, T, Hkv, d = v.shape
+    if res_dtype not in _RES_CODE:
+        raise ValueError(f"res_dtype must be one of {sorted(_RES_CODE)}")
+    bf, r, h, nb = (torch.bfloat16,), a.shape[-1], w1.shape[-2], -(-T // BLOCK)
+    _want("v", v, (Lr, T, Hkv, d), bf)
+    _want("a", a, (-(-Lr // group) if group > 0 else a.shape[0], T, r), bf)
+    _want("b_l", b_l, (Lr, Hkv * d, r), bf)
+    _want("w_lin", w_lin, (Lr, Hkv, d, d), bf)
+    _want("w1", w1, (Lr, Hkv, h, d), bf)
+    _want("w2", w2, (Lr, Hkv, d, h), bf)
+    if b1 is not None:
+        _want("b1", b1, (Lr, Hkv, h), bf)
+    if b2 is not None:
+        _want("b2", b2, (Lr, Hkv, d), bf)
+    if n_res > 0 or res_idx is not None:
+        _want("res_idx", res_idx, (Lr, Hkv, n_res), _I32)
+        _want("res_val", res_val, (Lr, Hkv, n_res, d // 4 if res_dtype == "i2" else d), (_RES_TORCH[res_dtype],))
+    if res_dtype in ("i8", "i2") and (n_res > 0 or res_scale is not None):
+        _want("res_scale", res_scale, (Lr, Hkv, n_res), (torch.float32,))
+    _want("res_blk_ptr", res_blk_ptr, (Lr, Hkv, nb + 1), _I32)
+    if err is not None:
+        _want("err", err, (Lr, Hkv, T), (torch.float64,))
+    if v_hat is not None:
+        _want("v_hat", v_hat, (Lr, T, Hkv, d), (torch.float32,))
+    _same_gpu((("v", v), ("a", a), ("b_l", b_l), ("w_lin", w_lin), ("w1", w1), ("w2", w2), ("b1", b1), ("b2", b2),
+               ("res_idx", res_idx), ("res_val", res_val), ("res_scale", res_scale), ("res_blk_ptr", res_blk_ptr),
+               ("err", err), ("v_hat", v_hat), ("workspace", workspace)))
     args = PrefillArgs()
     args.n_slices, args.group, args.ctx_len, args.n_kv_heads, args.head_dim = Lr, group, T, Hkv, d
     args.rank, args.mlp_hidden, args.block_size, args.n_res = a.shape[-1], w1.shape[-2], BLOCK, n_res

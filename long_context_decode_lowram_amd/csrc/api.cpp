@@ -50,6 +50,7 @@ int plan_decode(const lowram_decode_args* a, DecodePlan* pl) {
     if (a->win_len < 0 || a->win_cap < 0) return fail(LOWRAM_ERR_ARG, "win_len and win_cap must be >= 0");
     if (a->win_len > a->win_cap) return fail(LOWRAM_ERR_WINDOW_FULL, "win_len (%d) > win_cap (%d)", a->win_len, a->win_cap);
     if (a->win_len > 4096) return fail(LOWRAM_ERR_UNSUPPORTED, "win_len above 4096");
+    if (a->flags & ~(LOWRAM_FLAG_GENERIC | LOWRAM_FLAG_VALIDATE)) return fail(LOWRAM_ERR_ARG, "unknown flag bits 0x%x", a->flags);
     const int g = a->n_q_heads / a->n_kv_heads;
     pl->nb = (a->ctx_len + kBlock - 1) / kBlock;
     if (a->sel != nullptr && (a->n_sel < 0 || a->n_sel > pl->nb))
@@ -88,10 +89,13 @@ int check_decode_ptrs(const lowram_decode_args* a, const DecodePlan& pl) {
         return fail(LOWRAM_ERR_ARG, "int8 and 2-bit residuals need res_scale");
     if (a->win_len > 0 && (!a->win_k || !a->win_v)) return fail(LOWRAM_ERR_ARG, "win_k and win_v must be non-NULL when win_len > 0");
     if (a->combine_stream && !a->combine_ready) return fail(LOWRAM_ERR_ARG, "combine_stream needs combine_ready");
+    if ((a->flags & LOWRAM_FLAG_VALIDATE) && !a->check_flags)
+        return fail(LOWRAM_ERR_ARG, "LOWRAM_FLAG_VALIDATE needs check_flags");
     const void* v16[] = {a->q, a->a, a->b_l, a->w_lin, a->w1, a->w2, a->res_val, a->win_k, a->win_v, a->out, a->workspace};
     for (const void* p : v16)
         if (misaligned(p, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", p);
-    const void* v4[] = {a->a_scale, a->b1, a->b2, a->res_idx, a->res_scale, a->res_blk_ptr, a->sel, a->stats};
+    const void* v4[] = {a->a_scale, a->b1, a->b2, a->res_idx, a->res_scale, a->res_blk_ptr, a->sel, a->stats,
+                        a->win_len_dev, a->check_flags};
     for (const void* p : v4)
         if (misaligned(p, 4)) return fail(LOWRAM_ERR_ARG, "pointer %p is not 4-byte aligned", p);
     if (pl.total > 0 && (!a->workspace || a->workspace_bytes < pl.total))
@@ -133,6 +137,8 @@ int plan_prefill(const lowram_prefill_args* a, PrefillPlan* pl) {
         return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden must be a multiple of 64 in [64, 4096] (got %d)", a->mlp_hidden);
     if ((int64_t)a->ctx_len * a->rank * 2 >= (int64_t(1) << 31))
         return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * rank * 2 must stay below 2^31");
+    if ((int64_t)a->ctx_len * a->n_kv_heads * a->head_dim * 2 >= (int64_t(1) << 31))
+        return fail(LOWRAM_ERR_UNSUPPORTED, "ctx_len * n_kv_heads * head_dim * 2 must stay below 2^31");
     if (a->n_res < 0 || a->n_res > a->ctx_len) return fail(LOWRAM_ERR_ARG, "n_res (%d) must be in [0, ctx_len]", a->n_res);
     if (a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_UNSUPPORTED, "act_dtype must be BF16");
     if (a->res_dtype < LOWRAM_F32 || a->res_dtype > LOWRAM_I2) return fail(LOWRAM_ERR_ARG, "bad res_dtype");
@@ -311,6 +317,8 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.res_idx = a->res_idx; p.res_val = a->res_val;
     p.res_scale = a->res_scale; p.res_ptr = a->res_blk_ptr; p.sel = a->sel; p.keep = a->keep;
     p.win_k = a->win_k; p.win_v = a->win_v; p.out = a->out; p.stats = a->stats; p.n_sel = a->n_sel;
+    p.win_len_dev = a->win_len_dev;
+    p.check_flags = (a->flags & LOWRAM_FLAG_VALIDATE) ? a->check_flags : nullptr;
     char* ws = static_cast<char*>(a->workspace);
     p.att_list = reinterpret_cast<int32_t*>(ws + pl.off_list);
     p.att_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
@@ -322,6 +330,10 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     // compaction pass runs only when some selected blocks may be dropped.
     p.att_direct = a->keep == nullptr;
     hipError_t e = hipSuccess;
+    if (p.check_flags) {
+        e = launch_validate(p, s);
+        if (e != hipSuccess) return hip_fail(e, "validate launch");
+    }
     if (!p.att_direct) {
         e = launch_assemble(p, s);
         if (e != hipSuccess) return hip_fail(e, "assemble launch");
@@ -348,6 +360,27 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     e = launch_combine(p, a->act_dtype, cs);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return LOWRAM_OK;
+}
+
+int lowram_window_append(const lowram_window_args* a, void* stream) {
+    g_err[0] = 0;
+    if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
+    if (a->n_layers < 1 || a->n_layers > 65535 || a->batch < 1 || a->win_cap < 1)
+        return fail(LOWRAM_ERR_ARG, "n_layers must be in [1, 65535], batch and win_cap >= 1");
+    if (a->act_dtype != LOWRAM_F32 && a->act_dtype != LOWRAM_BF16) return fail(LOWRAM_ERR_ARG, "act_dtype must be F32 or BF16");
+    const int eb = a->act_dtype == LOWRAM_F32 ? 4 : 2;
+    if (a->width < 8 || (a->width * eb) % 16 != 0) return fail(LOWRAM_ERR_ARG, "width (%d) must fill whole 16-byte pieces", a->width);
+    if (!a->new_k || !a->new_v || !a->win_k || !a->win_v || !a->win_len_dev)
+        return fail(LOWRAM_ERR_ARG, "new_k, new_v, win_k, win_v and win_len_dev must be non-NULL");
+    const void* v16[] = {a->new_k, a->new_v, a->win_k, a->win_v};
+    for (const void* q : v16)
+        if (misaligned(q, 16)) return fail(LOWRAM_ERR_ARG, "tensor pointer %p is not 16-byte aligned", q);
+    if (misaligned(a->win_len_dev, 4)) return fail(LOWRAM_ERR_ARG, "win_len_dev is not 4-byte aligned");
+    WindowParams p{};
+    p.n_layers = a->n_layers; p.batch = a->batch; p.width = a->width; p.win_cap = a->win_cap; p.elem_bytes = eb;
+    p.new_k = a->new_k; p.new_v = a->new_v; p.win_k = a->win_k; p.win_v = a->win_v; p.win_len = a->win_len_dev;
+    const hipError_t e = launch_window_append(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LOWRAM_OK : hip_fail(e, "window append launch");
 }
 
 size_t lowram_rank_workspace_size(const lowram_rank_args* a) {

@@ -108,7 +108,16 @@ struct DecodeParams {
     int32_t* counts;       // [B, Hkv, n_split, 2]
     int n_sel;
     int att_direct;        // no eviction flags: the attended blocks are sel (or all blocks) as given
+    const int32_t* win_len_dev;   // window length read at run time (clamped to [0, win_len]), or null
+    uint32_t* check_flags;        // validate mode: defect bits are ORed in here, else null
 };
+
+// Window tokens attended by this call: win_len, or the device-held count
+// clamped to [0, win_len] (win_len is then the capacity the host checked).
+__device__ __forceinline__ int window_len(const DecodeParams& p) {
+    if (p.win_len_dev == nullptr) return p.win_len;
+    return min(max(*p.win_len_dev, 0), p.win_len);
+}
 
 // Attended block i of sequence b, or -1 for an entry outside the cache. With
 // eviction flags the assembly kernel has compacted the kept blocks into

@@ -41,6 +41,95 @@ hipError_t launch_assemble(const DecodeParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Validate mode: one workgroup per (b, KV head) row of the residual store,
+// plus one per sequence for its selection row (blockIdx.y == 1) and the
+// window count. Every read stays inside the documented shapes; a defect ORs
+// its bit into *check_flags (only defective threads write).
+__device__ __forceinline__ void flag(uint32_t* f, uint32_t bit) {
+    __hip_atomic_fetch_or(f, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void validate_kernel(DecodeParams p) {
+    const int tid = threadIdx.x;
+    if (blockIdx.y == 1) {
+        const int b = blockIdx.x;
+        if (b >= p.batch) return;
+        if (b == 0 && tid == 0 && p.win_len_dev != nullptr) {
+            const int w = *p.win_len_dev;
+            if (w < 0 || w > p.win_len) flag(p.check_flags, kCheckWinLen);
+        }
+        if (p.sel == nullptr) return;
+        // In-range entries strictly ascending, padding (outside [0, nb))
+        // anywhere: each in-range entry is compared with the previous one.
+        const int32_t* row = p.sel + (int64_t)b * p.n_sel;
+        bool bad = false;
+        for (int i = tid; i < p.n_sel; i += blockDim.x) {
+            const int cur = row[i];
+            if (cur < 0 || cur >= p.n_blocks) continue;
+            int prev = -1;
+            for (int k = i - 1; k >= 0; --k) {
+                const int v = row[k];
+                if (v >= 0 && v < p.n_blocks) { prev = v; break; }
+            }
+            bad |= prev >= cur;
+        }
+        if (bad) flag(p.check_flags, kCheckSelOrder);
+        return;
+    }
+    const int bh = blockIdx.x;                  // b * n_kv + h
+    const int32_t* idx = p.res_idx + (int64_t)bh * p.n_res;
+    const int32_t* ptr = p.res_ptr + (int64_t)bh * (p.n_blocks + 1);
+    uint32_t bits = 0;
+    for (int s = tid; s < p.n_res; s += blockDim.x) {
+        const int t = idx[s];
+        if (t < 0 || t >= p.ctx_len) { bits |= kCheckResRange; continue; }
+        if (s > 0 && idx[s - 1] >= t) bits |= kCheckResOrder;
+        const int blk = t / kBlock;
+        if (!(ptr[blk] <= s && s < ptr[blk + 1])) bits |= kCheckResPtr;
+    }
+    for (int i = tid; i <= p.n_blocks; i += blockDim.x) {
+        const int v = ptr[i];
+        if ((i == 0 && v != 0) || (i == p.n_blocks && v != p.n_res) || (i > 0 && ptr[i - 1] > v))
+            bits |= kCheckResPtr;
+    }
+    if (bits) flag(p.check_flags, bits);
+}
+
+hipError_t launch_validate(const DecodeParams& p, hipStream_t s) {
+    const int rows = p.batch * p.n_kv;
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)max(rows, p.batch), 2), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// Window append: workgroup l copies the new rows of layer l (all sequences)
+// into slot win_len_dev[l] of its buffers, then advances the count. The
+// count is read once, before the barrier, by every thread; one thread writes
+// it after the barrier, so no thread of the workgroup reads the new value.
+__global__ __launch_bounds__(256) void window_append_kernel(WindowParams p) {
+    const int l = blockIdx.x;
+    const int pos = p.win_len[l];
+    __syncthreads();
+    if (pos < 0 || pos >= p.win_cap) return;     // full (or bad) buffer: nothing written, count kept
+    const int pieces = p.width * p.elem_bytes / 16;           // 16-byte pieces per row
+    const int64_t n = (int64_t)p.batch * pieces;
+    const uint4* nk = reinterpret_cast<const uint4*>(static_cast<const char*>(p.new_k) + (int64_t)l * p.batch * p.width * p.elem_bytes);
+    const uint4* nv = reinterpret_cast<const uint4*>(static_cast<const char*>(p.new_v) + (int64_t)l * p.batch * p.width * p.elem_bytes);
+    uint4* wk = reinterpret_cast<uint4*>(static_cast<char*>(p.win_k) + (int64_t)l * p.batch * p.win_cap * p.width * p.elem_bytes);
+    uint4* wv = reinterpret_cast<uint4*>(static_cast<char*>(p.win_v) + (int64_t)l * p.batch * p.win_cap * p.width * p.elem_bytes);
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+        const int64_t b = e / pieces, c = e % pieces;
+        const int64_t dst = (b * p.win_cap + pos) * pieces + c;
+        wk[dst] = nk[e];
+        wv[dst] = nv[e];
+    }
+    if (threadIdx.x == 0) p.win_len[l] = pos + 1;
+}
+
+hipError_t launch_window_append(const WindowParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(window_append_kernel, dim3(p.n_layers), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     v = is_max ? wave_max(v) : wave_sum(v);
@@ -70,11 +159,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     const int lane = tid & 63, wv = tid >> 6;
     const int h = j / p.group, H = p.hidden, S = p.part_stride, nf = H + kHeadDim;
     const int nsplit = min(p.n_split, (attended_count(p, b) + p.blocks_per_split - 1) / p.blocks_per_split);
-    const int nw = p.win_len;
+    const int nw = window_len(p);         // at most p.win_len, which sizes sw
     const float* P = p.partials + ((int64_t)b * p.n_q + j) * p.n_split * (int64_t)S;
     extern __shared__ float sm[];
     float* sw = sm;                       // [win_len]
-    float* oc = sw + nw;                  // [H + 128]
+    float* oc = sw + p.win_len;           // [H + 128]
     float* qs = oc + nf;                  // [128]
     float* red = qs + kHeadDim;           // [8 + 3 * 128]: block reductions, then the W2 quarter sums
     float* part = red + 8 + 3 * kHeadDim; // [8][H + 128]: the waves' record sums

@@ -10,6 +10,20 @@ namespace lowram {
 // Attended-set assembly: att_list/att_count from sel and keep. Grid (B).
 hipError_t launch_assemble(const DecodeParams& p, hipStream_t s);
 
+// Validate mode: defect bits of the device-side index data into p.check_flags.
+constexpr uint32_t kCheckSelOrder = 1, kCheckResRange = 2, kCheckResOrder = 4, kCheckResPtr = 8, kCheckWinLen = 16;
+hipError_t launch_validate(const DecodeParams& p, hipStream_t s);
+
+// Window append: one new exact key/value row per (layer, sequence) at slot
+// win_len[l] of layer l's buffers, then win_len[l] += 1. Grid (n_layers).
+struct WindowParams {
+    int n_layers, batch, width, win_cap, elem_bytes;
+    const void* new_k; const void* new_v;   // [L, B, width]
+    void* win_k; void* win_v;               // [L, B, win_cap, width]
+    int32_t* win_len;                       // [L]
+};
+hipError_t launch_window_append(const WindowParams& p, hipStream_t s);
+
 // Generic fp32 SIMT kernel: one workgroup per (attended block, KV head, b).
 hipError_t launch_decode_generic(const DecodeParams& p, int act, int adt, int rdt, hipStream_t s);
 

@@ -20,7 +20,8 @@ import math
 import torch
 
 __all__ = ["DecodeConfig", "CONFIGS", "RankConfig", "RANK_C5", "PrefillConfig", "PREFILL_CONFIGS",
-           "make_generator", "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_rank_inputs",
+           "make_generator", "n_blocks", "gen_group_factor", "gen_layer", "gen_window", "gen_step_inputs",
+           "gen_rank_inputs",
            "gen_prefill_inputs", "block_ptr_from_idx", "XkvConfig", "XKV_CONFIGS", "gen_xkv_inputs",
            "FitConfig", "FIT_CONFIGS", "gen_fit_inputs", "gen_pinv_inputs"]
 
@@ -178,7 +179,9 @@ def gen_group_factor(cfg, group, device, batch=None):
 
 def _selection(cfg, bsz, layer, step, device):
     """Per sequence: blocks {0, 1, nb-2, nb-1} plus n_sel-4 drawn uniformly
-    without replacement from [2, nb-3], ascending (int32 [B, n_sel])."""
+    without replacement from [2, nb-3], ascending (int32 [B, n_sel]). Below
+    n_sel = 4 (tiny test contexts only) the rows keep the four edge blocks and
+    come out longer than n_sel; callers take the row length from the tensor."""
     nb, n_sel = cfg.nb, cfg.n_sel
     g = make_generator("cpu", cfg.seed, "sel", layer, step)
     rows = []
@@ -275,6 +278,27 @@ def gen_window(cfg, layer, device, *, batch=None):
     g = make_generator(device, cfg.seed, "win", layer)
     shape = (bsz, cfg.win_cap, cfg.n_kv_heads * cfg.head_dim)
     return _normal(shape, 0.25, act, device, g), _normal(shape, 0.1, act, device, g)
+
+
+def gen_step_inputs(cfg, step, device, *, batch=None, n_layers=None):
+    """What changes from one decode step to the next, for every layer: the
+    query q [L, B, Hq, d], the block selection sel [L, B, n_sel] (None when
+    every block is attended) and the new token's exact key and value rows
+    new_k, new_v [L, B, Hkv*d], appended to the recent window (drawn like the
+    window rows: keys with std 0.25, values with std 0.1). Keyed by step, so
+    step s of a run always sees the same draws."""
+    bsz = cfg.batch if batch is None else batch
+    nl = cfg.n_layers if n_layers is None else n_layers
+    act = _DT[cfg.act]
+    g = make_generator(device, cfg.seed, "step", step, bsz, nl)
+    width = cfg.n_kv_heads * cfg.head_dim
+    q = (torch.randn(nl, bsz, cfg.n_q_heads, cfg.head_dim, generator=g, device=device) * _SIGMA).to(act)
+    new_k = _normal((nl, bsz, width), 0.25, act, device, g)
+    new_v = _normal((nl, bsz, width), 0.1, act, device, g)
+    sel = None
+    if cfg.sel_den != 1:
+        sel = torch.stack([_selection(cfg, bsz, layer, step + 1, device) for layer in range(nl)])
+    return {"q": q, "sel": sel, "new_k": new_k, "new_v": new_v}
 
 
 def gen_rank_inputs(rc, device, *, n_slices=None, plant_ties=True):

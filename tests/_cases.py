@@ -86,3 +86,66 @@ def rel_err(got, ref):
     zero = den == 0
     assert np.all(num[zero] == 0), "rows with a zero reference must be zero"
     return float(np.max(num[~zero] / den[~zero])) if (~zero).any() else 0.0
+
+
+class WindowSession:
+    """A few decode steps of every layer, the way the long-context protocol
+    runs them: per step the query and block selection of each layer are
+    staged, lowram_window_append writes the new token's exact key and value
+    into each layer's window buffer and advances its device count, and each
+    layer's lowram_decode_step reads its window length from that count.
+    Group factors are generated once per group and shared by its layers."""
+
+    def __init__(self, cfg, cap, *, biases=True):
+        import long_context_decode_lowram_amd as L
+        self.L, self.cfg, self.cap = L, cfg, cap
+        nl, bsz, w = cfg.n_layers, cfg.batch, cfg.n_kv_heads * cfg.head_dim
+        act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+        groups = [synth.gen_group_factor(cfg, g, "cuda") for g in range(-(-nl // cfg.group))]
+        self.cases = []
+        for l in range(nl):
+            c = synth.gen_layer(cfg, l, "cuda", biases=biases)
+            a, a_scale = groups[l // cfg.group]
+            c.update(a=a, a_scale=a_scale, win_len=0, win_k=None, win_v=None)
+            self.cases.append(c)
+        self.win_k = torch.zeros(nl, bsz, cap, w, dtype=act, device="cuda")
+        self.win_v = torch.zeros_like(self.win_k)
+        self.count = torch.zeros(nl, dtype=torch.int32, device="cuda")
+        st = synth.gen_step_inputs(cfg, 0, "cuda")
+        self.q = torch.empty_like(st["q"])
+        self.sel = None if st["sel"] is None else torch.empty_like(st["sel"])
+        self.new_k, self.new_v = torch.empty_like(st["new_k"]), torch.empty_like(st["new_v"])
+        self.outs = [torch.empty_like(c["q"]) for c in self.cases]
+        self.stats = [torch.empty(bsz, cfg.n_kv_heads, 2, dtype=torch.int32, device="cuda") for _ in self.cases]
+        self.calls = []
+        for l, c in enumerate(self.cases):
+            self.calls.append(L.make_decode_args(
+                self.q[l], c["a"], c["bl"], c["w_lin"], c["w1"], c["w2"], c["res_idx"], c["res_val"], c["res_ptr"],
+                self.outs[l], a_scale=c["a_scale"], b1=c["b1"], b2=c["b2"], res_scale=c["res_scale"],
+                sel=None if self.sel is None else self.sel[l], keep=c["keep"], win_k=self.win_k[l],
+                win_v=self.win_v[l], win_len=cap, win_len_dev=self.count[l:l + 1], stats=self.stats[l]))
+        ws = max(L.decode_workspace_size(a) for a in self.calls)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        for a in self.calls:
+            a.workspace, a.workspace_bytes = self.ws.data_ptr(), ws
+        self.wargs = L.make_window_args(self.new_k, self.new_v, self.win_k, self.win_v, self.count)
+
+    def stage(self, step):
+        st = synth.gen_step_inputs(self.cfg, step, "cuda")
+        self.q.copy_(st["q"])
+        if self.sel is not None:
+            self.sel.copy_(st["sel"])
+        self.new_k.copy_(st["new_k"])
+        self.new_v.copy_(st["new_v"])
+        return st
+
+    def launch(self, stream=None):
+        self.L.window_launch(self.wargs, stream)
+        for a in self.calls:
+            self.L.decode_launch(a, stream)
+
+    def oracle(self, l, n_win, st, batch_index=None):
+        c = dict(self.cases[l])
+        c.update(q=st["q"][l], sel=None if st["sel"] is None else st["sel"][l], win_k=self.win_k[l],
+                 win_v=self.win_v[l], win_len=n_win)
+        return oracle_decode(c, batch_index)

@@ -314,3 +314,156 @@ def test_fit_rejects(field, value, status):
     setattr(a, field, value)
     assert L.lib().lowram_fit_predictor(ctypes.byref(a), None) == status
     assert L.last_error() != ""
+
+
+# ------------------------------------------------- window, validate mode
+def test_window_struct_layout_and_decode_tail_fields():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct lowram_window_args"):text.index("} lowram_window_args;")]
+    fields = re.findall(r"\*?\s*([a-z_0-9]+)\s*[;,]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == [f[0] for f in B.WindowArgs._fields_]
+    assert [f[0] for f in B.DecodeArgs._fields_][-2:] == ["win_len_dev", "check_flags"]
+    defs = dict(re.findall(r"#define\s+LOWRAM_([A-Z0-9_]+)\s+(-?\d+)", text))
+    for name in ("FLAG_VALIDATE", "CHECK_SEL_ORDER", "CHECK_RES_RANGE", "CHECK_RES_ORDER", "CHECK_RES_PTR",
+                 "CHECK_WIN_LEN"):
+        assert int(defs[name]) == getattr(B, name), name
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("flags", 4, B.ERR_ARG),                        # unknown flag bit
+    ("flags", B.FLAG_VALIDATE, B.ERR_ARG),          # validate mode without check_flags
+    ("win_len_dev", FAKE + 2, B.ERR_ARG),           # misaligned
+    ("check_flags", FAKE + 1, B.ERR_ARG),
+])
+def test_decode_rejects_new_fields(field, value, status):
+    a = valid_decode()
+    setattr(a, field, value)
+    assert call_decode(a) == status
+    assert L.last_error() != ""
+
+
+def test_decode_validate_and_device_window_stop_at_workspace():
+    a = valid_decode()
+    a.flags, a.check_flags, a.win_len_dev = B.FLAG_VALIDATE, FAKE, FAKE
+    assert call_decode(a) == B.ERR_WORKSPACE
+
+
+def valid_window():
+    a = B.WindowArgs()
+    a.n_layers, a.batch, a.width, a.win_cap, a.act_dtype = 32, 8, 1024, 1024, B.BF16
+    for n in ("new_k", "new_v", "win_k", "win_v", "win_len_dev"):
+        setattr(a, n, FAKE)
+    return a
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_layers", 0), ("batch", 0), ("win_cap", 0), ("width", 4), ("width", 1020), ("act_dtype", B.I8),
+    ("new_k", None), ("win_v", None), ("win_len_dev", None), ("win_k", FAKE + 8), ("win_len_dev", FAKE + 1),
+])
+def test_window_append_rejects(field, value):
+    a = valid_window()
+    setattr(a, field, value)
+    assert L.lib().lowram_window_append(ctypes.byref(a), None) == B.ERR_ARG
+    assert L.last_error() != ""
+
+
+def test_prefill_rejects_v_beyond_32_bit_offsets():
+    a = valid_prefill()
+    a.rank, a.n_kv_heads, a.ctx_len = 64, 8, 1 << 20        # T*rank*2 = 2^27 fits, T*Hkv*d*2 = 2^31 does not
+    assert call_prefill(a) == B.ERR_UNSUPPORTED
+    assert "head_dim" in L.last_error()
+
+
+# ------------------------------------------------- binding: tensor checks
+def _decode_tensors(dtype=None):
+    """A small, consistent set of host tensors for make_decode_args."""
+    import torch
+    act = dtype or torch.bfloat16
+    B_, T, r, hkv, hq, d, h, k, n_sel, cap = 2, 200, 64, 2, 4, 128, 64, 7, 3, 8
+    nb = -(-T // 64)
+    t = dict(q=torch.zeros(B_, hq, d, dtype=act), a=torch.zeros(B_, T, r, dtype=act),
+             b_l=torch.zeros(B_, hkv * d, r, dtype=act), w_lin=torch.zeros(B_, hkv, d, d, dtype=act),
+             w1=torch.zeros(B_, hkv, h, d, dtype=act), w2=torch.zeros(B_, hkv, d, h, dtype=act),
+             res_idx=torch.zeros(B_, hkv, k, dtype=torch.int32), res_val=torch.zeros(B_, hkv, k, d, dtype=act),
+             res_blk_ptr=torch.zeros(B_, hkv, nb + 1, dtype=torch.int32), out=torch.zeros(B_, hq, d, dtype=act))
+    kw = dict(b1=torch.zeros(B_, hkv, h, dtype=act), b2=torch.zeros(B_, hkv, d, dtype=act),
+              sel=torch.zeros(B_, n_sel, dtype=torch.int32), keep=torch.ones(B_, nb, dtype=torch.uint8),
+              win_k=torch.zeros(B_, cap, hkv * d, dtype=act), win_v=torch.zeros(B_, cap, hkv * d, dtype=act),
+              win_len=3, stats=torch.zeros(B_, hkv, 2, dtype=torch.int32))
+    return t, kw
+
+
+def _make(t, kw):
+    return L.make_decode_args(t["q"], t["a"], t["b_l"], t["w_lin"], t["w1"], t["w2"], t["res_idx"], t["res_val"],
+                              t["res_blk_ptr"], t["out"], **kw)
+
+
+def test_binding_accepts_consistent_shapes_then_rejects_host_tensors():
+    t, kw = _decode_tensors()
+    with pytest.raises(ValueError, match="device tensors only"):
+        _make(t, kw)
+
+
+def _mutations():
+    import torch
+    f32, bf, i8 = torch.float32, torch.bfloat16, torch.int8
+    return [
+        ("b_l", lambda t, kw: t.__setitem__("b_l", t["b_l"].to(f32)), "b_l: dtype"),          # fp32 weights, bf16 q
+        ("q", lambda t, kw: t.__setitem__("q", t["q"].to(f32)), "dtype"),                     # fp32 q, bf16 weights
+        ("w1", lambda t, kw: t.__setitem__("w1", t["w1"][:, :, :32].contiguous()), "w2: shape"),
+        ("w2", lambda t, kw: t.__setitem__("w2", t["w2"][..., :32].contiguous()), "w2: shape"),
+        ("w_lin", lambda t, kw: t.__setitem__("w_lin", t["w_lin"][:1].contiguous()), "w_lin: shape"),
+        ("res_blk_ptr", lambda t, kw: t.__setitem__("res_blk_ptr", t["res_blk_ptr"][..., :-1].contiguous()),
+         "res_blk_ptr: shape"),
+        ("res_val", lambda t, kw: t.__setitem__("res_val", t["res_val"][:, :, :3].contiguous()), "res_val: shape"),
+        ("res_idx", lambda t, kw: t.__setitem__("res_idx", t["res_idx"].to(torch.int64)), "res_idx: dtype"),
+        ("out", lambda t, kw: t.__setitem__("out", t["out"][:, :2].contiguous()), "out: shape"),
+        ("keep", lambda t, kw: kw.__setitem__("keep", kw["keep"][:, :-1].contiguous()), "keep: shape"),
+        ("keep", lambda t, kw: kw.__setitem__("keep", kw["keep"].bool()), "keep: dtype"),
+        ("sel", lambda t, kw: kw.__setitem__("sel", kw["sel"].to(torch.int64)), "sel"),
+        ("win_v", lambda t, kw: kw.__setitem__("win_v", kw["win_v"][:, :4].contiguous()), "win_v: shape"),
+        ("win_k", lambda t, kw: kw.__setitem__("win_k", None), "win_k"),
+        ("b2", lambda t, kw: kw.__setitem__("b2", kw["b2"].to(f32)), "b2: dtype"),
+        ("stats", lambda t, kw: kw.__setitem__("stats", kw["stats"][:, :1].contiguous()), "stats: shape"),
+        ("a_scale", lambda t, kw: (t.__setitem__("a", t["a"].to(i8))), "a_scale is required"),
+        ("a_scale", lambda t, kw: kw.__setitem__("a_scale", torch.ones(2, 200)), "int8 A only"),
+        ("res_scale", lambda t, kw: t.__setitem__("res_val", t["res_val"].to(i8)), "res_scale is required"),
+        ("res_scale", lambda t, kw: kw.__setitem__("res_scale", torch.ones(2, 2, 7)), "int8 and 2-bit"),
+        ("win_len_dev", lambda t, kw: kw.__setitem__("win_len_dev", torch.zeros(2, dtype=torch.int32)),
+         "win_len_dev: shape"),
+    ]
+
+
+@pytest.mark.parametrize("i", range(21))
+def test_binding_rejects_inconsistent_tensors(i):
+    name, mutate, msg = _mutations()[i]
+    t, kw = _decode_tensors()
+    mutate(t, kw)
+    with pytest.raises(ValueError, match=msg):
+        _make(t, kw)
+
+
+def test_binding_rank_and_window_checks():
+    import torch
+    v = torch.zeros(2, 100, 2, 128, dtype=torch.bfloat16)
+    idx = torch.zeros(2, 2, 10, dtype=torch.int32)
+    val = torch.zeros(2, 2, 10, 128, dtype=torch.int8)
+    scale = torch.zeros(2, 2, 10)
+    ptr = torch.zeros(2, 2, 3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="v_hat: dtype"):
+        L.make_rank_args(v, v.float(), 10, "i8", idx, val, scale, ptr)
+    with pytest.raises(ValueError, match="res_val: dtype"):
+        L.make_rank_args(v, v, 10, "bf16", idx, val, None, ptr)
+    with pytest.raises(ValueError, match="res_blk_ptr: shape"):
+        L.make_rank_args(v, v, 10, "i8", idx, val, scale, ptr[..., :2])
+    with pytest.raises(ValueError, match="device tensors only"):
+        L.make_rank_args(v, v, 10, "i8", idx, val, scale, ptr)
+    wk = torch.zeros(3, 2, 16, 256, dtype=torch.bfloat16)
+    nk = torch.zeros(3, 2, 256, dtype=torch.bfloat16)
+    cnt = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="new_v: shape"):
+        L.make_window_args(nk, nk[:2], wk, wk, cnt)
+    with pytest.raises(ValueError, match="win_len_dev: shape"):
+        L.make_window_args(nk, nk, wk, wk, cnt[:1])
+    with pytest.raises(ValueError, match="device tensors only"):
+        L.make_window_args(nk, nk, wk, wk, cnt)

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import synth
-from _cases import TOL, gpu_decode, make_case, oracle_decode, rel_err
+from _cases import TOL, WindowSession, gpu_decode, make_case, oracle_decode, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -42,3 +42,31 @@ def test_c4_llama_262k_batch8_with_window():
 def test_c5_composed_int8_evicted():
     cfg = synth.CONFIGS["c5_composed"]
     run(cfg, 5, [0, 11])
+
+
+def test_c4_llama_262k_batch8_128_step_protocol():
+    """The long-context workload as configured: batch 8, 262144 cached tokens,
+    32 layers, 256 of 4096 blocks per layer and step (a fresh selection and
+    query every step), 128 consecutive decode steps, each appending the new
+    token's exact key and value to every layer's recent-window buffer of 1024
+    (project site, Figure 5 caption: 128 decode steps; explainer,
+    prefill/decode paragraph: new tokens stored exactly), so step s attends
+    s + 1 window tokens. Parity with the float64 oracle at steps 0 and 127 on
+    the first and last layer of the first and last sequence; stats exact."""
+    cfg = synth.CONFIGS["c4_llama_262k"]
+    s = WindowSession(cfg, cfg.win_cap, biases=False)
+    for step in range(cfg.steps):
+        st = s.stage(step)
+        s.launch()
+        if step in (0, cfg.steps - 1):
+            torch.cuda.synchronize()
+            assert s.count.tolist() == [step + 1] * cfg.n_layers
+            for l in (0, cfg.n_layers - 1):
+                for b in (0, cfg.batch - 1):
+                    ref, rstats = s.oracle(l, step + 1, st, batch_index=b)
+                    err = rel_err(s.outs[l][b:b + 1].float().cpu().numpy(), ref)
+                    print(f"step {step} layer {l} b={b}: rel_err={err:.2e}", flush=True)
+                    assert err <= TOL[cfg.act]
+                    np.testing.assert_array_equal(s.stats[l][b:b + 1].cpu().numpy(), rstats)
+    torch.cuda.synchronize()
+    assert s.count.tolist() == [cfg.steps] * cfg.n_layers
