@@ -1,6 +1,6 @@
 """Build liblowram.so for gfx950 in-tree with hipcc (no GPU needed).
 
-Usage: python -m long_context_decode_lowram_amd.build [-v]
+Usage: python -m long_context_decode_lowram_amd.build [-v] [--sanitize]
 """
 import concurrent.futures
 import os
@@ -60,5 +60,52 @@ def build(verbose=False):
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
+# layer (api.cpp: argument checks, workspace carving, launch sequence), linked
+# with the normal kernel objects. Device code is built without sanitizers.
+SAN_HOST = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(BUILD, "san", "liblowram.so")
+
+
+def asan_runtime():
+    """The compiler's shared ASan runtime, which must be preloaded into the
+    process that loads the sanitized library."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("shared ASan runtime not found")
+    return path
+
+
+def build_sanitized(verbose=False):
+    """Compile api.cpp with host sanitizers and link it with the other
+    objects into _build/san/liblowram.so (run build() first)."""
+    os.makedirs(os.path.join(BUILD, "san"), exist_ok=True)
+    obj = os.path.join(BUILD, "san", "api.o")
+    cmd = [hipcc(), *[f for f in COMMON if f != "-O3"], *SAN_HOST, "-c", os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized api.cpp failed:\n{r.stdout}\n{r.stderr}")
+    others = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "api.cpp"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: missing {missing}")
+    link = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", obj, *others, "-Xarch_host", "-fsanitize=address",
+            "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB]
+    if verbose:
+        print(" ".join(cmd), "\n", " ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
