@@ -77,9 +77,38 @@ def test_mid_two_groups_all_segments():
     print(f"p_mid: max V_hat rel err {worst:.2e}", flush=True)
 
 
-def test_full_shape_sampled_segments():
+@pytest.fixture(scope="module")
+def p_c5_ranked():
     pc = synth.PREFILL_CONFIGS["p_c5"]                    # 32 x 131072 x 8 x 128
     x, out = _launch(pc, pc.res_dtype)
+    yield pc, x, out
+    del x, out
+    torch.cuda.empty_cache()
+
+
+def test_full_shape_sampled_v_hat(p_c5_ranked):
+    """V_hat against the float64 predictor on sampled (layer, head) segments,
+    with the exact ranking of those segments."""
+    pc, x, out = p_c5_ranked
     for l, h in ((0, 0), (17, 5), (31, 7)):
         rel = _check_segment(x, out, pc, pc.res_dtype, l, h)
         print(f"p_c5 layer {l} head {h}: V_hat rel err {rel:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_full_shape_every_segment_ranked_exactly(p_c5_ranked, part):
+    """Every (layer, head) segment at the full shape: errors, index set, block
+    pointers and int8 residuals exactly the oracle's ranking of V against the
+    V_hat the library returns, one layer (all heads) at a time; a quarter of
+    the 32 layers per test."""
+    pc, x, out = p_c5_ranked
+    for l in range(8 * part, 8 * part + 8):
+        v = _np(x["v"][l:l + 1])
+        vh = out["v_hat"][l:l + 1].cpu().numpy().astype(np.float64)
+        ref = oracle.prefill_rank(v, vh, pc.n_res, pc.block, pc.res_dtype)
+        np.testing.assert_array_equal(out["err"][l].cpu().numpy(), ref["err"][0])
+        np.testing.assert_array_equal(out["idx"][l].cpu().numpy(), ref["idx"][0])
+        np.testing.assert_array_equal(out["ptr"][l].cpu().numpy(), ref["ptr"][0])
+        np.testing.assert_array_equal(out["val"][l].cpu().numpy(), ref["val"][0])
+        np.testing.assert_array_equal(out["scale"][l].cpu().numpy(), ref["scale"][0])
+        print(f"layer {l}: 8 heads exact", flush=True)

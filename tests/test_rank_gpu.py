@@ -74,23 +74,41 @@ def test_two_bit_ties_and_zero_rows():
     assert q.tolist() == [2] * 128 and got["scale"][0, 0, 1].item() == 0.0
 
 
-def test_c5_full_shape_sampled_segments():
-    """32 slices x 131072 tokens x 8 heads, bf16 in, int8 residuals, k = 13107:
-    every segment checked structurally, three checked exactly."""
+@pytest.fixture(scope="module")
+def c5_ranked():
+    """32 slices x 131072 tokens x 8 heads, bf16 in, int8 residuals,
+    k = 13107, ranked once on the GPU for the tests below."""
     rc = synth.RANK_C5
     torch.manual_seed(0)
     v, vh = synth.gen_rank_inputs(rc, "cuda")
     import long_context_decode_lowram_amd as L
     out = L.rank_residuals(v, vh, rc.n_res, "i8", want_err=True)
     torch.cuda.synchronize()
+    yield rc, v, vh, out
+    del v, vh, out
+    torch.cuda.empty_cache()
+
+
+def test_c5_full_shape_structure(c5_ranked):
+    rc, v, vh, out = c5_ranked
     idx, ptr = out["idx"], out["ptr"]
     k = rc.n_res
     assert bool((idx[..., 1:] > idx[..., :-1]).all())
     assert bool((idx >= 0).all()) and bool((idx < rc.ctx_len).all())
     assert bool((ptr[..., -1] == k).all()) and bool((ptr[..., 0] == 0).all())
     assert torch.equal(ptr, synth.block_ptr_from_idx(idx, rc.ctx_len, 64))
-    segs = [(0, 0), (17, 5), (31, 7)]
-    for sl, h in segs:
-        ref = oracle.rank_residuals(np64(v[sl:sl + 1, :, h:h + 1]), np64(vh[sl:sl + 1, :, h:h + 1]), k, 64, "i8")
-        got = {n: (None if t is None else t[sl:sl + 1, h:h + 1].cpu()) for n, t in out.items()}
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_c5_full_shape_every_segment_exact(c5_ranked, part):
+    """Index-exact at the full ranking shape: every (slice, head) segment's
+    errors, index set, block pointers, int8 codes and scales against the
+    oracle, one slice (all eight heads) at a time; a quarter of the 32 slices
+    per test."""
+    rc, v, vh, out = c5_ranked
+    k = rc.n_res
+    for sl in range(8 * part, 8 * part + 8):
+        ref = oracle.rank_residuals(np64(v[sl:sl + 1]), np64(vh[sl:sl + 1]), k, 64, "i8")
+        got = {n: (None if t is None else t[sl:sl + 1].cpu()) for n, t in out.items()}
         compare(got, ref, "i8")
+        print(f"slice {sl}: 8 heads exact", flush=True)
