@@ -163,6 +163,28 @@ int lowram_decode_step(const lowram_decode_args *args, void *stream);
 size_t lowram_decode_workspace_size(const lowram_decode_args *args);
 
 /*
+ * lowram_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, kernels and results as
+ * lowram_decode_step; workspace and workspace_bytes are ignored. The step's
+ * scratch (attended-block lists, split-K partial records, counts) lives in a
+ * static device array of LOWRAM_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends; the call itself allocates
+ * and frees nothing. Its device address is looked up once per device, at the
+ * first call on that device (make that first call outside graph capture).
+ * Shapes whose lowram_decode_workspace_size exceeds the array are rejected
+ * with LOWRAM_ERR_WORKSPACE before any HIP call (e.g. batch 12 with every one
+ * of 2048 blocks a candidate; the 131072- and 262144-token shapes with a
+ * selection of 256 blocks fit up to batch 8 and beyond). Nothing in the
+ * scratch has to start at zero: every value the kernels read was written
+ * earlier in the same call. All calls on one GPU share its array, so calls
+ * that may overlap there (on different streams, or a combine_stream that
+ * overlaps the next call) race: order them on one stream.
+ */
+#define LOWRAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int lowram_decode_step_noalloc(const lowram_decode_args *args, void *stream);
+
+/*
  * Validate mode (flags & LOWRAM_FLAG_VALIDATE, check_flags non-NULL). Before
  * the step's kernels, one more kernel reads the device-side index data the
  * host cannot see and ORs a LOWRAM_CHECK_* bit into *check_flags for every

@@ -19,6 +19,7 @@ F32, BF16, I8, I2 = 0, 1, 2, 3
 FLAG_GENERIC, FLAG_VALIDATE = 1, 2
 CHECK_SEL_ORDER, CHECK_RES_RANGE, CHECK_RES_ORDER, CHECK_RES_PTR, CHECK_WIN_LEN = 1, 2, 4, 8, 16
 BLOCK = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # uint8 tensors carry 2-bit codes packed four per byte (residual rows [.., d/4]).
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.uint8: I2}
@@ -100,6 +101,8 @@ def lib():
         L.lowram_decode_step.restype = ctypes.c_int
         L.lowram_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.lowram_decode_workspace_size.restype = ctypes.c_size_t
+        L.lowram_decode_step_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _p]
+        L.lowram_decode_step_noalloc.restype = ctypes.c_int
         L.lowram_window_append.argtypes = [ctypes.POINTER(WindowArgs), _p]
         L.lowram_window_append.restype = ctypes.c_int
         L.lowram_rank_residuals.argtypes = [ctypes.POINTER(RankArgs), _p]
@@ -301,6 +304,14 @@ def decode_workspace_size(args):
 
 def decode_launch(args, stream=None):
     rc = lib().lowram_decode_step(ctypes.byref(args), _stream(stream))
+    if rc != OK:
+        raise LowramError(rc, last_error())
+
+
+def decode_launch_noalloc(args, stream=None):
+    """lowram_decode_step_noalloc: the step with the library's static scratch
+    array in place of a workspace (args.workspace is ignored)."""
+    rc = lib().lowram_decode_step_noalloc(ctypes.byref(args), _stream(stream))
     if rc != OK:
         raise LowramError(rc, last_error())
 

@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -276,6 +278,37 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(LOWRAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+int decode_launch_all(const lowram_decode_args* a, const DecodePlan& pl, char* ws, void* stream);
+
+// Scratch of lowram_decode_step_noalloc: a static device array, one copy per
+// GPU, alive until the process ends. In host code its name is only a
+// stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device (with that device current) at
+// the first call on it and kept here.
+static __device__ __align__(256) unsigned char scratch[LOWRAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LOWRAM_ERR_UNSUPPORTED, "device %d above the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255) != 0)
+            return fail(LOWRAM_ERR_HIP, "scratch array address %p is not 256-byte aligned", ptr);
+        g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return LOWRAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,7 +340,33 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     if (rc != LOWRAM_OK) return rc;
     rc = check_decode_ptrs(a, pl);
     if (rc != LOWRAM_OK) return rc;
+    return decode_launch_all(a, pl, static_cast<char*>(a->workspace), stream);
+}
 
+int lowram_decode_step_noalloc(const lowram_decode_args* a, void* stream) {
+    g_err[0] = 0;
+    DecodePlan pl;
+    int rc = plan_decode(a, &pl);
+    if (rc != LOWRAM_OK) return rc;
+    if (pl.total > (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES)
+        return fail(LOWRAM_ERR_WORKSPACE, "these shapes need %zu bytes of scratch, above the %zu of the static array "
+                    "(use lowram_decode_step with a workspace)", pl.total, (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES);
+    lowram_decode_args chk = *a;          // the caller's workspace fields are ignored
+    chk.workspace = reinterpret_cast<void*>(uintptr_t(256));
+    chk.workspace_bytes = LOWRAM_NOALLOC_SCRATCH_BYTES;
+    rc = check_decode_ptrs(&chk, pl);     // every host check before the first HIP call
+    if (rc != LOWRAM_OK) return rc;
+    char* ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc != LOWRAM_OK) return rc;
+    return decode_launch_all(a, pl, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_launch_all(const lowram_decode_args* a, const DecodePlan& pl, char* ws, void* stream) {
     DecodeParams p{};
     p.batch = a->batch; p.ctx_len = a->ctx_len; p.n_q = a->n_q_heads; p.n_kv = a->n_kv_heads;
     p.group = a->n_q_heads / a->n_kv_heads; p.rank = a->rank; p.hidden = a->mlp_hidden; p.n_res = a->n_res;
@@ -319,7 +378,6 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     p.win_k = a->win_k; p.win_v = a->win_v; p.out = a->out; p.stats = a->stats; p.n_sel = a->n_sel;
     p.win_len_dev = a->win_len_dev;
     p.check_flags = (a->flags & LOWRAM_FLAG_VALIDATE) ? a->check_flags : nullptr;
-    char* ws = static_cast<char*>(a->workspace);
     p.att_list = reinterpret_cast<int32_t*>(ws + pl.off_list);
     p.att_count = reinterpret_cast<int32_t*>(ws + pl.off_count);
     p.partials = reinterpret_cast<float*>(ws + pl.off_part);
@@ -361,6 +419,10 @@ int lowram_decode_step(const lowram_decode_args* a, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return LOWRAM_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int lowram_window_append(const lowram_window_args* a, void* stream) {
     g_err[0] = 0;
