@@ -251,7 +251,7 @@ int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
     p.n_layers = a->n_layers; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads; p.hidden = a->mlp_hidden;
     p.n_steps = a->n_steps; p.lr = a->lr;
     p.n_probs = a->n_layers * a->n_kv_heads;
-    p.m_tiles = (a->ctx_len + 127) / 128;
+    p.m_tiles = (a->ctx_len + 63) / 64;   // 64-token tiles of the fused products
     const int tiles = p.n_probs * (a->mlp_hidden / 128);
     int nc = (2048 + tiles - 1) / tiles;
     const int maxc = (a->ctx_len + 31) / 32;

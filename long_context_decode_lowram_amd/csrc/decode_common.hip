@@ -164,8 +164,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     extern __shared__ float sm[];
     float* sw = sm;                       // [win_len]
     float* oc = sw + p.win_len;           // [H + 128]
-    float* qs = oc + nf;                  // [128]
-    float* red = qs + kHeadDim;           // [8 + 3 * 128]: block reductions, then the W2 quarter sums
+    float* red = oc + nf + kHeadDim;      // [8 + 3 * 128]: block reductions, then the W2 quarter sums
     float* part = red + 8 + 3 * kHeadDim; // [8][H + 128]: the waves' record sums
     float* wml = part + kCombWaves * nf;  // [8][2]: each wave's max and weight sum
 
@@ -230,20 +229,28 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
         }
     }
 
-    // Window tokens: exact keys and values, scored here.
-    for (int f = tid; f < kHeadDim; f += blockDim.x)
-        qs[f] = ld<ACT>(p.q, ((int64_t)b * p.n_q + j) * kHeadDim + f);
-    __syncthreads();
+    // Window tokens: exact keys and values, scored here. Wave wv scores the
+    // tokens wv, wv + 8, ..., two at a time: lane l holds features 2l and
+    // 2l + 1 of the query and reads the same two of each key row (the wave
+    // reads a row's 128 features in one coalesced pass), then the wave sums.
+    const int64_t q_row = ((int64_t)b * p.n_q + j) * kHeadDim;
+    const float q0 = ld<ACT>(p.q, q_row + 2 * lane), q1 = ld<ACT>(p.q, q_row + 2 * lane + 1);
     float mx = -INFINITY;
-    for (int u = tid; u < nw; u += blockDim.x) {
-        const int64_t row = (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim;
-        float acc = 0.f;
-        for (int n = 0; n < kHeadDim; ++n) acc += qs[n] * ld<ACT>(p.win_k, row + n);
-        acc *= p.scale;
-        sw[u] = acc;
-        mx = fmaxf(mx, acc);
+    for (int u0 = wv; u0 < nw; u0 += 2 * kCombWaves) {
+        const int u1 = u0 + kCombWaves;
+        const int64_t r0 = (((int64_t)b * p.win_cap + u0) * p.n_kv + h) * kHeadDim + 2 * lane;
+        const int64_t r1 = (((int64_t)b * p.win_cap + (u1 < nw ? u1 : u0)) * p.n_kv + h) * kHeadDim + 2 * lane;
+        float s0 = q0 * ld<ACT>(p.win_k, r0) + q1 * ld<ACT>(p.win_k, r0 + 1);
+        float s1 = q0 * ld<ACT>(p.win_k, r1) + q1 * ld<ACT>(p.win_k, r1 + 1);
+        s0 = wave_sum(s0) * p.scale;
+        s1 = wave_sum(s1) * p.scale;
+        if (lane == 0) {
+            sw[u0] = s0;
+            if (u1 < nw) sw[u1] = s1;
+        }
+        mx = fmaxf(mx, u1 < nw ? fmaxf(s0, s1) : s0);
     }
-    float M = block_reduce(mx, red, true);     // its barriers also publish part and wml
+    float M = block_reduce(mx, red, true);     // its barriers also publish part, wml and sw
     for (int w8 = 0; w8 < kCombWaves; ++w8) M = fmaxf(M, wml[2 * w8]);
 
     const int64_t out_row = ((int64_t)b * p.n_q + j) * kHeadDim;
@@ -291,11 +298,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
             const int i1 = quarter == 3 ? H : i0 + H / 4;
             for (int i = i0; i < i1; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
         }
+        // Window values: quarter q takes the tokens u = q (mod 4); each token's
+        // row is read by 128 threads, coalesced.
+        for (int u = quarter; u < nw; u += 4)
+            y += sw[u] * ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f);
         if (quarter == 3) {
             y += oc[H + f];
             if (p.b2) y += Lt * ld<ACT>(p.b2, ((int64_t)b * p.n_kv + h) * kHeadDim + f);
-            for (int u = 0; u < nw; ++u)
-                y += sw[u] * ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f);
         }
         if (quarter > 0) red[8 + (quarter - 1) * kHeadDim + f] = y;
         __syncthreads();

@@ -6,10 +6,9 @@
 // per context at prefill. Loss L = (1 / T) sum_t ||v_hat_t - v_t||^2, plain
 // gradient descent on W1, b1, W2, b2 (W_lin fixed). Per step and problem
 // (layer, KV head), with weights stored output-major:
-//   H = gelu(K W1^T + b1)                              fit_nt_kernel<kEpiZ>
-//   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           fit_nt_kernel<kEpiG>   (+ loss, sum_t G)
-//   dZ = (G W2) * gelu'(K W1^T + b1)                   fit_nt_kernel<kEpiDz>  (+ sum_t dZ; the
-//                                                      pre-activations are recomputed, not stored)
+//   H = gelu(K W1^T + b1)                              fit_fused_kernel, one workgroup per
+//   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           (problem, 64-token tile) (+ loss, sum_t G,
+//   dZ = (G W2) * gelu'(K W1^T + b1)                   sum_t dZ; the pre-activations are recomputed)
 //   dW2 = G^T H, dW1 = dZ^T K                          fit_tn_kernel (token chunks)
 //   theta -= lr dL/dtheta                              fit_update_kernel
 // Products on bf16 MFMA with fp32 sums; the parameters are fp32 masters with
@@ -23,14 +22,11 @@
 
 namespace lowram {
 
-constexpr int kFM = 128;                 // tokens per tile (MFMA B operand rows)
-constexpr int kFN = 128;                 // outputs per tile (MFMA A operand rows)
+constexpr int kFN = 128;                 // outputs per product tile (MFMA A operand rows)
 constexpr int kFK = 64;                  // contraction step
 constexpr int kFRowB = kFK * 2;          // 128-byte LDS rows
-constexpr int kFOp0 = kFN * kFRowB;      // 16 KB
-constexpr int kFStage = (kFN + kFM) * kFRowB;   // 32 KB
+constexpr int kFOp0 = kFN * kFRowB;      // 16 KB: a weight stage buffer
 constexpr int kFThreads = 512;
-enum : int { kEpiZ = 0, kEpiG = 1, kEpiDz = 2 };
 
 __device__ __forceinline__ uint32_t fslot(int row, int piece) {
     return (uint32_t)(row * kFRowB + ((piece ^ (row & 7)) << 4));
@@ -55,226 +51,227 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// One segment of a contraction: op1 rows are tokens of `a` (row stride lda
-// elements), op0 rows are outputs of `b` (row stride ldb), kdim contiguous.
-struct NtSeg {
-    const __bf16* a; int lda;
-    const __bf16* b; int ldb;
-    int kdim;
-};
+// --------------------------------------------------------------- fused
+// The three token-tile products of a gradient step in one workgroup per
+// (problem, 64-token tile), so the tile's keys are read from HBM once and H
+// and G are never read back from it:
+//   for each 128-wide hidden tile u:  Z_u = K W1_u^T;  H_u = gelu(Z_u + b1_u)
+//                                     (stored for dW2, and kept in LDS);
+//                                     V_hat += H_u W2_u^T
+//   V_hat += K W_lin^T;  G = (2 / T)(V_hat + b2 - V)   (stored, kept in LDS)
+//   for each hidden tile u:           dZ_u = (G W2_u) * gelu'(K W1_u^T + b1_u)
+// (BACKWARD = false stops after G: the loss after the last step). The keys and
+// H_u (then G, in the same place) stay resident in LDS as the token operand
+// ([64 tokens][128] bf16, two 64-wide halves in swizzled 128-byte rows); the
+// weight rows stream through two 16 KB stage buffers, 64 columns of the
+// contraction at a time. 66 KB of LDS, so two workgroups share a CU and hide
+// each other's copy latency. Eight waves: wave w covers outputs 64 (w & 1)
+// .. + 63 and tokens 16 (w >> 1) .. + 15; lane (l16, g4) ends with outputs
+// n .. n + 3 (n = 4 g4 + 16 a) of token l16. H, G, dZ, the column sums and
+// the loss partials have the values and layout the weight-gradient products
+// and the update read. Workgroups of one problem run on one XCD at a time
+// (its L2 then holds the problem's weights): XCD x takes problems x, x + 8,
+// ..., each problem's tiles in turn.
+constexpr int kFTok = 64;                       // tokens per tile
+constexpr int kFHalf = kFTok * kFRowB;          // one 64-wide half of a resident tile: 8 KB
 
-// NT product over up to two segments for a 128-token x 128-output tile of
-// problem blockIdx.y, then the fused epilogue. Grid (m_tiles * n_tiles, P);
-// 64 KB of LDS (two workgroups per CU), 32 KB for EPI_Z (three). Eight
-// waves: wave w covers
-// outputs 64 (w & 1) .. and tokens 32 (w >> 1) ..; lane (l16, g4) ends with
-// outputs n .. n + 3 (n = 4 g4 + 16 nt) of token l16 + 16 tt of its block.
-template <int EPI>
-__global__ __launch_bounds__(kFThreads, 2) void fit_nt_kernel(FitParams p) {
-    // EPI_Z (two contraction steps) keeps one stage buffer: 32 KB of LDS, so
-    // three workgroups share a CU (its 65 registers allow three as well) and
-    // hide each other's load latency, which pays more than overlapping its
-    // second copy with its first step (measured: the fit call 118.6 -> 113.5
-    // ms). The others double-buffer.
-    constexpr int kNst = EPI == kEpiZ ? 1 : 2;
-    __shared__ __attribute__((aligned(16))) unsigned char stg[kNst * kFStage];
-    unsigned char* const st0 = stg;
-    unsigned char* const st1 = stg + (kNst - 1) * kFStage;
-    __shared__ float red_cs[4][256];
+template <bool BACKWARD>
+__global__ __launch_bounds__(kFThreads, 2) void fit_fused_kernel(FitParams p, int n_per_xcd) {
+    __shared__ __attribute__((aligned(16))) unsigned char kt[2 * kFHalf];   // keys of the tile
+    __shared__ __attribute__((aligned(16))) unsigned char ht[2 * kFHalf];   // H_u, then G
+    __shared__ __attribute__((aligned(16))) unsigned char ws0[kFOp0], ws1[kFOp0];
+    __shared__ float red_cs[4][kFN];
     __shared__ float red_loss[8];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q = blockIdx.y;
+    // blockIdx -> (problem, token tile): XCD x = blockIdx % 8 walks its own
+    // list of (problem, tile) pairs in order.
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= n_per_xcd) return;
+    const int q = (local / p.m_tiles) * 8 + xcd;
+    const int mt = local - (local / p.m_tiles) * p.m_tiles;
+    if (q >= p.n_probs) return;
     const int l = q / p.n_kv, h = q - l * p.n_kv;
     const int d = kHeadDim, H = p.hidden, T = p.ctx_len;
-    const int N = EPI == kEpiG ? d : H;
-    const int n_tiles = N / kFN;
-    // The output tiles of one token tile sit 8 blocks apart, so that they run
-    // on the same XCD (blocks go round-robin over the 8) and share its L2
-    // copy of the token rows. Blocks past the last token tile exit.
-    const int grp = blockIdx.x / (8 * n_tiles), rem = blockIdx.x - grp * 8 * n_tiles;
-    const int ntile = rem >> 3, mt = grp * 8 + (rem & 7);
-    if (mt >= p.m_tiles) return;
-    const int t0 = mt * kFM, n0 = ntile * kFN;
+    const int t0 = mt * kFTok;
     const int ldkv = p.n_kv * d;
-    const __bf16* kq = p.keys + (int64_t)l * T * ldkv + h * d;
     const int64_t th = (int64_t)q * T * H, td = (int64_t)q * T * d;
-
-    // Segments of the contraction; EPI_G sums two into one accumulator,
-    // EPI_DZ runs two separate products (pre-activations, then G W2).
-    NtSeg seg[2];
-    int n_seg = 1;
-    const NtSeg zseg = NtSeg{kq, ldkv, p.w1b + (int64_t)q * H * d, d, d};
-    if (EPI == kEpiZ) {
-        seg[0] = zseg;
-    } else if (EPI == kEpiG) {
-        seg[0] = NtSeg{kq, ldkv, p.w_lin + (int64_t)q * d * d, d, d};
-        seg[1] = NtSeg{p.hb + th, H, p.w2b + (int64_t)q * d * H, H, H};
-        n_seg = 2;
-    } else {
-        seg[0] = NtSeg{p.gb + td, d, p.w2tb + (int64_t)q * H * d, d, d};
-    }
-
-    // Direct copies: op0 (128 output rows) and op1 (128 token rows, zeros
-    // past T) by 2 copies per wave each; lane i lands in row 8 c + i / 8,
-    // slot i % 8, and fetches piece (i % 8) ^ (row % 8).
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int wn = (w & 1) * 64, wt = (w >> 1) * 16;
     const int dma_row = lane >> 3;
     const uint32_t dma_piece = (uint32_t)(((lane & 7) ^ dma_row) * 16);
-    auto dma = [&](const NtSeg* sgs, int steps0, int s, unsigned char* stage) {
-        const int sg = s < steps0 ? 0 : 1;
-        const int k0 = (s - (sg ? steps0 : 0)) * kFK;
-        const NtSeg& g = sgs[sg];
-        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(g.b + (int64_t)n0 * g.ldb, (uint32_t)(kFN * g.ldb * 2));
-        const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(g.a + (int64_t)t0 * g.lda,
-                                                      (uint32_t)((int64_t)max(0, T - t0) * g.lda * 2));
+
+    // The keys of the tile, both 64-wide halves (rows past T read as zeros);
+    // read once: non-temporal. Wave w copies rows 8 w .. 8 w + 7.
+    {
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.keys + (int64_t)l * T * ldkv + h * d + (int64_t)t0 * ldkv,
+                                                      (uint32_t)((int64_t)max(0, T - t0) * ldkv * 2));
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+            dma16<kNonTemporal>(rk, kt + half * kFHalf + w * 8 * kFRowB,
+                                (uint32_t)(((w * 8 + dma_row) * ldkv + half * kFK) * 2) + dma_piece, 0u);
+    }
+    // 128 weight rows (outputs n0 .. n0 + 127 of a row-major matrix with row
+    // stride ldw), contraction columns k0 .. k0 + 63, into a stage buffer.
+    auto dma_w = [&](const __bf16* wmat, int ldw, int n0, int k0, unsigned char* stage) {
+        const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wmat + (int64_t)n0 * ldw, (uint32_t)(kFN * ldw * 2));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int r0 = (w * 2 + c) * 8;
-            dma16(rb, stage + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * g.ldb + k0) * 2) + dma_piece, 0u);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int r0 = (w * 2 + c) * 8;
-            dma16(ra, stage + kFOp0 + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * g.lda + k0) * 2) + dma_piece, 0u);
+            dma16(rw, stage + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * ldw + k0) * 2) + dma_piece, 0u);
         }
     };
-
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int wn = (w & 1) * 64, wt = (w >> 1) * 32;
-    auto mma = [&](const unsigned char* stage, f32x4 (&acc)[4][2]) {
+    auto mma = [&](const unsigned char* op0, const unsigned char* op1, f32x4 (&acc)[4]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 af[4], bf[2];
+            bf16x8 af[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) af[a] = lds16(stage, fslot(wn + a * 16 + l16, ks * 4 + g4));
+            for (int a = 0; a < 4; ++a) af[a] = lds16(op0, fslot(wn + a * 16 + l16, ks * 4 + g4));
+            const bf16x8 bf = lds16(op1, fslot(wt + l16, ks * 4 + g4));
 #pragma unroll
-            for (int b = 0; b < 2; ++b) bf[b] = lds16(stage + kFOp0, fslot(wt + b * 16 + l16, ks * 4 + g4));
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma(af[a], bf[b], acc[a][b]);
+            for (int a = 0; a < 4; ++a) acc[a] = mfma(af[a], bf, acc[a]);
         }
     };
-    // acc = sum over the segments' contraction, copies one 64-wide step ahead
-    // into two static stage buffers.
-    auto contract = [&](const NtSeg* sgs, int ns, f32x4 (&acc)[4][2]) {
+    // acc (+)= W[n0 .. n0 + 127][k0 .. k0 + 127] . tok^T over a resident
+    // 128-wide token tile (two halves): two 64-wide steps, weights double
+    // buffered. The barriers also publish resident-tile rows written before
+    // the call, and on return every wave is done with the stage buffers and
+    // with tok.
+    auto contract = [&](const __bf16* wmat, int ldw, int n0, int k0, const unsigned char* tok, f32x4 (&acc)[4],
+                        bool zero) {
+        if (zero) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        dma_w(wmat, ldw, n0, k0, ws0);
+        dma_w(wmat, ldw, n0, k0 + kFK, ws1);
+        wait_vmcnt<2>();                    // this wave's step 0 copies (the older two) have landed
+        barrier_lds();                      // (step 1's copies stay in flight)
+        mma(ws0, tok, acc);
+        wait_vmcnt<0>();
+        barrier_lds();
+        mma(ws1, tok + kFHalf, acc);
+        barrier_lds();
+    };
+    // Store a lane's four consecutive outputs (as bf16) of token row r into a
+    // resident tile: output n lands in half n / 64, piece (n % 64) / 8.
+    auto put = [&](unsigned char* tile, int r, int n, u32x2 v) {
+        const int hf = n >> 6, nn = n & 63;
+        *reinterpret_cast<u32x2*>(tile + hf * kFHalf + fslot(r, nn >> 3) + (nn & 7) * 2) = v;
+    };
+    // Column sums of a 128-output tile over this tile's tokens, in a fixed
+    // order: lanes l16 = 0..15 share outputs, then the 4 token waves of an
+    // output half meet in LDS.
+    auto colsum = [&](float (&cs)[4][4], float* dst) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int steps0 = sgs[0].kdim / kFK;
-        const int n_steps = steps0 + (ns == 2 ? sgs[1].kdim / kFK : 0);
-        dma(sgs, steps0, 0, st0);
-        if constexpr (kNst == 1) {
-            for (int s = 0; s < n_steps; ++s) {
-                wait_vmcnt<0>();
-                barrier_lds();
-                mma(st0, acc);
-                if (s + 1 < n_steps) {
-                    barrier_lds();       // every wave is done reading the buffer
-                    dma(sgs, steps0, s + 1, st0);
-                }
+            for (int v = 0; v < 4; ++v) {
+                float x = cs[a][v];
+                for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+                cs[a][v] = x;
             }
-        } else {
-            auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-                wait_vmcnt<0>();
-                barrier_lds();
-                if (s + 1 < n_steps) dma(sgs, steps0, s + 1, nxt);
-                mma(cur, acc);
-            };
-            for (int s = 0; s < n_steps; s += 2) {
-                step(s, st0, st1);
-                if (s + 1 < n_steps) step(s + 1, st1, st0);
-            }
+        if (l16 == 0) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red_cs[w >> 1][wn + a * 16 + g4 * 4 + v] = cs[a][v];
         }
-        wait_vmcnt<0>();
+        __syncthreads();
+        if (tid < kFN) dst[tid] = ((red_cs[0][tid] + red_cs[1][tid]) + red_cs[2][tid]) + red_cs[3][tid];
     };
-    f32x4 acc[4][2], accz[4][2];
-    if (EPI == kEpiDz) {
-        contract(&zseg, 1, accz);
-        barrier_lds();       // every wave is done with the stage buffers
-    }
-    contract(seg, n_seg, acc);
-
-    // Epilogue.
-    float cs[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) cs[a][v] = 0.f;
-    float loss = 0.f;
     const float gscale = 2.0f / (float)T;
+    const __bf16* w1b = p.w1b + (int64_t)q * H * d;
+    const __bf16* w2b = p.w2b + (int64_t)q * d * H;
+    const __bf16* w2tb = p.w2tb + (int64_t)q * H * d;
+    const __bf16* wl = p.w_lin + (int64_t)q * d * d;
+    const float* b1 = p.b1 + (int64_t)q * H;
+    const float* b2 = p.b2 + (int64_t)q * d;
+    const int r = wt + l16, t = t0 + r;          // this lane's token row
+    f32x4 acc[4], accv[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int t = t0 + wt + b * 16 + l16;
-        if (t >= T) continue;
+    for (int a = 0; a < 4; ++a) accv[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- forward: H_u and V_hat
+    for (int u0 = 0; u0 < H; u0 += kFN) {
+        contract(w1b, d, u0, 0, kt, acc, true);                 // Z_u
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const int n = n0 + wn + a * 16 + g4 * 4;
-            const f32x4 x = acc[a][b];
-            if (EPI == kEpiZ) {
-                const float* bb = p.b1 + (int64_t)q * H + n;
-                float hv[4];
+            const int n = wn + a * 16 + g4 * 4;
+            u32x2 hv = {0u, 0u};
+            if (t < T) {
+                float v4[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) hv[v] = gelu_f(x[v] + bb[v]);
-                *reinterpret_cast<u32x2*>(p.hb + th + (int64_t)t * H + n) =
-                    u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-            } else if (EPI == kEpiG) {
-                const float* bb = p.b2 + (int64_t)q * d + n;
+                for (int v = 0; v < 4; ++v) v4[v] = gelu_f(acc[a][v] + b1[u0 + n + v]);
+                hv = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+                *reinterpret_cast<u32x2*>(p.hb + th + (int64_t)t * H + u0 + n) = hv;
+            }
+            put(ht, r, n, hv);
+        }
+        contract(w2b, H, 0, u0, ht, accv, false);              // V_hat += H_u W2_u^T
+    }
+    contract(wl, d, 0, 0, kt, accv, false);                     // V_hat += K W_lin^T
+
+    // ---- G (into the H tile's place: its last reader has passed the barrier
+    // that ends the contraction above), loss, column sums of G
+    {
+        float cs[4][4];
+        float loss = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int n = wn + a * 16 + g4 * 4;
+            u32x2 gv = {0u, 0u};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cs[a][v] = 0.f;
+            if (t < T) {
                 const u32x2 vv = *reinterpret_cast<const u32x2*>(p.v + ((int64_t)l * T + t) * ldkv + h * d + n);
                 const float vt[4] = {bf16_lo(vv[0]), bf16_hi(vv[0]), bf16_lo(vv[1]), bf16_hi(vv[1])};
                 float g[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float e = x[v] + bb[v] - vt[v];
+                    const float e = accv[a][v] + b2[n + v] - vt[v];
                     loss = fmaf(e, e, loss);
                     g[v] = gscale * e;
-                    cs[a][v] += g[v];
+                    cs[a][v] = g[v];
                 }
-                *reinterpret_cast<u32x2*>(p.gb + td + (int64_t)t * d + n) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-            } else {
-                const float* bb = p.b1 + (int64_t)q * H + n;
-                const f32x4 zx = accz[a][b];
+                gv = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+                *reinterpret_cast<u32x2*>(p.gb + td + (int64_t)t * d + n) = gv;
+            }
+            put(ht, r, n, gv);
+        }
+        for (int off = 32; off > 0; off >>= 1) loss += __shfl_xor(loss, off, kWave);
+        if (lane == 0) red_loss[w] = loss;
+        colsum(cs, p.cs_g + ((int64_t)q * p.m_tiles + mt) * d);
+        if (tid == 0) {
+            float sum = 0.f;
+            for (int i = 0; i < 8; ++i) sum += red_loss[i];
+            p.loss_p[(int64_t)q * p.m_tiles + mt] = sum;
+        }
+    }
+    if (!BACKWARD) return;
+
+    // ---- backward: dZ_u = (G W2_u) * gelu'(Z_u + b1_u), column sums of dZ
+    for (int u0 = 0; u0 < H; u0 += kFN) {
+        contract(w1b, d, u0, 0, kt, accv, true);                // Z_u again (cheaper than keeping every tile)
+        contract(w2tb, d, u0, 0, ht, acc, true);                // G W2_u
+        float cs[4][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int n = wn + a * 16 + g4 * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cs[a][v] = 0.f;
+            if (t < T) {
                 float dz[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    dz[v] = x[v] * gelu_grad_f(zx[v] + bb[v]);
-                    cs[a][v] += dz[v];
+                    dz[v] = acc[a][v] * gelu_grad_f(accv[a][v] + b1[u0 + n + v]);
+                    cs[a][v] = dz[v];
                 }
-                *reinterpret_cast<u32x2*>(p.dzb + th + (int64_t)t * H + n) = u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
+                *reinterpret_cast<u32x2*>(p.dzb + th + (int64_t)t * H + u0 + n) =
+                    u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
             }
         }
-    }
-    if (EPI == kEpiZ) return;
-    // Column sums over this tile's tokens: lanes l16 = 0..15 share outputs;
-    // the 4 token waves of an output half meet in LDS in a fixed order.
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float x = cs[a][v];
-            for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
-            cs[a][v] = x;
-        }
-    if (l16 == 0) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) red_cs[w >> 1][wn + a * 16 + g4 * 4 + v] = cs[a][v];
-    }
-    if (EPI == kEpiG) {
-        for (int off = 32; off > 0; off >>= 1) loss += __shfl_xor(loss, off, kWave);
-        if (lane == 0) red_loss[w] = loss;
-    }
-    __syncthreads();
-    if (tid < kFN) {
-        const float c = ((red_cs[0][tid] + red_cs[1][tid]) + red_cs[2][tid]) + red_cs[3][tid];
-        if (EPI == kEpiG) p.cs_g[((int64_t)q * p.m_tiles + mt) * d + n0 + tid] = c;
-        else p.cs_dz[((int64_t)q * p.m_tiles + mt) * H + n0 + tid] = c;
-    }
-    if (EPI == kEpiG && tid == 0) {
-        float sum = 0.f;
-        for (int i = 0; i < 8; ++i) sum += red_loss[i];
-        p.loss_p[(int64_t)q * p.m_tiles + mt] = sum;
+        colsum(cs, p.cs_dz + ((int64_t)q * p.m_tiles + mt) * H + u0);
+        __syncthreads();                    // red_cs is free for the next hidden tile
     }
 }
 
@@ -410,17 +407,21 @@ __global__ __launch_bounds__(256, 1) void fit_tn_kernel(FitParams p) {
 }
 
 // --------------------------------------------------------------- update
-// One block per problem. mode 0: loss only (slot `step`); mode 1: gradient
-// step `step` (reduces the partials in a fixed order, updates the fp32
-// masters, refreshes the bf16 copies); mode 2: bf16 copies only.
+// Grid (problem, slice of kUpdSlices). mode 0: loss only (slot `step`, slice
+// 0); mode 1: gradient step `step` (each weight's partials reduced in a fixed
+// order, the fp32 master updated, its bf16 copies refreshed, by the one
+// thread that owns it); mode 2: bf16 copies only.
+constexpr int kUpdSlices = 8;
+
 __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, int mode) {
-    const int q = blockIdx.x, tid = threadIdx.x;
+    const int q = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
     const int d = kHeadDim, H = p.hidden;
+    const int e0 = slice * 256 + tid, es = 256 * kUpdSlices;
     float* w1 = p.w1 + (int64_t)q * H * d;
     float* w2 = p.w2 + (int64_t)q * d * H;
     float* b1 = p.b1 + (int64_t)q * H;
     float* b2 = p.b2 + (int64_t)q * d;
-    if (mode != 2 && tid == 0 && p.losses) {
+    if (mode != 2 && slice == 0 && tid == 0 && p.losses) {
         double s = 0.0;
         for (int m = 0; m < p.m_tiles; ++m) s += (double)p.loss_p[(int64_t)q * p.m_tiles + m];
         p.losses[(int64_t)q * (p.n_steps + 1) + step] = (float)(s / (double)p.ctx_len);
@@ -430,35 +431,34 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
         const float lr = p.lr;
         const float* pw1 = p.pw1 + (int64_t)q * p.n_chunks * H * d;   // [c][i][u]
         const float* pw2 = p.pw2 + (int64_t)q * p.n_chunks * H * d;   // [c][u][o]
-        for (int e = tid; e < H * d; e += 256) {
+        for (int e = e0; e < H * d; e += es) {
             const int u = e / d, i = e - u * d;        // w1[u][i]
             float g = 0.f;
             for (int c = 0; c < p.n_chunks; ++c) g += pw1[((int64_t)c * d + i) * H + u];
             w1[e] -= lr * g;
         }
-        for (int e = tid; e < d * H; e += 256) {
+        for (int e = e0; e < d * H; e += es) {
             const int o = e / H, u = e - o * H;        // w2[o][u]
             float g = 0.f;
             for (int c = 0; c < p.n_chunks; ++c) g += pw2[((int64_t)c * H + u) * d + o];
             w2[e] -= lr * g;
         }
-        for (int u = tid; u < H; u += 256) {
+        for (int u = e0; u < H; u += es) {
             float g = 0.f;
             for (int m = 0; m < p.m_tiles; ++m) g += p.cs_dz[((int64_t)q * p.m_tiles + m) * H + u];
             b1[u] -= lr * g;
         }
-        for (int o = tid; o < d; o += 256) {
+        for (int o = e0; o < d; o += es) {
             float g = 0.f;
             for (int m = 0; m < p.m_tiles; ++m) g += p.cs_g[((int64_t)q * p.m_tiles + m) * d + o];
             b2[o] -= lr * g;
         }
-        __syncthreads();
     }
     uint16_t* w1b = reinterpret_cast<uint16_t*>(p.w1b) + (int64_t)q * H * d;
     uint16_t* w2b = reinterpret_cast<uint16_t*>(p.w2b) + (int64_t)q * d * H;
     uint16_t* w2tb = reinterpret_cast<uint16_t*>(p.w2tb) + (int64_t)q * H * d;
-    for (int e = tid; e < H * d; e += 256) w1b[e] = f32_to_bf16_bits(w1[e]);
-    for (int e = tid; e < d * H; e += 256) {
+    for (int e = e0; e < H * d; e += es) w1b[e] = f32_to_bf16_bits(w1[e]);   // the thread that updated w1[e]
+    for (int e = e0; e < d * H; e += es) {
         const int o = e / H, u = e - o * H;
         const uint16_t v = f32_to_bf16_bits(w2[e]);
         w2b[e] = v;
@@ -468,24 +468,24 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
 
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s) {
     const unsigned P = (unsigned)p.n_probs;
-    const unsigned mt8 = (unsigned)((p.m_tiles + 7) / 8 * 8);
-    const dim3 gz(mt8 * (unsigned)(p.hidden / kFN), P), gg(mt8, P);
     const dim3 t2((unsigned)(p.n_chunks * (kHeadDim / 128) * (p.hidden / 128)), P);
     hipError_t e;
-    hipLaunchKernelGGL(fit_update_kernel, dim3(P), dim3(256), 0, s, p, 0, 2);
+    hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, 0, 2);
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), s)) != hipSuccess) return e;
+    // Fused token-tile products: (problem, tile) pairs dealt to the 8 XCDs by
+    // problem (see fit_fused_kernel).
+    const int per_xcd = (int)(((P + 7) / 8) * (unsigned)p.m_tiles);
+    const dim3 gf((unsigned)per_xcd * 8u);
     for (int it = 0; it < p.n_steps; ++it) {
-        hipLaunchKernelGGL((fit_nt_kernel<kEpiZ>), gz, dim3(kFThreads), 0, s, p);
-        hipLaunchKernelGGL((fit_nt_kernel<kEpiG>), gg, dim3(kFThreads), 0, s, p);
-        hipLaunchKernelGGL((fit_nt_kernel<kEpiDz>), gz, dim3(kFThreads), 0, s, p);
+        hipLaunchKernelGGL((fit_fused_kernel<true>), gf, dim3(kFThreads), 0, s, p, per_xcd);
         hipLaunchKernelGGL((fit_tn_kernel<0>), t2, dim3(256), 0, s, p);
         hipLaunchKernelGGL((fit_tn_kernel<1>), t2, dim3(256), 0, s, p);
-        hipLaunchKernelGGL(fit_update_kernel, dim3(P), dim3(256), 0, s, p, it, 1);
+        hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, it, 1);
     }
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((fit_nt_kernel<kEpiZ>), gz, dim3(kFThreads), 0, s, p);
-    hipLaunchKernelGGL((fit_nt_kernel<kEpiG>), gg, dim3(kFThreads), 0, s, p);
-    hipLaunchKernelGGL(fit_update_kernel, dim3(P), dim3(256), 0, s, p, p.n_steps, 0);
+    hipLaunchKernelGGL((fit_fused_kernel<false>), gf, dim3(kFThreads), 0, s, p, per_xcd);
+    hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, p.n_steps, 0);
+
     return hipGetLastError();
 }
 

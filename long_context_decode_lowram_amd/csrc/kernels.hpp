@@ -97,7 +97,7 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s);   // M, iterati
 struct FitParams {
     int n_layers, ctx_len, n_kv, hidden, n_steps;
     int n_probs;                  // n_layers * n_kv
-    int m_tiles;                  // 128-token tiles
+    int m_tiles;                  // 64-token tiles
     int n_chunks, chunk_len;      // token chunks of the weight-gradient products
     float lr;
     const __bf16* keys;           // [L, T, Hkv*d]
