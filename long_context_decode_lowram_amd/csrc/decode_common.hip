@@ -235,20 +235,28 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     // reads a row's 128 features in one coalesced pass), then the wave sums.
     const int64_t q_row = ((int64_t)b * p.n_q + j) * kHeadDim;
     const float q0 = ld<ACT>(p.q, q_row + 2 * lane), q1 = ld<ACT>(p.q, q_row + 2 * lane + 1);
+    // Eight tokens per batch: their sixteen loads are issued before any sum,
+    // so the batch waits for memory once.
     float mx = -INFINITY;
-    for (int u0 = wv; u0 < nw; u0 += 2 * kCombWaves) {
-        const int u1 = u0 + kCombWaves;
-        const int64_t r0 = (((int64_t)b * p.win_cap + u0) * p.n_kv + h) * kHeadDim + 2 * lane;
-        const int64_t r1 = (((int64_t)b * p.win_cap + (u1 < nw ? u1 : u0)) * p.n_kv + h) * kHeadDim + 2 * lane;
-        float s0 = q0 * ld<ACT>(p.win_k, r0) + q1 * ld<ACT>(p.win_k, r0 + 1);
-        float s1 = q0 * ld<ACT>(p.win_k, r1) + q1 * ld<ACT>(p.win_k, r1 + 1);
-        s0 = wave_sum(s0) * p.scale;
-        s1 = wave_sum(s1) * p.scale;
-        if (lane == 0) {
-            sw[u0] = s0;
-            if (u1 < nw) sw[u1] = s1;
+    constexpr int kWinBatch = 8;
+    for (int u0 = wv; u0 < nw; u0 += kWinBatch * kCombWaves) {
+        float k0[kWinBatch], k1[kWinBatch];
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+            const int u = u0 + i * kCombWaves;
+            const int64_t row = (((int64_t)b * p.win_cap + (u < nw ? u : u0)) * p.n_kv + h) * kHeadDim + 2 * lane;
+            k0[i] = ld<ACT>(p.win_k, row);
+            k1[i] = ld<ACT>(p.win_k, row + 1);
         }
-        mx = fmaxf(mx, u1 < nw ? fmaxf(s0, s1) : s0);
+#pragma unroll
+        for (int i = 0; i < kWinBatch; ++i) {
+            const int u = u0 + i * kCombWaves;
+            const float sc = wave_sum(q0 * k0[i] + q1 * k1[i]) * p.scale;
+            if (u < nw) {
+                if (lane == 0) sw[u] = sc;
+                mx = fmaxf(mx, sc);
+            }
+        }
     }
     float M = block_reduce(mx, red, true);     // its barriers also publish part, wml and sw
     for (int w8 = 0; w8 < kCombWaves; ++w8) M = fmaxf(M, wml[2 * w8]);
@@ -299,9 +307,21 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
             for (int i = i0; i < i1; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
         }
         // Window values: quarter q takes the tokens u = q (mod 4); each token's
-        // row is read by 128 threads, coalesced.
-        for (int u = quarter; u < nw; u += 4)
-            y += sw[u] * ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f);
+        // row is read by 128 threads, coalesced; eight rows' loads in flight
+        // together.
+        for (int u0 = quarter; u0 < nw; u0 += 4 * kWinBatch) {
+            float vv[kWinBatch];
+#pragma unroll
+            for (int i = 0; i < kWinBatch; ++i) {
+                const int u = u0 + 4 * i;
+                vv[i] = u < nw ? ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f) : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kWinBatch; ++i) {
+                const int u = u0 + 4 * i;
+                if (u < nw) y += sw[u] * vv[i];
+            }
+        }
         if (quarter == 3) {
             y += oc[H + f];
             if (p.b2) y += Lt * ld<ACT>(p.b2, ((int64_t)b * p.n_kv + h) * kHeadDim + f);

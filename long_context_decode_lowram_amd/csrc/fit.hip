@@ -408,9 +408,11 @@ __global__ __launch_bounds__(256, 1) void fit_tn_kernel(FitParams p) {
 
 // --------------------------------------------------------------- update
 // Grid (problem, slice of kUpdSlices). mode 0: loss only (slot `step`, slice
-// 0); mode 1: gradient step `step` (each weight's partials reduced in a fixed
-// order, the fp32 master updated, its bf16 copies refreshed, by the one
-// thread that owns it); mode 2: bf16 copies only.
+// 0); mode 1: gradient step `step`: each weight's partials reduced in a fixed
+// order by the one thread that owns it, which updates the fp32 master and
+// writes its bf16 copies; mode 2: bf16 copies only. Threads walk the
+// weights in the order of the partials' fastest axis, so the (n_chunks x
+// more numerous) partial reads coalesce.
 constexpr int kUpdSlices = 8;
 
 __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, int mode) {
@@ -421,6 +423,9 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
     float* w2 = p.w2 + (int64_t)q * d * H;
     float* b1 = p.b1 + (int64_t)q * H;
     float* b2 = p.b2 + (int64_t)q * d;
+    uint16_t* w1b = reinterpret_cast<uint16_t*>(p.w1b) + (int64_t)q * H * d;
+    uint16_t* w2b = reinterpret_cast<uint16_t*>(p.w2b) + (int64_t)q * d * H;
+    uint16_t* w2tb = reinterpret_cast<uint16_t*>(p.w2tb) + (int64_t)q * H * d;
     if (mode != 2 && slice == 0 && tid == 0 && p.losses) {
         double s = 0.0;
         for (int m = 0; m < p.m_tiles; ++m) s += (double)p.loss_p[(int64_t)q * p.m_tiles + m];
@@ -432,16 +437,22 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
         const float* pw1 = p.pw1 + (int64_t)q * p.n_chunks * H * d;   // [c][i][u]
         const float* pw2 = p.pw2 + (int64_t)q * p.n_chunks * H * d;   // [c][u][o]
         for (int e = e0; e < H * d; e += es) {
-            const int u = e / d, i = e - u * d;        // w1[u][i]
+            const int i = e / H, u = e - i * H;        // w1[u][i]; partials contiguous in u
             float g = 0.f;
             for (int c = 0; c < p.n_chunks; ++c) g += pw1[((int64_t)c * d + i) * H + u];
-            w1[e] -= lr * g;
+            const float x = w1[(int64_t)u * d + i] - lr * g;
+            w1[(int64_t)u * d + i] = x;
+            w1b[(int64_t)u * d + i] = f32_to_bf16_bits(x);
         }
         for (int e = e0; e < d * H; e += es) {
-            const int o = e / H, u = e - o * H;        // w2[o][u]
+            const int u = e / d, o = e - u * d;        // w2[o][u]; partials contiguous in o
             float g = 0.f;
             for (int c = 0; c < p.n_chunks; ++c) g += pw2[((int64_t)c * H + u) * d + o];
-            w2[e] -= lr * g;
+            const float x = w2[(int64_t)o * H + u] - lr * g;
+            w2[(int64_t)o * H + u] = x;
+            const uint16_t v = f32_to_bf16_bits(x);
+            w2b[(int64_t)o * H + u] = v;
+            w2tb[e] = v;                               // w2tb[u][o]
         }
         for (int u = e0; u < H; u += es) {
             float g = 0.f;
@@ -453,11 +464,9 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
             for (int m = 0; m < p.m_tiles; ++m) g += p.cs_g[((int64_t)q * p.m_tiles + m) * d + o];
             b2[o] -= lr * g;
         }
+        return;
     }
-    uint16_t* w1b = reinterpret_cast<uint16_t*>(p.w1b) + (int64_t)q * H * d;
-    uint16_t* w2b = reinterpret_cast<uint16_t*>(p.w2b) + (int64_t)q * d * H;
-    uint16_t* w2tb = reinterpret_cast<uint16_t*>(p.w2tb) + (int64_t)q * H * d;
-    for (int e = e0; e < H * d; e += es) w1b[e] = f32_to_bf16_bits(w1[e]);   // the thread that updated w1[e]
+    for (int e = e0; e < H * d; e += es) w1b[e] = f32_to_bf16_bits(w1[e]);
     for (int e = e0; e < d * H; e += es) {
         const int o = e / H, u = e - o * H;
         const uint16_t v = f32_to_bf16_bits(w2[e]);
