@@ -3,6 +3,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include <hip/hip_runtime.h>
@@ -232,7 +233,7 @@ int plan_pinv(const lowram_pinv_args* a, PinvPlan* pl) {
     return LOWRAM_OK;
 }
 
-struct FitPlan { FitParams p; size_t off[14]; size_t total; };
+struct FitPlan { FitParams p; size_t off[9]; size_t total; };
 
 int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
     if (a == nullptr) return fail(LOWRAM_ERR_ARG, "args is NULL");
@@ -251,22 +252,23 @@ int plan_fit(const lowram_fit_args* a, FitPlan* pl) {
     p.n_layers = a->n_layers; p.ctx_len = a->ctx_len; p.n_kv = a->n_kv_heads; p.hidden = a->mlp_hidden;
     p.n_steps = a->n_steps; p.lr = a->lr;
     p.n_probs = a->n_layers * a->n_kv_heads;
-    p.m_tiles = (a->ctx_len + 63) / 64;   // 64-token tiles of the fused products
-    const int tiles = p.n_probs * (a->mlp_hidden / 128);
-    int nc = (2048 + tiles - 1) / tiles;
-    const int maxc = (a->ctx_len + 31) / 32;
-    nc = nc < 1 ? 1 : (nc > 64 ? 64 : nc);
-    nc = nc > maxc ? maxc : nc;
-    p.chunk_len = ((a->ctx_len + nc - 1) / nc + 31) / 32 * 32;
-    p.n_chunks = (a->ctx_len + p.chunk_len - 1) / p.chunk_len;
-    const size_t P = p.n_probs, T = a->ctx_len, H = a->mlp_hidden, d = a->head_dim;
-    const size_t sz[14] = {0, P * T * H * 2, P * T * d * 2, P * T * H * 2,                    // (unused) hb gb dzb
-                           P * H * d * 2, P * H * d * 2, P * H * d * 2,                      // w1b w2b w2tb
-                           P * p.n_chunks * H * d * 4, P * p.n_chunks * H * d * 4,          // pw1 pw2
-                           P * p.m_tiles * d * 4, P * p.m_tiles * H * 4, P * p.m_tiles * 4,  // cs_g cs_dz loss_p
-                           0, 0};
+    p.m_tiles = (a->ctx_len + 63) / 64;
+    // Token ranges: enough workgroups for the 256 CUs (one per CU each).
+    const int P = p.n_probs, T = a->ctx_len, H = a->mlp_hidden, d = a->head_dim;
+    const int fwd_tiles = (T + 31) / 32, bwd_tiles = (T + 63) / 64;
+    p.fwd_ranges = std::max(1, std::min((256 + P - 1) / P, (fwd_tiles + 7) / 8));
+    const int per_q = H / 128;
+    p.bwd_ranges = std::max(1, std::min((256 + P * per_q - 1) / (P * per_q), bwd_tiles));
+    p.n_parts = 2 * p.bwd_ranges;
+    p.n_loss_parts = H <= 256 ? 8 * p.fwd_ranges : p.m_tiles;
+    const size_t Pz = P, Tz = T, Hz = H, dz = d, np = p.n_parts;
+    const size_t sz[9] = {Pz * Tz * dz * 2,                                   // gb
+                          Pz * Hz * dz * 2, Pz * Hz * dz * 2, Pz * Hz * dz * 2, // w1b w2b w2tb
+                          Pz * np * Hz * dz * 4, Pz * np * Hz * dz * 4,        // pw1 pw2
+                          Pz * np * Hz * 4, Pz * np * dz * 4,                  // pb1 pb2
+                          Pz * (size_t)p.n_loss_parts * 4};                    // loss_p
     size_t off = 0;
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 9; ++i) {
         pl->off[i] = off;
         off = up256(off + sz[i]);
     }
@@ -656,17 +658,15 @@ int lowram_fit_predictor(const lowram_fit_args* a, void* stream) {
     p.v = static_cast<const __bf16*>(a->v);
     p.w_lin = static_cast<const __bf16*>(a->w_lin);
     p.w1 = a->w1; p.b1 = a->b1; p.w2 = a->w2; p.b2 = a->b2; p.losses = a->losses;
-    p.hb = reinterpret_cast<__bf16*>(ws + pl.off[1]);
-    p.gb = reinterpret_cast<__bf16*>(ws + pl.off[2]);
-    p.dzb = reinterpret_cast<__bf16*>(ws + pl.off[3]);
-    p.w1b = reinterpret_cast<__bf16*>(ws + pl.off[4]);
-    p.w2b = reinterpret_cast<__bf16*>(ws + pl.off[5]);
-    p.w2tb = reinterpret_cast<__bf16*>(ws + pl.off[6]);
-    p.pw1 = reinterpret_cast<float*>(ws + pl.off[7]);
-    p.pw2 = reinterpret_cast<float*>(ws + pl.off[8]);
-    p.cs_g = reinterpret_cast<float*>(ws + pl.off[9]);
-    p.cs_dz = reinterpret_cast<float*>(ws + pl.off[10]);
-    p.loss_p = reinterpret_cast<float*>(ws + pl.off[11]);
+    p.gb = reinterpret_cast<__bf16*>(ws + pl.off[0]);
+    p.w1b = reinterpret_cast<__bf16*>(ws + pl.off[1]);
+    p.w2b = reinterpret_cast<__bf16*>(ws + pl.off[2]);
+    p.w2tb = reinterpret_cast<__bf16*>(ws + pl.off[3]);
+    p.pw1 = reinterpret_cast<float*>(ws + pl.off[4]);
+    p.pw2 = reinterpret_cast<float*>(ws + pl.off[5]);
+    p.pb1 = reinterpret_cast<float*>(ws + pl.off[6]);
+    p.pb2 = reinterpret_cast<float*>(ws + pl.off[7]);
+    p.loss_p = reinterpret_cast<float*>(ws + pl.off[8]);
     hipError_t e = launch_fit(p, a->ev_main_begin, a->ev_main_end, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LOWRAM_OK : hip_fail(e, "fit launch");
 }

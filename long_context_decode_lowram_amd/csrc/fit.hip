@@ -6,13 +6,14 @@
 // per context at prefill. Loss L = (1 / T) sum_t ||v_hat_t - v_t||^2, plain
 // gradient descent on W1, b1, W2, b2 (W_lin fixed). Per step and problem
 // (layer, KV head), with weights stored output-major:
-//   H = gelu(K W1^T + b1)                              fit_fused_kernel, one workgroup per
-//   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           (problem, 64-token tile) (+ loss, sum_t G,
-//   dZ = (G W2) * gelu'(K W1^T + b1)                   sum_t dZ; the pre-activations are recomputed)
-//   dW2 = G^T H, dW1 = dZ^T K                          fit_tn_kernel (token chunks)
-//   theta -= lr dL/dtheta                              fit_update_kernel
+//   Z = K W1^T + b1,  H = gelu(Z)
+//   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           fit_fwd_kernel (loss partials too)
+//   dZ = (G W2) * gelu'(Z)
+//   dW2 = G^T H,  dW1 = dZ^T K,  db2 = sum_t G,  db1 = sum_t dZ
+//                                                       fit_bwd_kernel (Z and H recomputed)
+//   theta -= lr dL/dtheta                               fit_update_kernel
 // Products on bf16 MFMA with fp32 sums; the parameters are fp32 masters with
-// bf16 copies for the products.
+// bf16 copies for the products. Only G goes through HBM between the passes.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -22,27 +23,20 @@
 
 namespace lowram {
 
-constexpr int kFN = 128;                 // outputs per product tile (MFMA A operand rows)
-constexpr int kFK = 64;                  // contraction step
-constexpr int kFRowB = kFK * 2;          // 128-byte LDS rows
-constexpr int kFOp0 = kFN * kFRowB;      // 16 KB: a weight stage buffer
-constexpr int kFThreads = 512;
-
-__device__ __forceinline__ uint32_t fslot(int row, int piece) {
-    return (uint32_t)(row * kFRowB + ((piece ^ (row & 7)) << 4));
-}
+constexpr int kFitThreads = 512;          // eight waves, two per SIMD
+constexpr int kLdsAll = 163840;           // the whole LDS of a CU
+constexpr int kFwdMaxHidden = 256;        // widest hidden layer whose weights stay resident in LDS
 
 // GELU and its derivative from the normal tail fit (normal_tail): with
-// a = |z|, gelu(z) = max(z, 0) - a Q(a) and gelu'(z) = Phi(z) + z phi(z),
-// Phi(z) = 1 - Q(a) for z >= 0, Q(a) below; phi(z) = 2^(-z^2 / (2 ln 2)) / sqrt(2 pi).
-__device__ __forceinline__ float gelu_f(float z) {
-    const float a = fabsf(z);
-    return fmaxf(z, 0.0f) - a * normal_tail(a);
+// a = |z| and q = Q(a), gelu(z) = max(z, 0) - a q and
+// gelu'(z) = Phi(z) + z phi(z), Phi(z) = 1 - q for z >= 0 and q below;
+// phi(z) = 2^(-z^2 / (2 ln 2) + log2(1 / sqrt(2 pi))).
+__device__ __forceinline__ float gelu_q(float z, float q) {
+    return fmaf(-fabsf(z), q, __builtin_amdgcn_fmed3f(z, 0.0f, 3.0e38f));
 }
-__device__ __forceinline__ float gelu_grad_f(float z) {
-    const float q = normal_tail(fabsf(z));
-    const float phi = __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z) * 0.39894228040143268f;
-    return (z >= 0.0f ? 1.0f - q : q) + z * phi;
+__device__ __forceinline__ float gelu_grad_q(float z, float q) {
+    const float phi = __builtin_amdgcn_exp2f(fmaf(-0.72134752044448170f * z, z, -1.3257480647361593f));
+    return fmaf(z, phi, z >= 0.0f ? 1.0f - q : q);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -51,40 +45,233 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// --------------------------------------------------------------- fused
-// The three token-tile products of a gradient step in one workgroup per
-// (problem, 64-token tile), so the tile's keys are read from HBM once and H
-// and G are never read back from it:
-//   for each 128-wide hidden tile u:  Z_u = K W1_u^T;  H_u = gelu(Z_u + b1_u)
-//                                     (stored for dW2, and kept in LDS);
-//                                     V_hat += H_u W2_u^T
-//   V_hat += K W_lin^T;  G = (2 / T)(V_hat + b2 - V)   (stored, kept in LDS)
-//   for each hidden tile u:           dZ_u = (G W2_u) * gelu'(K W1_u^T + b1_u)
-// (BACKWARD = false stops after G: the loss after the last step). The keys and
-// H_u (then G, in the same place) stay resident in LDS as the token operand
-// ([64 tokens][128] bf16, two 64-wide halves in swizzled 128-byte rows); the
-// weight rows stream through two 16 KB stage buffers, 64 columns of the
-// contraction at a time. 66 KB of LDS, so two workgroups share a CU and hide
-// each other's copy latency. Eight waves: wave w covers outputs 64 (w & 1)
-// .. + 63 and tokens 16 (w >> 1) .. + 15; lane (l16, g4) ends with outputs
-// n .. n + 3 (n = 4 g4 + 16 a) of token l16. H, G, dZ, the column sums and
-// the loss partials have the values and layout the weight-gradient products
-// and the update read. Workgroups of one problem run on one XCD at a time
-// (its L2 then holds the problem's weights): XCD x takes problems x, x + 8,
-// ..., each problem's tiles in turn.
-constexpr int kFTok = 64;                       // tokens per tile
-constexpr int kFHalf = kFTok * kFRowB;          // one 64-wide half of a resident tile: 8 KB
+// 16-byte piece `piece` of row `row` of an LDS matrix with `row_bytes`-byte
+// rows, swizzled: piece p of row r sits in slot p ^ (r & 15). Sixteen lanes
+// reading the same logical piece of sixteen consecutive rows then hit
+// sixteen different bank groups.
+__device__ __forceinline__ uint32_t sw_off(int row, int piece, int row_bytes) {
+    return (uint32_t)(row * row_bytes + ((piece ^ (row & 15)) << 4));
+}
 
-template <bool BACKWARD>
-__global__ __launch_bounds__(kFThreads, 2) void fit_fused_kernel(FitParams p, int n_per_xcd) {
-    __shared__ __attribute__((aligned(16))) unsigned char kt[2 * kFHalf];   // keys of the tile
-    __shared__ __attribute__((aligned(16))) unsigned char ht[2 * kFHalf];   // H_u, then G
-    __shared__ __attribute__((aligned(16))) unsigned char ws0[kFOp0], ws1[kFOp0];
-    __shared__ float red_cs[4][kFN];
+// ------------------------------------------------------------ forward
+// One workgroup per (problem, token range); W1 [h][d], W2 [d][h] and W_lin
+// [d][d] stay in LDS for the workgroup's life (160 KB at h = 256, the MFMA A
+// operands); each wave takes 32-token tiles in turn (tile w, w + 8, ...) and
+// holds the tile's keys as B-operand fragments read straight from HBM, so no
+// token data passes through LDS and the waves never wait for each other.
+// Per tile and 32 hidden units c:
+//   Z^T (2 x 2 tiles of 16) = W1[32 c ..] K^T + b1      16 MFMAs
+//   H^T = gelu(Z^T), bf16: lane (token j, g4) holds units 4 g4 + i and
+//         16 + 4 g4 + i, the k-slots of one B fragment
+//   V_hat^T (8 x 2 tiles) += W2[:, 32 c ..] H^T          16 MFMAs
+// W2's columns are stored in LDS in that k-slot order (within every 32
+// units, piece g4 holds units 4 g4 .. + 3 and 16 + 4 g4 .. + 3), so its A
+// fragments are single 16-byte reads. The V_hat^T accumulators start at b2;
+// then V_hat^T += W_lin K^T and G = (2 / T)(V_hat - V) by element; the lane's
+// squared errors go to a per-wave loss partial.
+template <bool WRITE_G>
+__global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsAll];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int H = p.hidden, T = p.ctx_len, d = kHeadDim;
+    const int q = blockIdx.x / p.fwd_ranges, rg = blockIdx.x - q * p.fwd_ranges;
+    const int l = q / p.n_kv, h = q - l * p.n_kv;
+    const int ldkv = p.n_kv * d;
+    const int w2row = 2 * H;                          // bytes per W2 row
+    unsigned char* const w1s = lds;                   // [h][d]
+    unsigned char* const w2s = lds + H * 256;         // [d][h], permuted columns
+    unsigned char* const wls = w2s + d * w2row;       // [d][d]
+
+    {
+        // all loads first, then the LDS stores (H <= 256: at most 8 W1 and W2
+        // pieces and 4 W_lin pieces per thread)
+        const u32x4* w1g = reinterpret_cast<const u32x4*>(p.w1b + (int64_t)q * H * d);
+        const u32x4* wlg = reinterpret_cast<const u32x4*>(p.w_lin + (int64_t)q * d * d);
+        const u32x2* w2g = reinterpret_cast<const u32x2*>(p.w2b + (int64_t)q * d * H);
+        const int npc = H / 8;                        // pieces per W2 row
+        u32x4 v1[8], vl[4], v2[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = tid + k * kFitThreads;
+            if (i < H * 16) v1[k] = w1g[i];
+            if (i < d * npc) {
+                const int r = i / npc, pc = i - r * npc;      // piece pc = 4 c + gg of row r
+                const int c = pc >> 2, gg = pc & 3;
+                const u32x2 lo = w2g[(r * H + 32 * c + 4 * gg) >> 2];
+                const u32x2 hi = w2g[(r * H + 32 * c + 16 + 4 * gg) >> 2];
+                v2[k] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vl[k] = wlg[tid + k * kFitThreads];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = tid + k * kFitThreads;
+            if (i < H * 16) *reinterpret_cast<u32x4*>(w1s + sw_off(i >> 4, i & 15, 256)) = v1[k];
+            if (i < d * npc) *reinterpret_cast<u32x4*>(w2s + sw_off(i / npc, i % npc, w2row)) = v2[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = tid + k * kFitThreads;
+            *reinterpret_cast<u32x4*>(wls + sw_off(i >> 4, i & 15, 256)) = vl[k];
+        }
+    }
+    __syncthreads();
+
+    const int n_tiles = (T + 31) / 32;
+    const int per = (n_tiles + p.fwd_ranges - 1) / p.fwd_ranges;
+    const int tb = rg * per, te = min(n_tiles, tb + per);
+    const uint32_t kv_bytes = (uint32_t)((int64_t)T * ldkv * 2);   // below 2^31 (checked on the host)
+    const uint32_t ldkv_u = (uint32_t)ldkv;                          // offsets of rows past T stay below 2^32
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.keys + (int64_t)l * T * ldkv + h * d, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + (int64_t)l * T * ldkv + h * d, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rgo = buffer_rsrc(p.gb + (int64_t)q * T * d, (uint32_t)((int64_t)T * d * 2));
+    const float* const b1 = p.b1 + (int64_t)q * H;
+    const float* const b2 = p.b2 + (int64_t)q * d;
+    const float gscale = 2.0f / (float)T;
+    // Keys of a tile as B fragments: kf[tt][s] = K[t0 + 16 tt + l16][32 s + 8 g4 .. + 7]
+    // (rows past T read as zeros).
+    auto load_k = [&](int tile, bf16x8 (&kf)[2][4]) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kf[tt][s] = as_bf16x8(__builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rk, ((uint32_t)(tile * 32 + 16 * tt + l16) * ldkv_u + 32 * s + 8 * g4) * 2u, 0, 0)));
+    };
+    float loss = 0.f;
+    bf16x8 kf[2][4];
+    for (int tile = tb + w; tile < te; tile += 8) {
+        const int t0 = tile * 32;
+        // A zero the compiler cannot see through: the W_lin fragments and b2
+        // below are the same for every tile, and hoisting their loads out of
+        // the loop would hold 160 registers for the kernel's life.
+        int zero = 0;
+        asm volatile("" : "+v"(zero));
+        // Loads in the order they are needed (the counter of outstanding
+        // loads drains in order): keys, the first hidden chunk's b1, b2 (the
+        // accumulators start at it), V for the G step.
+        load_k(tile, kf);
+        f32x4 bn[2];                                  // b1 of the next hidden chunk, one chunk ahead
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) bn[ht] = *reinterpret_cast<const f32x4*>(b1 + 16 * ht + 4 * g4 + zero);
+        f32x4 acc[8][2];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(b2 + 16 * dt + 4 * g4 + zero);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = bb;
+        }
+        // V for the G step: vv[tt][dt] = V[t0 + 16 tt + l16][16 dt + 4 g4 .. + 3]
+        u32x2 vv[2][8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                vv[tt][dt] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                               rv, ((uint32_t)(t0 + 16 * tt + l16) * ldkv_u + 16 * dt + 4 * g4) * 2u, 0, 0));
+        for (int c = 0; c < H / 32; ++c) {
+            f32x4 z[2][2];                            // [ht][tt]
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) z[ht][tt] = bn[ht];
+            if (c + 1 < H / 32) {
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+                    bn[ht] = *reinterpret_cast<const f32x4*>(b1 + 32 * (c + 1) + 16 * ht + 4 * g4);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    const bf16x8 wf = lds16(w1s, sw_off(32 * c + 16 * ht + l16, 4 * s + g4, 256));
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) z[ht][tt] = mfma(wf, kf[tt][s], z[ht][tt]);
+                }
+            bf16x8 hf[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4 g0, g1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    g0[i] = gelu_q(z[0][tt][i], normal_tail(fabsf(z[0][tt][i])));
+                    g1[i] = gelu_q(z[1][tt][i], normal_tail(fabsf(z[1][tt][i])));
+                }
+                hf[tt] = pack8(g0, g1);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const bf16x8 wf = lds16(w2s, sw_off(16 * dt + l16, 4 * c + g4, w2row));
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = mfma(wf, hf[tt], acc[dt][tt]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const bf16x8 wf = lds16(wls, sw_off(16 * dt + l16, 4 * s + g4, 256) + zero);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = mfma(wf, kf[tt][s], acc[dt][tt]);
+            }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = t0 + 16 * tt + l16;
+            const bool valid = t < T;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const float vt[4] = {bf16_lo(vv[tt][dt][0]), bf16_hi(vv[tt][dt][0]), bf16_lo(vv[tt][dt][1]),
+                                     bf16_hi(vv[tt][dt][1])};
+                float g[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = acc[dt][tt][i] - vt[i];
+                    if (valid) loss = fmaf(e, e, loss);
+                    g[i] = gscale * e;
+                }
+                if (WRITE_G)      // rows past T fall outside the descriptor and are dropped
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
+                                           u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])}),
+                        rgo, (uint32_t)((t * d + 16 * dt + 4 * g4) * 2), 0, 0);
+            }
+        }
+    }
+    loss = wave_sum(loss);
+    if (lane == 0) p.loss_p[((int64_t)q * p.fwd_ranges + rg) * 8 + w] = loss;
+}
+
+// ------------------------------------------------------ tiled forward
+// The forward for hidden layers too wide to keep resident (h > 256): one
+// workgroup per (problem, 64-token tile); the keys and H_u stay in LDS as the
+// token operand and the weight rows stream through two 16 KB stage buffers,
+// 64 columns of the contraction at a time. Eight waves: wave w covers
+// outputs 64 (w & 1) .. + 63 and tokens 16 (w >> 1) .. + 15; lane (l16, g4)
+// ends with outputs n .. n + 3 (n = 4 g4 + 16 a) of token l16.
+constexpr int kTN = 128;                 // outputs per product tile
+constexpr int kTK = 64;                  // contraction step
+constexpr int kTRowB = kTK * 2;          // 128-byte LDS rows
+constexpr int kTOp = kTN * kTRowB;       // 16 KB: a weight stage buffer
+constexpr int kTTok = 64;                // tokens per tile
+constexpr int kTHalf = kTTok * kTRowB;   // one 64-wide half of a resident tile: 8 KB
+
+__device__ __forceinline__ uint32_t tslot(int row, int piece) {
+    return (uint32_t)(row * kTRowB + ((piece ^ (row & 7)) << 4));
+}
+
+template <bool WRITE_G>
+__global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams p, int n_per_xcd) {
+    __shared__ __attribute__((aligned(16))) unsigned char kt[2 * kTHalf];   // keys of the tile
+    __shared__ __attribute__((aligned(16))) unsigned char ht[2 * kTHalf];   // H_u
+    __shared__ __attribute__((aligned(16))) unsigned char ws0[kTOp], ws1[kTOp];
     __shared__ float red_loss[8];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // blockIdx -> (problem, token tile): XCD x = blockIdx % 8 walks its own
-    // list of (problem, tile) pairs in order.
+    // problems' tiles in order, so its L2 holds those problems' weights.
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     if (local >= n_per_xcd) return;
     const int q = (local / p.m_tiles) * 8 + xcd;
@@ -92,32 +279,27 @@ __global__ __launch_bounds__(kFThreads, 2) void fit_fused_kernel(FitParams p, in
     if (q >= p.n_probs) return;
     const int l = q / p.n_kv, h = q - l * p.n_kv;
     const int d = kHeadDim, H = p.hidden, T = p.ctx_len;
-    const int t0 = mt * kFTok;
+    const int t0 = mt * kTTok;
     const int ldkv = p.n_kv * d;
-    const int64_t th = (int64_t)q * T * H, td = (int64_t)q * T * d;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int wn = (w & 1) * 64, wt = (w >> 1) * 16;
     const int dma_row = lane >> 3;
     const uint32_t dma_piece = (uint32_t)(((lane & 7) ^ dma_row) * 16);
 
-    // The keys of the tile, both 64-wide halves (rows past T read as zeros);
-    // read once: non-temporal. Wave w copies rows 8 w .. 8 w + 7.
     {
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.keys + (int64_t)l * T * ldkv + h * d + (int64_t)t0 * ldkv,
                                                       (uint32_t)((int64_t)max(0, T - t0) * ldkv * 2));
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-            dma16<kNonTemporal>(rk, kt + half * kFHalf + w * 8 * kFRowB,
-                                (uint32_t)(((w * 8 + dma_row) * ldkv + half * kFK) * 2) + dma_piece, 0u);
+            dma16<kNonTemporal>(rk, kt + half * kTHalf + w * 8 * kTRowB,
+                                (uint32_t)(((w * 8 + dma_row) * ldkv + half * kTK) * 2) + dma_piece, 0u);
     }
-    // 128 weight rows (outputs n0 .. n0 + 127 of a row-major matrix with row
-    // stride ldw), contraction columns k0 .. k0 + 63, into a stage buffer.
     auto dma_w = [&](const __bf16* wmat, int ldw, int n0, int k0, unsigned char* stage) {
-        const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wmat + (int64_t)n0 * ldw, (uint32_t)(kFN * ldw * 2));
+        const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wmat + (int64_t)n0 * ldw, (uint32_t)(kTN * ldw * 2));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int r0 = (w * 2 + c) * 8;
-            dma16(rw, stage + r0 * kFRowB, (uint32_t)(((r0 + dma_row) * ldw + k0) * 2) + dma_piece, 0u);
+            dma16(rw, stage + r0 * kTRowB, (uint32_t)(((r0 + dma_row) * ldw + k0) * 2) + dma_piece, 0u);
         }
     };
     auto mma = [&](const unsigned char* op0, const unsigned char* op1, f32x4 (&acc)[4]) {
@@ -125,17 +307,15 @@ __global__ __launch_bounds__(kFThreads, 2) void fit_fused_kernel(FitParams p, in
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 af[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) af[a] = lds16(op0, fslot(wn + a * 16 + l16, ks * 4 + g4));
-            const bf16x8 bf = lds16(op1, fslot(wt + l16, ks * 4 + g4));
+            for (int a = 0; a < 4; ++a) af[a] = lds16(op0, tslot(wn + a * 16 + l16, ks * 4 + g4));
+            const bf16x8 bf = lds16(op1, tslot(wt + l16, ks * 4 + g4));
 #pragma unroll
             for (int a = 0; a < 4; ++a) acc[a] = mfma(af[a], bf, acc[a]);
         }
     };
     // acc (+)= W[n0 .. n0 + 127][k0 .. k0 + 127] . tok^T over a resident
-    // 128-wide token tile (two halves): two 64-wide steps, weights double
-    // buffered. The barriers also publish resident-tile rows written before
-    // the call, and on return every wave is done with the stage buffers and
-    // with tok.
+    // 128-wide token tile (two halves), weights double buffered. On return
+    // every wave is done with the stage buffers and with tok.
     auto contract = [&](const __bf16* wmat, int ldw, int n0, int k0, const unsigned char* tok, f32x4 (&acc)[4],
                         bool zero) {
         if (zero) {
@@ -143,159 +323,112 @@ __global__ __launch_bounds__(kFThreads, 2) void fit_fused_kernel(FitParams p, in
             for (int a = 0; a < 4; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         dma_w(wmat, ldw, n0, k0, ws0);
-        dma_w(wmat, ldw, n0, k0 + kFK, ws1);
-        wait_vmcnt<2>();                    // this wave's step 0 copies (the older two) have landed
-        barrier_lds();                      // (step 1's copies stay in flight)
+        dma_w(wmat, ldw, n0, k0 + kTK, ws1);
+        wait_vmcnt<2>();
+        barrier_lds();
         mma(ws0, tok, acc);
         wait_vmcnt<0>();
         barrier_lds();
-        mma(ws1, tok + kFHalf, acc);
+        mma(ws1, tok + kTHalf, acc);
         barrier_lds();
     };
-    // Store a lane's four consecutive outputs (as bf16) of token row r into a
-    // resident tile: output n lands in half n / 64, piece (n % 64) / 8.
     auto put = [&](unsigned char* tile, int r, int n, u32x2 v) {
         const int hf = n >> 6, nn = n & 63;
-        *reinterpret_cast<u32x2*>(tile + hf * kFHalf + fslot(r, nn >> 3) + (nn & 7) * 2) = v;
-    };
-    // Column sums of a 128-output tile over this tile's tokens, in a fixed
-    // order: lanes l16 = 0..15 share outputs, then the 4 token waves of an
-    // output half meet in LDS.
-    auto colsum = [&](float (&cs)[4][4], float* dst) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float x = cs[a][v];
-                for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
-                cs[a][v] = x;
-            }
-        if (l16 == 0) {
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) red_cs[w >> 1][wn + a * 16 + g4 * 4 + v] = cs[a][v];
-        }
-        __syncthreads();
-        if (tid < kFN) dst[tid] = ((red_cs[0][tid] + red_cs[1][tid]) + red_cs[2][tid]) + red_cs[3][tid];
+        *reinterpret_cast<u32x2*>(tile + hf * kTHalf + tslot(r, nn >> 3) + (nn & 7) * 2) = v;
     };
     const float gscale = 2.0f / (float)T;
     const __bf16* w1b = p.w1b + (int64_t)q * H * d;
     const __bf16* w2b = p.w2b + (int64_t)q * d * H;
-    const __bf16* w2tb = p.w2tb + (int64_t)q * H * d;
     const __bf16* wl = p.w_lin + (int64_t)q * d * d;
     const float* b1 = p.b1 + (int64_t)q * H;
     const float* b2 = p.b2 + (int64_t)q * d;
-    const int r = wt + l16, t = t0 + r;          // this lane's token row
+    const int r = wt + l16, t = t0 + r;
     f32x4 acc[4], accv[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) accv[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // ---- forward: H_u and V_hat
-    for (int u0 = 0; u0 < H; u0 += kFN) {
+    for (int u0 = 0; u0 < H; u0 += kTN) {
         contract(w1b, d, u0, 0, kt, acc, true);                 // Z_u
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int n = wn + a * 16 + g4 * 4;
-            u32x2 hv = {0u, 0u};
-            if (t < T) {
-                float v4[4];
+            float v4[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) v4[v] = gelu_f(acc[a][v] + b1[u0 + n + v]);
-                hv = u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-                *reinterpret_cast<u32x2*>(p.hb + th + (int64_t)t * H + u0 + n) = hv;
+            for (int v = 0; v < 4; ++v) {
+                const float z = acc[a][v] + b1[u0 + n + v];
+                v4[v] = gelu_q(z, normal_tail(fabsf(z)));
             }
-            put(ht, r, n, hv);
+            put(ht, r, n, u32x2{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])});
         }
         contract(w2b, H, 0, u0, ht, accv, false);              // V_hat += H_u W2_u^T
     }
     contract(wl, d, 0, 0, kt, accv, false);                     // V_hat += K W_lin^T
-
-    // ---- G (into the H tile's place: its last reader has passed the barrier
-    // that ends the contraction above), loss, column sums of G
-    {
-        float cs[4][4];
-        float loss = 0.f;
+    float loss = 0.f;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int n = wn + a * 16 + g4 * 4;
-            u32x2 gv = {0u, 0u};
+    for (int a = 0; a < 4; ++a) {
+        const int n = wn + a * 16 + g4 * 4;
+        if (t < T) {
+            const u32x2 vv = *reinterpret_cast<const u32x2*>(p.v + ((int64_t)l * T + t) * ldkv + h * d + n);
+            const float vt[4] = {bf16_lo(vv[0]), bf16_hi(vv[0]), bf16_lo(vv[1]), bf16_hi(vv[1])};
+            float g[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) cs[a][v] = 0.f;
-            if (t < T) {
-                const u32x2 vv = *reinterpret_cast<const u32x2*>(p.v + ((int64_t)l * T + t) * ldkv + h * d + n);
-                const float vt[4] = {bf16_lo(vv[0]), bf16_hi(vv[0]), bf16_lo(vv[1]), bf16_hi(vv[1])};
-                float g[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float e = accv[a][v] + b2[n + v] - vt[v];
-                    loss = fmaf(e, e, loss);
-                    g[v] = gscale * e;
-                    cs[a][v] = g[v];
-                }
-                gv = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-                *reinterpret_cast<u32x2*>(p.gb + td + (int64_t)t * d + n) = gv;
+            for (int v = 0; v < 4; ++v) {
+                const float e = accv[a][v] + b2[n + v] - vt[v];
+                loss = fmaf(e, e, loss);
+                g[v] = gscale * e;
             }
-            put(ht, r, n, gv);
-        }
-        for (int off = 32; off > 0; off >>= 1) loss += __shfl_xor(loss, off, kWave);
-        if (lane == 0) red_loss[w] = loss;
-        colsum(cs, p.cs_g + ((int64_t)q * p.m_tiles + mt) * d);
-        if (tid == 0) {
-            float sum = 0.f;
-            for (int i = 0; i < 8; ++i) sum += red_loss[i];
-            p.loss_p[(int64_t)q * p.m_tiles + mt] = sum;
+            if (WRITE_G)
+                *reinterpret_cast<u32x2*>(p.gb + ((int64_t)q * T + t) * d + n) =
+                    u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
         }
     }
-    if (!BACKWARD) return;
-
-    // ---- backward: dZ_u = (G W2_u) * gelu'(Z_u + b1_u), column sums of dZ
-    for (int u0 = 0; u0 < H; u0 += kFN) {
-        contract(w1b, d, u0, 0, kt, accv, true);                // Z_u again (cheaper than keeping every tile)
-        contract(w2tb, d, u0, 0, ht, acc, true);                // G W2_u
-        float cs[4][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int n = wn + a * 16 + g4 * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cs[a][v] = 0.f;
-            if (t < T) {
-                float dz[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    dz[v] = acc[a][v] * gelu_grad_f(accv[a][v] + b1[u0 + n + v]);
-                    cs[a][v] = dz[v];
-                }
-                *reinterpret_cast<u32x2*>(p.dzb + th + (int64_t)t * H + u0 + n) =
-                    u32x2{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
-            }
-        }
-        colsum(cs, p.cs_dz + ((int64_t)q * p.m_tiles + mt) * H + u0);
-        __syncthreads();                    // red_cs is free for the next hidden tile
+    loss = wave_sum(loss);
+    if (lane == 0) red_loss[w] = loss;
+    __syncthreads();
+    if (tid == 0) {
+        float sum = 0.f;
+        for (int i = 0; i < 8; ++i) sum += red_loss[i];
+        p.loss_p[(int64_t)q * p.m_tiles + mt] = sum;
     }
 }
 
-// ------------------------------------------------------------------- TN
-// C[m][n] = sum over this chunk's tokens of A[t][m] B[t][n], a 128 x 128
-// tile, stored transposed: out[n][m]. Both operands are token-major, copied
-// untransposed into a 4-stage ring of 32-token steps (256-byte rows, piece p
-// of row t in slot p ^ tsw(t)) three steps ahead and read with the
-// transposing LDS read (lanes 4r .. 4r+3 of a 16-lane group name row r's 16
-// columns, lane j gets column j of the 4 rows). Four waves of 64 x 64.
-// role 0: dW2 = G^T H (A = G [T][d], B = H [T][h]); role 1: dW1 = dZ^T K.
-constexpr int kTK = 32;
-constexpr int kTRowB = 256;
-constexpr int kTOp = kTK * kTRowB;       // 8 KB
-constexpr int kTStage = 2 * kTOp;
+// ------------------------------------------------------------ backward
+// One workgroup per (problem, 128-unit hidden slice, token range), 64 tokens
+// per iteration. Wave w takes hidden units u0 = 128 slice + 32 (w & 3) .. + 31
+// and the 32-token half w >> 2 of each tile, and keeps its dW1 and dW2^T rows
+// (32 x 128 each) in registers for the whole range. Resident: the slice's W1
+// rows in LDS (B operand of Z), the wave's W2^T rows as register fragments
+// (B operand of G W2). The keys and G of each tile arrive by direct
+// global -> LDS copies into a four-tile ring, three tiles ahead. Per tile:
+//   Z  [tok][u] = K W1^T + b1           A = K rows (LDS)        16 MFMAs
+//   dH [tok][u] = G W2                  A = G rows (LDS)        16 MFMAs
+//   H = gelu(Z), dZ = dH gelu'(Z); lane (unit j, g4) holds tokens 4 g4 + i
+//     and 16 + 4 g4 + i of its unit, the k-slots of one A fragment of the
+//     token contractions below
+//   dW2^T[u][o] += H^T G                B = G^T by transposing LDS reads
+//   dW1  [u][i] += dZ^T K               B = K^T likewise        32 MFMAs
+//   db2 (slice 0; wave w sums d tiles 2 (w & 3), + 1) from the same G^T
+//   fragments and db1 from dZ, on the vector ALU in fp32.
+// Tokens past T read as zeros: their G and dH vanish, so they add nothing.
+// The two token halves write separate partials; the update sums them.
+constexpr int kBwdTok = 64;
+constexpr int kBwdRing = 4;
+constexpr int kBwdTile = kBwdTok * 256;          // 16 KB: 64 rows of 128 bf16
+constexpr int kBwdW1 = 128 * 256;                // the slice's W1 rows: 32 KB
+static_assert(kBwdW1 + kBwdRing * 2 * kBwdTile == kLdsAll, "backward LDS layout");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
 
-__device__ __forceinline__ int tsw(int t) { return 2 * ((t & 3) | (((t >> 3) & 1) << 2)); }
-
-__device__ __forceinline__ bf16x8 tn_frag(const unsigned char* op, uint32_t off) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off + 4 * kTRowB));
+// Transposing read of a B fragment over a 32-token slab: lane (j, g4) gets
+// column c0 + j of slab rows 4 g4 + 0..3 (low half) and 16 + 4 g4 + 0..3
+// (high half). Each 16-lane group's lane i names row 4 g4 + i / 4, columns
+// c0 + 4 (i % 4) .. + 3 (8 bytes); rows are 256 bytes, swizzled as sw_off.
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* slab, int c0, int l16, int g4) {
+    const int rr = 4 * g4 + (l16 >> 2);
+    const int byte = (c0 + 4 * (l16 & 3)) * 2;
+    const uint32_t off = sw_off(rr, byte >> 4, 256) + (byte & 15);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(slab + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(slab + off + 16 * 256));
     u32x4 v;
     v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
     v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -304,115 +437,191 @@ __device__ __forceinline__ bf16x8 tn_frag(const unsigned char* op, uint32_t off)
     return as_bf16x8(v);
 }
 
-template <int ROLE>
-__global__ __launch_bounds__(256, 1) void fit_tn_kernel(FitParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char s0[kTStage];
-    __shared__ __attribute__((aligned(16))) unsigned char s1[kTStage];
-    __shared__ __attribute__((aligned(16))) unsigned char s2[kTStage];
-    __shared__ __attribute__((aligned(16))) unsigned char s3[kTStage];
+__global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsAll];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q = blockIdx.y;
-    const int l = q / p.n_kv, h = q - l * p.n_kv;
-    const int d = kHeadDim, H = p.hidden, T = p.ctx_len;
-    const int M = ROLE == 0 ? d : H, N = ROLE == 0 ? H : d;
-    const int mtn = M / 128, ntn = N / 128;
-    const int per_chunk = mtn * ntn;
-    const int chunk = blockIdx.x / per_chunk;
-    const int tile = blockIdx.x - chunk * per_chunk;
-    const int mi = tile / ntn, ni = tile - mi * ntn;
-    const int tb0 = chunk * p.chunk_len;
-    const int tb1 = min(T, tb0 + p.chunk_len);
-    const int n_steps = (tb1 - tb0 + kTK - 1) / kTK;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int hg = w & 3, th = w >> 2;
+    const int H = p.hidden, T = p.ctx_len, d = kHeadDim;
+    const int n_sl = H / 128;
+    // blockIdx -> (problem, slice, range): XCD x = blockIdx % 8 takes
+    // problems x, x + 8, ..., each problem's slices and ranges back to back,
+    // so they share the keys and G of a tile in that XCD's L2.
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int per_q = n_sl * p.bwd_ranges;
+    const int q = (j / per_q) * 8 + xcd, sr = j - (j / per_q) * per_q;
+    if (q >= p.n_probs) return;
+    const int sl = sr / p.bwd_ranges, rg = sr - sl * p.bwd_ranges;
+    const int l = q / p.n_kv, hh = q - l * p.n_kv;
     const int ldkv = p.n_kv * d;
-    const int64_t th = (int64_t)q * T * H, td = (int64_t)q * T * d;
-    const __bf16* A;
-    const __bf16* B;
-    int lda, ldb;
-    if (ROLE == 0) { A = p.gb + td; lda = d; B = p.hb + th; ldb = H; }
-    else { A = p.dzb + th; lda = H; B = p.keys + (int64_t)l * T * ldkv + h * d; ldb = ldkv; }
-    const int rows = tb1 - tb0;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (int64_t)tb0 * lda + mi * 128, (uint32_t)((int64_t)rows * lda * 2));
-    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(B + (int64_t)tb0 * ldb + ni * 128, (uint32_t)((int64_t)rows * ldb * 2));
-    // Copies: wave w fills rows 8 w .. 8 w + 7 of both operands, 4 rows per
-    // instruction (lane i: row 8 w + 4 c + i / 16, slot i % 16).
-    uint32_t va[2], vb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int row = w * 8 + c * 4 + (lane >> 4);
-        const int piece = (lane & 15) ^ tsw(row);
-        va[c] = (uint32_t)(row * lda * 2 + piece * 16);
-        vb[c] = (uint32_t)(row * ldb * 2 + piece * 16);
+    const int u0 = sl * 128 + hg * 32;
+
+    unsigned char* const w1s = lds;
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(p.w1b + ((int64_t)q * H + sl * 128) * d);
+        for (int i = tid; i < 128 * 16; i += kFitThreads)
+            *reinterpret_cast<u32x4*>(w1s + sw_off(i >> 4, i & 15, 256)) = src[i];
     }
-    auto dma = [&](int s, unsigned char* stage) {
-        const uint32_t sa = (uint32_t)(s * kTK * lda * 2), sb = (uint32_t)(s * kTK * ldb * 2);
+    // W2^T fragments: w2f[ht][s] = W2^T[u0 + 16 ht + l16][32 s + 8 g4 .. + 7]
+    bf16x8 w2f[2][4];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            w2f[ht][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                p.w2tb + ((int64_t)q * H + u0 + 16 * ht + l16) * d + 32 * s + 8 * g4));
+    const float bb0 = p.b1[(int64_t)q * H + u0 + l16], bb1 = p.b1[(int64_t)q * H + u0 + 16 + l16];
+
+    const int n_all = (T + kBwdTok - 1) / kBwdTok;
+    const int per = (n_all + p.bwd_ranges - 1) / p.bwd_ranges;
+    const int ib = rg * per, n_it = max(0, min(n_all, ib + per) - ib);
+    const __bf16* const kq = p.keys + (int64_t)l * T * ldkv + hh * d;
+    const __bf16* const gq = p.gb + (int64_t)q * T * d;
+    auto ktile = [&](int i) { return lds + kBwdW1 + (i & (kBwdRing - 1)) * 2 * kBwdTile; };
+    // Tile i's keys and G rows: wave w copies rows 8 w .. 8 w + 7 of each
+    // (two copies of 4 rows; lane L fills row 4 c' + L / 16, slot L % 16 with
+    // the piece that the swizzle puts there). Rows past T read as zeros.
+    const int crow = lane >> 4, cslot = lane & 15;
+    auto issue = [&](int i) {
+        const int t0 = (ib + i) * kBwdTok;
+        unsigned char* const kt = ktile(i);
+        const int rows = max(0, T - t0);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kq + (int64_t)t0 * ldkv, (uint32_t)(rows * ldkv * 2));
+        const __amdgpu_buffer_rsrc_t rgt = buffer_rsrc(gq + (int64_t)t0 * d, (uint32_t)(rows * d * 2));
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            dma16(ra, stage + (w * 8 + c * 4) * kTRowB, va[c], sa);
-            // B (H or K rows) is read by one workgroup only: non-temporal.
-            // A (G or dZ rows) is shared by the two output tiles' workgroups.
-            dma16<kNonTemporal>(rb, stage + kTOp + (w * 8 + c * 4) * kTRowB, vb[c], sb);
+            const int row = 8 * w + 4 * c + crow;
+            const uint32_t pc = (uint32_t)((cslot ^ (row & 15)) << 4);
+            dma16(rk, kt + (8 * w + 4 * c) * 256, (uint32_t)(row * ldkv * 2) + pc, 0u);
+            dma16(rgt, kt + kBwdTile + (8 * w + 4 * c) * 256, (uint32_t)(row * 256) + pc, 0u);
         }
     };
-    const int g = lane >> 4, i16 = lane & 15;
-    const int trow = 8 * g + (i16 >> 2);
-    const int lane_sw = tsw(trow) | ((i16 & 3) >> 1);
-    const uint32_t lane_off = (uint32_t)(trow * kTRowB + ((i16 & 1) << 3));
-    auto off = [&](int m0) { return lane_off + ((uint32_t)(((m0 >> 3) ^ lane_sw)) << 4); };
 
-    f32x4 acc[4][4];
+    f32x4 dw1[2][8], dw2[2][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-    auto mma = [&](const unsigned char* stage) {
-        bf16x8 af[4], bf[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) af[a] = tn_frag(stage, off(wm + a * 16));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = tn_frag(stage + kTOp, off(wn + b * 16));
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = mfma(af[a], bf[b], acc[a][b]);
-    };
-    if (n_steps > 0) dma(0, s0);
-    if (n_steps > 1) dma(1, s1);
-    if (n_steps > 2) dma(2, s2);
-    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-        if (s + 2 < n_steps) wait_vmcnt<8>();
-        else if (s + 1 < n_steps) wait_vmcnt<4>();
+        for (int dt = 0; dt < 8; ++dt) dw1[ht][dt] = dw2[ht][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float db1a[2] = {0.f, 0.f}, db2a[2] = {0.f, 0.f};
+    const bool db2_duty = sl == 0;
+
+    for (int i = 0; i < min(kBwdRing - 1, n_it); ++i) issue(i);
+    for (int it = 0; it < n_it; ++it) {
+        // this wave's copies of tile `it` have landed (4 per tile; those of
+        // the tiles after it may still be in flight), then every wave's
+        const int ahead = min(n_it - 1 - it, kBwdRing - 2);
+        if (ahead >= 2) wait_vmcnt<8>();
+        else if (ahead == 1) wait_vmcnt<4>();
         else wait_vmcnt<0>();
         barrier_lds();
-        if (s + 3 < n_steps) dma(s + 3, nxt);
-        mma(cur);
-    };
-    for (int s = 0; s < n_steps; s += 4) {
-        step(s, s0, s3);
-        if (s + 1 < n_steps) step(s + 1, s1, s0);
-        if (s + 2 < n_steps) step(s + 2, s2, s1);
-        if (s + 3 < n_steps) step(s + 3, s3, s2);
-    }
-    wait_vmcnt<0>();
-    float* out = (ROLE == 0 ? p.pw2 : p.pw1) + ((int64_t)q * p.n_chunks + chunk) * (int64_t)M * N;
-    const int l16 = lane & 15, g4 = lane >> 4;
+        // the ring slot of tile it - 1 is free: every wave has passed the barrier
+        if (it + kBwdRing - 1 < n_it) issue(it + kBwdRing - 1);
+        const unsigned char* const ks = ktile(it) + th * 32 * 256;       // this wave's 32 rows
+        int zero = 0;                                 // keeps the W1 reads inside the loop (as in the forward)
+        asm volatile("" : "+v"(zero));
+        const unsigned char* const gs = ks + kBwdTile;
+
+        f32x4 z[2][2], dh[2][2];                      // [tt][ht]
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int m = mi * 128 + wm + a * 16 + g4 * 4;
-            const int n = ni * 128 + wn + b * 16 + l16;
-            *reinterpret_cast<f32x4*>(out + (int64_t)n * M + m) = acc[a][b];
+        for (int tt = 0; tt < 2; ++tt) {
+            z[tt][0] = f32x4{bb0, bb0, bb0, bb0};
+            z[tt][1] = f32x4{bb1, bb1, bb1, bb1};
+            dh[tt][0] = dh[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 ka[2], ga[2], wb[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                ka[tt] = lds16(ks, sw_off(16 * tt + l16, 4 * s + g4, 256));
+                ga[tt] = lds16(gs, sw_off(16 * tt + l16, 4 * s + g4, 256));
+            }
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+                wb[ht] = lds16(w1s, sw_off(32 * hg + 16 * ht + l16, 4 * s + g4, 256) + zero);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht) {
+                    z[tt][ht] = mfma(ka[tt], wb[ht], z[tt][ht]);
+                    dh[tt][ht] = mfma(ga[tt], w2f[ht][s], dh[tt][ht]);
+                }
+        }
+        bf16x8 hp[2], dzp[2];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+            f32x4 hv[2], dv[2];
+            float sdz = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float zz = z[tt][ht][i];
+                    const float qq = normal_tail(fabsf(zz));
+                    hv[tt][i] = gelu_q(zz, qq);
+                    dv[tt][i] = dh[tt][ht][i] * gelu_grad_q(zz, qq);
+                    sdz += dv[tt][i];
+                }
+            db1a[ht] += sdz;
+            hp[ht] = pack8(hv[0], hv[1]);
+            dzp[ht] = pack8(dv[0], dv[1]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const bf16x8 gtr = tr_frag(gs, 16 * dt, l16, g4);
+            const bf16x8 ktr = tr_frag(ks, 16 * dt, l16, g4);
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) {
+                dw2[ht][dt] = mfma(hp[ht], gtr, dw2[ht][dt]);
+                dw1[ht][dt] = mfma(dzp[ht], ktr, dw1[ht][dt]);
+            }
+            if (db2_duty && (dt >> 1) == hg) {
+                float sg = 0.f;               // lane (column j, g4): its 8 tokens of column 16 dt + j
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sg += (float)gtr[i];
+                db2a[dt & 1] += sg;
+            }
+        }
+    }
+
+    // partials of this (range, token half)
+    const int64_t part = (int64_t)q * p.n_parts + rg * 2 + th;
+    float* const o1 = p.pw1 + part * H * d;
+    float* const o2 = p.pw2 + part * H * d;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t e = (int64_t)(u0 + 16 * ht + 4 * g4 + i) * d + 16 * dt + l16;
+                o1[e] = dw1[ht][dt][i];
+                o2[e] = dw2[ht][dt][i];
+            }
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+        float x = db1a[ht];
+        x += __shfl_xor(x, 16, kWave);
+        x += __shfl_xor(x, 32, kWave);
+        if (g4 == 0) p.pb1[part * H + u0 + 16 * ht + l16] = x;
+    }
+    if (db2_duty) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float x = db2a[e];
+            x += __shfl_xor(x, 16, kWave);
+            x += __shfl_xor(x, 32, kWave);
+            if (g4 == 0) p.pb2[part * d + 16 * (2 * hg + e) + l16] = x;
+        }
+    }
 }
 
 // --------------------------------------------------------------- update
 // Grid (problem, slice of kUpdSlices). mode 0: loss only (slot `step`, slice
-// 0); mode 1: gradient step `step`: each weight's partials reduced in a fixed
+// 0); mode 1: gradient step `step`: each weight's partials summed in a fixed
 // order by the one thread that owns it, which updates the fp32 master and
-// writes its bf16 copies; mode 2: bf16 copies only. Threads walk the
-// weights in the order of the partials' fastest axis, so the (n_chunks x
-// more numerous) partial reads coalesce.
+// writes its bf16 copies; mode 2: bf16 copies only. Threads walk the weights
+// along the partials' contiguous axis.
 constexpr int kUpdSlices = 8;
 
 __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, int mode) {
@@ -428,40 +637,39 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
     uint16_t* w2tb = reinterpret_cast<uint16_t*>(p.w2tb) + (int64_t)q * H * d;
     if (mode != 2 && slice == 0 && tid == 0 && p.losses) {
         double s = 0.0;
-        for (int m = 0; m < p.m_tiles; ++m) s += (double)p.loss_p[(int64_t)q * p.m_tiles + m];
+        for (int m = 0; m < p.n_loss_parts; ++m) s += (double)p.loss_p[(int64_t)q * p.n_loss_parts + m];
         p.losses[(int64_t)q * (p.n_steps + 1) + step] = (float)(s / (double)p.ctx_len);
     }
     if (mode == 0) return;
     if (mode == 1) {
         const float lr = p.lr;
-        const float* pw1 = p.pw1 + (int64_t)q * p.n_chunks * H * d;   // [c][i][u]
-        const float* pw2 = p.pw2 + (int64_t)q * p.n_chunks * H * d;   // [c][u][o]
+        const int np = p.n_parts;
+        const float* pw1 = p.pw1 + (int64_t)q * np * H * d;   // [part][u][i]
+        const float* pw2 = p.pw2 + (int64_t)q * np * H * d;   // [part][u][o]
         for (int e = e0; e < H * d; e += es) {
-            const int i = e / H, u = e - i * H;        // w1[u][i]; partials contiguous in u
-            float g = 0.f;
-            for (int c = 0; c < p.n_chunks; ++c) g += pw1[((int64_t)c * d + i) * H + u];
-            const float x = w1[(int64_t)u * d + i] - lr * g;
-            w1[(int64_t)u * d + i] = x;
-            w1b[(int64_t)u * d + i] = f32_to_bf16_bits(x);
-        }
-        for (int e = e0; e < d * H; e += es) {
-            const int u = e / d, o = e - u * d;        // w2[o][u]; partials contiguous in o
-            float g = 0.f;
-            for (int c = 0; c < p.n_chunks; ++c) g += pw2[((int64_t)c * H + u) * d + o];
-            const float x = w2[(int64_t)o * H + u] - lr * g;
-            w2[(int64_t)o * H + u] = x;
-            const uint16_t v = f32_to_bf16_bits(x);
+            float g1 = 0.f, g2 = 0.f;
+            for (int c = 0; c < np; ++c) {
+                g1 += pw1[(int64_t)c * H * d + e];
+                g2 += pw2[(int64_t)c * H * d + e];
+            }
+            const float x1 = w1[e] - lr * g1;         // w1[u][i], e = u d + i
+            w1[e] = x1;
+            w1b[e] = f32_to_bf16_bits(x1);
+            const int u = e / d, o = e - u * d;       // w2[o][u]
+            const float x2 = w2[(int64_t)o * H + u] - lr * g2;
+            w2[(int64_t)o * H + u] = x2;
+            const uint16_t v = f32_to_bf16_bits(x2);
             w2b[(int64_t)o * H + u] = v;
             w2tb[e] = v;                               // w2tb[u][o]
         }
         for (int u = e0; u < H; u += es) {
             float g = 0.f;
-            for (int m = 0; m < p.m_tiles; ++m) g += p.cs_dz[((int64_t)q * p.m_tiles + m) * H + u];
+            for (int c = 0; c < np; ++c) g += p.pb1[((int64_t)q * np + c) * H + u];
             b1[u] -= lr * g;
         }
         for (int o = e0; o < d; o += es) {
             float g = 0.f;
-            for (int m = 0; m < p.m_tiles; ++m) g += p.cs_g[((int64_t)q * p.m_tiles + m) * d + o];
+            for (int c = 0; c < np; ++c) g += p.pb2[((int64_t)q * np + c) * d + o];
             b2[o] -= lr * g;
         }
         return;
@@ -477,24 +685,24 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
 
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s) {
     const unsigned P = (unsigned)p.n_probs;
-    const dim3 t2((unsigned)(p.n_chunks * (kHeadDim / 128) * (p.hidden / 128)), P);
+    const bool resident = p.hidden <= kFwdMaxHidden;
+    const dim3 gf(P * (unsigned)p.fwd_ranges);
+    const int per_xcd = (int)(((P + 7) / 8) * (unsigned)p.m_tiles);
+    const dim3 gt((unsigned)per_xcd * 8u);
+    const dim3 gb(((P + 7) / 8) * 8u * (unsigned)(p.hidden / 128 * p.bwd_ranges));
     hipError_t e;
     hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, 0, 2);
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), s)) != hipSuccess) return e;
-    // Fused token-tile products: (problem, tile) pairs dealt to the 8 XCDs by
-    // problem (see fit_fused_kernel).
-    const int per_xcd = (int)(((P + 7) / 8) * (unsigned)p.m_tiles);
-    const dim3 gf((unsigned)per_xcd * 8u);
     for (int it = 0; it < p.n_steps; ++it) {
-        hipLaunchKernelGGL((fit_fused_kernel<true>), gf, dim3(kFThreads), 0, s, p, per_xcd);
-        hipLaunchKernelGGL((fit_tn_kernel<0>), t2, dim3(256), 0, s, p);
-        hipLaunchKernelGGL((fit_tn_kernel<1>), t2, dim3(256), 0, s, p);
+        if (resident) hipLaunchKernelGGL((fit_fwd_kernel<true>), gf, dim3(kFitThreads), 0, s, p);
+        else hipLaunchKernelGGL((fit_fwd_tiled_kernel<true>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
+        hipLaunchKernelGGL(fit_bwd_kernel, gb, dim3(kFitThreads), 0, s, p);
         hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, it, 1);
     }
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((fit_fused_kernel<false>), gf, dim3(kFThreads), 0, s, p, per_xcd);
+    if (resident) hipLaunchKernelGGL((fit_fwd_kernel<false>), gf, dim3(kFitThreads), 0, s, p);
+    else hipLaunchKernelGGL((fit_fwd_tiled_kernel<false>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
     hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, p.n_steps, 0);
-
     return hipGetLastError();
 }
 

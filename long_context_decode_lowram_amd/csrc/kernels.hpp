@@ -97,8 +97,11 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s);   // M, iterati
 struct FitParams {
     int n_layers, ctx_len, n_kv, hidden, n_steps;
     int n_probs;                  // n_layers * n_kv
-    int m_tiles;                  // 64-token tiles
-    int n_chunks, chunk_len;      // token chunks of the weight-gradient products
+    int m_tiles;                  // 64-token tiles (tiled forward, h > 256)
+    int fwd_ranges;               // token ranges per problem of the resident-weight forward (h <= 256)
+    int bwd_ranges;               // token ranges per problem and hidden slice of the backward
+    int n_parts;                  // weight-gradient partials per problem: 2 * bwd_ranges
+    int n_loss_parts;             // loss partials per problem
     float lr;
     const __bf16* keys;           // [L, T, Hkv*d]
     const __bf16* v;              // [L, T, Hkv, d]
@@ -106,15 +109,13 @@ struct FitParams {
     float* w1; float* b1; float* w2; float* b2;   // [P, h, d], [P, h], [P, d, h], [P, d]
     float* losses;                // [P, n_steps + 1] or null
     // workspace, per problem
-    __bf16* hb;                   // [P, T, h]  gelu(K W1^T + b1)
     __bf16* gb;                   // [P, T, d]  (2 / T)(v_hat - v)
-    __bf16* dzb;                  // [P, T, h]  gradient at the pre-activations
     __bf16* w1b; __bf16* w2b; __bf16* w2tb;       // bf16 copies: [P, h, d], [P, d, h], [P, h, d]
-    float* pw1;                   // [P, n_chunks, d, h]  partial dW1, stored [i][u]
-    float* pw2;                   // [P, n_chunks, h, d]  partial dW2, stored [u][o]
-    float* cs_g;                  // [P, m_tiles, d]      column sums of g
-    float* cs_dz;                 // [P, m_tiles, h]      column sums of dz
-    float* loss_p;                // [P, m_tiles]         sums of squared errors
+    float* pw1;                   // [P, n_parts, h, d]  partial dW1
+    float* pw2;                   // [P, n_parts, h, d]  partial dW2, stored transposed ([u][o])
+    float* pb1;                   // [P, n_parts, h]     partial db1
+    float* pb2;                   // [P, n_parts, d]     partial db2
+    float* loss_p;                // [P, n_loss_parts]   sums of squared errors
 };
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s);
 

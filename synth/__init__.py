@@ -437,6 +437,8 @@ class FitConfig:
 FIT_CONFIGS = {c.name: c for c in (
     FitConfig("f_small_ragged", 2, 1000, 2, 128, 3),
     FitConfig("f_mid", 2, 8192, 8, 256, 2, lr=0.02),
+    # a hidden layer too wide for the resident-weight forward (the tiled one runs), ragged T
+    FitConfig("f_wide_ragged", 1, 700, 2, 384, 2, lr=0.01),
     # a 32-layer Llama-3.1-8B prefill at 131072 tokens, h = 256, the quick two-step fit
     FitConfig("f_llama_131k", 32, 131072, 8, 256, 2, lr=0.02),
 )}

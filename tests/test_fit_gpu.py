@@ -86,6 +86,13 @@ def test_small_ragged_every_problem():
     print(f"f_small_ragged: worst update rel err {worst:.2e}", flush=True)
 
 
+def test_wide_hidden_every_problem():
+    fc = synth.FIT_CONFIGS["f_wide_ragged"]         # h = 384: the tiled forward, three hidden slices
+    x, start, losses = _fit(fc)
+    worst = max(_check(fc, x, start, losses, l, h)[0] for l in range(fc.n_layers) for h in range(fc.n_kv_heads))
+    print(f"f_wide_ragged: worst update rel err {worst:.2e}", flush=True)
+
+
 def test_mid_sampled():
     fc = synth.FIT_CONFIGS["f_mid"]
     x, start, losses = _fit(fc)
