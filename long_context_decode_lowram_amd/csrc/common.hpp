@@ -19,12 +19,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16 bits, round to nearest even (NaN kept quiet).
+// float32 -> bfloat16 bits, round to nearest even (NaN kept quiet). Written
+// with selects, not branches, so a wave never splits on it.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : rounded);
 }
 
 // binary64 -> bfloat16 bits with one round-to-nearest-even step: first to
@@ -33,15 +33,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // bits than bfloat16 at every exponent, so the two steps round exactly like
 // one.
 __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
-    float f = static_cast<float>(x);
+    const float f = static_cast<float>(x);
     const double back = static_cast<double>(f);
-    if (back != x && x == x) {
-        uint32_t u = __float_as_uint(f);
-        if (fabs(back) > fabs(x)) u -= 1u;
-        u |= 1u;
-        f = __uint_as_float(u);
-    }
-    return f32_to_bf16_bits(f);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t odd = (u - (fabs(back) > fabs(x) ? 1u : 0u)) | 1u;
+    return f32_to_bf16_bits(__uint_as_float(back != x && x == x ? odd : u));
 }
 
 // Element load of a stored tensor as float (int8 returns the raw code).

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_util.hpp"
@@ -39,8 +41,11 @@ __device__ __forceinline__ float gelu_grad_q(float z, float q) {
     return fmaf(z, phi, z >= 0.0f ? 1.0f - q : q);
 }
 
+// Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -61,20 +66,21 @@ __device__ __forceinline__ uint32_t sw_off(int row, int piece, int row_bytes) {
 // token data passes through LDS and the waves never wait for each other.
 // Per tile and 32 hidden units c:
 //   Z^T (2 x 2 tiles of 16) = W1[32 c ..] K^T + b1      16 MFMAs
-//   H^T = gelu(Z^T), bf16: lane (token j, g4) holds units 4 g4 + i and
-//         16 + 4 g4 + i, the k-slots of one B fragment
+//   H^T = gelu(Z^T) (gelu_tail16), bf16: lane (token j, g4) holds units
+//         4 g4 + i and 16 + 4 g4 + i, the k-slots of one B fragment
 //   V_hat^T (8 x 2 tiles) += W2[:, 32 c ..] H^T          16 MFMAs
 // W2's columns are stored in LDS in that k-slot order (within every 32
 // units, piece g4 holds units 4 g4 .. + 3 and 16 + 4 g4 .. + 3), so its A
 // fragments are single 16-byte reads. The V_hat^T accumulators start at b2;
 // then V_hat^T += W_lin K^T and G = (2 / T)(V_hat - V) by element; the lane's
 // squared errors go to a per-wave loss partial.
-template <bool WRITE_G>
+template <bool WRITE_G, int NC>                      // NC = h / 32 hidden chunks (4 or 8)
 __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsAll];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int H = p.hidden, T = p.ctx_len, d = kHeadDim;
+    constexpr int H = 32 * NC;
+    const int T = p.ctx_len, d = kHeadDim;
     const int q = blockIdx.x / p.fwd_ranges, rg = blockIdx.x - q * p.fwd_ranges;
     const int l = q / p.n_kv, h = q - l * p.n_kv;
     const int ldkv = p.n_kv * d;
@@ -154,9 +160,13 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
         // loads drains in order): keys, the first hidden chunk's b1, b2 (the
         // accumulators start at it), V for the G step.
         load_k(tile, kf);
-        f32x4 bn[2];                                  // b1 of the next hidden chunk, one chunk ahead
+        // b1 of hidden chunks c and c + 1 (loaded two chunks ahead)
+        f32x4 bq[3][2];
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) bn[ht] = *reinterpret_cast<const f32x4*>(b1 + 16 * ht + 4 * g4 + zero);
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+                bq[c][ht] = *reinterpret_cast<const f32x4*>(b1 + 32 * c + 16 * ht + 4 * g4 + zero);
         f32x4 acc[8][2];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -173,41 +183,57 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
                 vv[tt][dt] = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                rv, ((uint32_t)(t0 + 16 * tt + l16) * ldkv_u + 16 * dt + 4 * g4) * 2u, 0, 0));
-        for (int c = 0; c < H / 32; ++c) {
-            f32x4 z[2][2];                            // [ht][tt]
+        __builtin_amdgcn_sched_barrier(0);            // every load of the tile is in flight before the products
+        // Z^T of hidden chunk c: zt[2 ht + tt], started at b1, 16 MFMAs over the keys
+        auto zchunk = [&](int c, f32x4 (&zt)[4]) {
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) z[ht][tt] = bn[ht];
-            if (c + 1 < H / 32) {
-#pragma unroll
-                for (int ht = 0; ht < 2; ++ht)
-                    bn[ht] = *reinterpret_cast<const f32x4*>(b1 + 32 * (c + 1) + 16 * ht + 4 * g4);
-            }
+                for (int tt = 0; tt < 2; ++tt) zt[2 * ht + tt] = bq[c % 3][ht];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int ht = 0; ht < 2; ++ht) {
                     const bf16x8 wf = lds16(w1s, sw_off(32 * c + 16 * ht + l16, 4 * s + g4, 256));
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) z[ht][tt] = mfma(wf, kf[tt][s], z[ht][tt]);
+                    for (int tt = 0; tt < 2; ++tt) zt[2 * ht + tt] = mfma(wf, kf[tt][s], zt[2 * ht + tt]);
                 }
+        };
+        // Chunks in a software pipeline: the next chunk's Z MFMAs are issued
+        // between this chunk's GELU operations, so the matrix pipe and the
+        // vector ALU work side by side; then this chunk's W2 products.
+        f32x4 zc[4], zn[4];
+        zchunk(0, zc);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c + 2 < NC) {
+#pragma unroll
+                for (int ht = 0; ht < 2; ++ht)
+                    bq[(c + 2) % 3][ht] = *reinterpret_cast<const f32x4*>(b1 + 32 * (c + 2) + 16 * ht + 4 * g4);
+                __builtin_amdgcn_sched_barrier(0);    // issue the prefetch here, not next to its use
+            }
+            if (c + 1 < NC) zchunk(c + 1, zn);
+            gelu_tail16(zc);                          // H^T in place
             bf16x8 hf[2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                f32x4 g0, g1;
+            for (int tt = 0; tt < 2; ++tt) hf[tt] = pack8(zc[tt], zc[2 + tt]);
+            if (c + 1 < NC) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);      // the next chunk's W1 fragments
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    g0[i] = gelu_q(z[0][tt][i], normal_tail(fabsf(z[0][tt][i])));
-                    g1[i] = gelu_q(z[1][tt][i], normal_tail(fabsf(z[1][tt][i])));
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then a share of the GELU
                 }
-                hf[tt] = pack8(g0, g1);
             }
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 const bf16x8 wf = lds16(w2s, sw_off(16 * dt + l16, 4 * c + g4, w2row));
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = mfma(wf, hf[tt], acc[dt][tt]);
+            }
+            if (c + 1 < NC) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zc[i] = zn[i];
             }
         }
 #pragma unroll
@@ -407,14 +433,14 @@ __global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams
 //   dW2^T[u][o] += H^T G                B = G^T by transposing LDS reads
 //   dW1  [u][i] += dZ^T K               B = K^T likewise        32 MFMAs
 //   db2 (slice 0; wave w sums d tiles 2 (w & 3), + 1) from the same G^T
-//   fragments and db1 from dZ, on the vector ALU in fp32.
+//   fragments by bf16 dot products with ones, db1 from dZ, both in fp32.
 // Tokens past T read as zeros: their G and dH vanish, so they add nothing.
 // The two token halves write separate partials; the update sums them.
 constexpr int kBwdTok = 64;
-constexpr int kBwdRing = 4;
+constexpr int kBwdRing = 2;
 constexpr int kBwdTile = kBwdTok * 256;          // 16 KB: 64 rows of 128 bf16
-constexpr int kBwdW1 = 128 * 256;                // the slice's W1 rows: 32 KB
-static_assert(kBwdW1 + kBwdRing * 2 * kBwdTile == kLdsAll, "backward LDS layout");
+constexpr int kBwdW = 128 * 256;                 // the slice's W1 or W2^T rows: 32 KB
+static_assert(kBwdRing * 2 * kBwdTile + 2 * kBwdW <= kLdsAll, "backward LDS layout");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_t;
@@ -438,7 +464,12 @@ __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* slab, int c0, int
 }
 
 __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsAll];
+    // Separate objects, so the compiler's waits for the direct-to-LDS copies
+    // into one tile buffer do not hold up reads of the other.
+    __shared__ __attribute__((aligned(16))) unsigned char tile0[2 * kBwdTile];
+    __shared__ __attribute__((aligned(16))) unsigned char tile1[2 * kBwdTile];
+    __shared__ __attribute__((aligned(16))) unsigned char w1s[kBwdW];   // the slice's W1 rows [128][d]
+    __shared__ __attribute__((aligned(16))) unsigned char w2s[kBwdW];   // the slice's W2^T rows [128][d]
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const int hg = w & 3, th = w >> 2;
@@ -456,20 +487,22 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
     const int ldkv = p.n_kv * d;
     const int u0 = sl * 128 + hg * 32;
 
-    unsigned char* const w1s = lds;
     {
-        const u32x4* src = reinterpret_cast<const u32x4*>(p.w1b + ((int64_t)q * H + sl * 128) * d);
-        for (int i = tid; i < 128 * 16; i += kFitThreads)
-            *reinterpret_cast<u32x4*>(w1s + sw_off(i >> 4, i & 15, 256)) = src[i];
+        const u32x4* s1 = reinterpret_cast<const u32x4*>(p.w1b + ((int64_t)q * H + sl * 128) * d);
+        const u32x4* s2 = reinterpret_cast<const u32x4*>(p.w2tb + ((int64_t)q * H + sl * 128) * d);
+        u32x4 v1[4], v2[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v1[k] = s1[tid + k * kFitThreads];
+            v2[k] = s2[tid + k * kFitThreads];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = tid + k * kFitThreads;
+            *reinterpret_cast<u32x4*>(w1s + sw_off(i >> 4, i & 15, 256)) = v1[k];
+            *reinterpret_cast<u32x4*>(w2s + sw_off(i >> 4, i & 15, 256)) = v2[k];
+        }
     }
-    // W2^T fragments: w2f[ht][s] = W2^T[u0 + 16 ht + l16][32 s + 8 g4 .. + 7]
-    bf16x8 w2f[2][4];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            w2f[ht][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                p.w2tb + ((int64_t)q * H + u0 + 16 * ht + l16) * d + 32 * s + 8 * g4));
     const float bb0 = p.b1[(int64_t)q * H + u0 + l16], bb1 = p.b1[(int64_t)q * H + u0 + 16 + l16];
 
     const int n_all = (T + kBwdTok - 1) / kBwdTok;
@@ -477,17 +510,19 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
     const int ib = rg * per, n_it = max(0, min(n_all, ib + per) - ib);
     const __bf16* const kq = p.keys + (int64_t)l * T * ldkv + hh * d;
     const __bf16* const gq = p.gb + (int64_t)q * T * d;
-    auto ktile = [&](int i) { return lds + kBwdW1 + (i & (kBwdRing - 1)) * 2 * kBwdTile; };
     // Tile i's keys and G rows: wave w copies rows 8 w .. 8 w + 7 of each
     // (two copies of 4 rows; lane L fills row 4 c' + L / 16, slot L % 16 with
     // the piece that the swizzle puts there). Rows past T read as zeros.
-    const int crow = lane >> 4, cslot = lane & 15;
-    auto issue = [&](int i) {
+    auto issue = [&](int i, unsigned char* const kt) {
         const int t0 = (ib + i) * kBwdTok;
-        unsigned char* const kt = ktile(i);
         const int rows = max(0, T - t0);
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kq + (int64_t)t0 * ldkv, (uint32_t)(rows * ldkv * 2));
         const __amdgpu_buffer_rsrc_t rgt = buffer_rsrc(gq + (int64_t)t0 * d, (uint32_t)(rows * d * 2));
+        // the lane's offsets are recomputed per tile (a few ALU operations)
+        // rather than held in registers for the whole loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int crow = ln >> 4, cslot = ln & 15;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int row = 8 * w + 4 * c + crow;
@@ -505,21 +540,17 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
     float db1a[2] = {0.f, 0.f}, db2a[2] = {0.f, 0.f};
     const bool db2_duty = sl == 0;
 
-    for (int i = 0; i < min(kBwdRing - 1, n_it); ++i) issue(i);
-    for (int it = 0; it < n_it; ++it) {
-        // this wave's copies of tile `it` have landed (4 per tile; those of
-        // the tiles after it may still be in flight), then every wave's
-        const int ahead = min(n_it - 1 - it, kBwdRing - 2);
-        if (ahead >= 2) wait_vmcnt<8>();
-        else if (ahead == 1) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-        barrier_lds();
-        // the ring slot of tile it - 1 is free: every wave has passed the barrier
-        if (it + kBwdRing - 1 < n_it) issue(it + kBwdRing - 1);
-        const unsigned char* const ks = ktile(it) + th * 32 * 256;       // this wave's 32 rows
-        int zero = 0;                                 // keeps the W1 reads inside the loop (as in the forward)
-        asm volatile("" : "+v"(zero));
+    // One tile per step: wait for its copies, the barrier, then the copies of
+    // the next tile into the other buffer (whose tile every wave has finished).
+    auto step = [&](auto slot_c, int it) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        wait_vmcnt<0>();                              // this wave's copies of tile `it`
+        barrier_lds();                                // and every wave's
+        if (it + 1 < n_it) issue(it + 1, SLOT ? tile0 : tile1);
+        const unsigned char* const ks = (SLOT ? tile1 : tile0) + th * 32 * 256;     // this wave's 32 rows
         const unsigned char* const gs = ks + kBwdTile;
+        int zero = 0;                                 // keeps the weight reads inside the loop (as in the forward)
+        asm volatile("" : "+v"(zero));
 
         f32x4 z[2][2], dh[2][2];                      // [tt][ht]
 #pragma unroll
@@ -530,21 +561,23 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            bf16x8 ka[2], ga[2], wb[2];
+            bf16x8 ka[2], ga[2], wb[2], wd[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 ka[tt] = lds16(ks, sw_off(16 * tt + l16, 4 * s + g4, 256));
                 ga[tt] = lds16(gs, sw_off(16 * tt + l16, 4 * s + g4, 256));
             }
 #pragma unroll
-            for (int ht = 0; ht < 2; ++ht)
+            for (int ht = 0; ht < 2; ++ht) {
                 wb[ht] = lds16(w1s, sw_off(32 * hg + 16 * ht + l16, 4 * s + g4, 256) + zero);
+                wd[ht] = lds16(w2s, sw_off(32 * hg + 16 * ht + l16, 4 * s + g4, 256) + zero);
+            }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int ht = 0; ht < 2; ++ht) {
                     z[tt][ht] = mfma(ka[tt], wb[ht], z[tt][ht]);
-                    dh[tt][ht] = mfma(ga[tt], w2f[ht][s], dh[tt][ht]);
+                    dh[tt][ht] = mfma(ga[tt], wd[ht], dh[tt][ht]);
                 }
         }
         bf16x8 hp[2], dzp[2];
@@ -575,13 +608,25 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
                 dw2[ht][dt] = mfma(hp[ht], gtr, dw2[ht][dt]);
                 dw1[ht][dt] = mfma(dzp[ht], ktr, dw1[ht][dt]);
             }
-            if (db2_duty && (dt >> 1) == hg) {
-                float sg = 0.f;               // lane (column j, g4): its 8 tokens of column 16 dt + j
+        }
+        if (db2_duty) {
+            // lane (column j, g4): its 8 tokens of columns 16 dt + j, dt = 2 (w & 3) + e,
+            // summed in fp32 by bf16 dot products with ones
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sg += (float)gtr[i];
-                db2a[dt & 1] += sg;
+            for (int e = 0; e < 2; ++e) {
+                const bf16x8 gtr = tr_frag(gs, 16 * (2 * hg + e), l16, g4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    db2a[e] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{gtr[2 * k], gtr[2 * k + 1]}, one2, db2a[e], false);
             }
         }
+    };
+    if (n_it > 0) issue(0, tile0);
+    for (int it = 0; it < n_it; it += 2) {
+        step(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < n_it) step(std::integral_constant<int, 1>{}, it + 1);
     }
 
     // partials of this (range, token half)
@@ -685,7 +730,7 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
 
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s) {
     const unsigned P = (unsigned)p.n_probs;
-    const bool resident = p.hidden <= kFwdMaxHidden;
+    const bool resident = p.hidden <= kFwdMaxHidden, wide = p.hidden > 128;
     const dim3 gf(P * (unsigned)p.fwd_ranges);
     const int per_xcd = (int)(((P + 7) / 8) * (unsigned)p.m_tiles);
     const dim3 gt((unsigned)per_xcd * 8u);
@@ -694,13 +739,15 @@ hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStrea
     hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, 0, 2);
     if (ev_begin && (e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), s)) != hipSuccess) return e;
     for (int it = 0; it < p.n_steps; ++it) {
-        if (resident) hipLaunchKernelGGL((fit_fwd_kernel<true>), gf, dim3(kFitThreads), 0, s, p);
+        if (resident && wide) hipLaunchKernelGGL((fit_fwd_kernel<true, 8>), gf, dim3(kFitThreads), 0, s, p);
+        else if (resident) hipLaunchKernelGGL((fit_fwd_kernel<true, 4>), gf, dim3(kFitThreads), 0, s, p);
         else hipLaunchKernelGGL((fit_fwd_tiled_kernel<true>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
         hipLaunchKernelGGL(fit_bwd_kernel, gb, dim3(kFitThreads), 0, s, p);
         hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, it, 1);
     }
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), s)) != hipSuccess) return e;
-    if (resident) hipLaunchKernelGGL((fit_fwd_kernel<false>), gf, dim3(kFitThreads), 0, s, p);
+    if (resident && wide) hipLaunchKernelGGL((fit_fwd_kernel<false, 8>), gf, dim3(kFitThreads), 0, s, p);
+    else if (resident) hipLaunchKernelGGL((fit_fwd_kernel<false, 4>), gf, dim3(kFitThreads), 0, s, p);
     else hipLaunchKernelGGL((fit_fwd_tiled_kernel<false>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
     hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, p.n_steps, 0);
     return hipGetLastError();
