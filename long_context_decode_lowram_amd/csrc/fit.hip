@@ -7,13 +7,14 @@
 // gradient descent on W1, b1, W2, b2 (W_lin fixed). Per step and problem
 // (layer, KV head), with weights stored output-major:
 //   Z = K W1^T + b1,  H = gelu(Z)
-//   G = (2 / T)(K W_lin^T + H W2^T + b2 - V)           fit_fwd_kernel (loss partials too)
-//   dZ = (G W2) * gelu'(Z)
-//   dW2 = G^T H,  dW1 = dZ^T K,  db2 = sum_t G,  db1 = sum_t dZ
-//                                                       fit_bwd_kernel (Z and H recomputed)
-//   theta -= lr dL/dtheta                               fit_update_kernel
-// Products on bf16 MFMA with fp32 sums; the parameters are fp32 masters with
-// bf16 copies for the products. Only G goes through HBM between the passes.
+//   E = K W_lin^T + H W2^T + b2 - V                     fit_fwd_kernel (loss partials too)
+//   dZ = (E W2) * gelu'(Z)
+//   E^T H,  dZ^T K,  sum_t E,  sum_t dZ                 fit_bwd_kernel (Z and H recomputed)
+//   theta -= lr (2 / T) (those sums)                    fit_update_kernel
+// (dL/dW2 = G^T H with G = (2 / T) E, and so on: every gradient is linear in
+// E, so the factor 2 / T is applied once, in the update.) Products on bf16
+// MFMA with fp32 sums; the parameters are fp32 masters with bf16 copies for
+// the products. Only E goes through HBM between the passes.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -30,15 +31,17 @@ constexpr int kLdsAll = 163840;           // the whole LDS of a CU
 constexpr int kFwdMaxHidden = 256;        // widest hidden layer whose weights stay resident in LDS
 
 // GELU and its derivative from the normal tail fit (normal_tail): with
-// a = |z| and q = Q(a), gelu(z) = max(z, 0) - a q and
-// gelu'(z) = Phi(z) + z phi(z), Phi(z) = 1 - q for z >= 0 and q below;
-// phi(z) = 2^(-z^2 / (2 ln 2) + log2(1 / sqrt(2 pi))).
+// q = Q(|z|), Phi(z) = 1 - q for z >= 0 and q below; gelu(z) = z Phi(z) and
+// gelu'(z) = Phi(z) + z phi(z), phi(z) = 2^(-z^2 / (2 ln 2) + log2(1 / sqrt(2 pi))).
 __device__ __forceinline__ float gelu_q(float z, float q) {
     return fmaf(-fabsf(z), q, __builtin_amdgcn_fmed3f(z, 0.0f, 3.0e38f));
 }
-__device__ __forceinline__ float gelu_grad_q(float z, float q) {
+__device__ __forceinline__ void gelu_and_grad(float z, float& h, float& g) {
+    const float q = normal_tail(fabsf(z));
+    const float cdf = z >= 0.0f ? 1.0f - q : q;
     const float phi = __builtin_amdgcn_exp2f(fmaf(-0.72134752044448170f * z, z, -1.3257480647361593f));
-    return fmaf(z, phi, z >= 0.0f ? 1.0f - q : q);
+    h = z * cdf;
+    g = fmaf(z, phi, cdf);
 }
 
 // Two floats to packed bf16 (round to nearest even, one v_cvt_pk_bf16_f32).
@@ -72,9 +75,11 @@ __device__ __forceinline__ uint32_t sw_off(int row, int piece, int row_bytes) {
 // W2's columns are stored in LDS in that k-slot order (within every 32
 // units, piece g4 holds units 4 g4 .. + 3 and 16 + 4 g4 .. + 3), so its A
 // fragments are single 16-byte reads. The V_hat^T accumulators start at b2;
-// then V_hat^T += W_lin K^T and G = (2 / T)(V_hat - V) by element; the lane's
-// squared errors go to a per-wave loss partial.
-template <bool WRITE_G, int NC>                      // NC = h / 32 hidden chunks (4 or 8)
+// then V_hat^T += W_lin K^T, and V is subtracted on the matrix pipe too (one
+// MFMA per tile pair with a -I fragment against V read like the keys), so E
+// comes out of the accumulators; the lane's squared errors go to a per-wave
+// loss partial.
+template <bool WRITE_E, int NC>                      // NC = h / 32 hidden chunks (4 or 8)
 __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsAll];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,7 +140,15 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
     const __amdgpu_buffer_rsrc_t rgo = buffer_rsrc(p.gb + (int64_t)q * T * d, (uint32_t)((int64_t)T * d * 2));
     const float* const b1 = p.b1 + (int64_t)q * H;
     const float* const b2 = p.b2 + (int64_t)q * d;
-    const float gscale = 2.0f / (float)T;
+    // -I as A fragments (rows d, k-slots d): neg_eye[e] serves the d tiles with
+    // dt % 2 == e against k-step dt / 2; lane (i, g4) holds -1 in slot
+    // 16 e + i - 8 g4 when that lies in 0..7.
+    bf16x8 neg_eye[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            neg_eye[e][jj] = (__bf16)(16 * e + l16 - 8 * g4 == jj ? -1.0f : 0.0f);
     // Keys of a tile as B fragments: kf[tt][s] = K[t0 + 16 tt + l16][32 s + 8 g4 .. + 7]
     // (rows past T read as zeros).
     auto load_k = [&](int tile, bf16x8 (&kf)[2][4]) {
@@ -157,8 +170,8 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
         int zero = 0;
         asm volatile("" : "+v"(zero));
         // Loads in the order they are needed (the counter of outstanding
-        // loads drains in order): keys, the first hidden chunk's b1, b2 (the
-        // accumulators start at it), V for the G step.
+        // loads drains in order): keys, the first hidden chunks' b1, b2 (the
+        // accumulators start at it), V for the last step.
         load_k(tile, kf);
         // b1 of hidden chunks c and c + 1 (loaded two chunks ahead)
         f32x4 bq[3][2];
@@ -174,15 +187,15 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = bb;
         }
-        // V for the G step: vv[tt][dt] = V[t0 + 16 tt + l16][16 dt + 4 g4 .. + 3]
-        u32x2 vv[2][8];
+        // V as B fragments, like the keys: vf[tt][s] = V[t0 + 16 tt + l16][32 s + 8 g4 .. + 7]
+        bf16x8 vf[2][4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                vv[tt][dt] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                               rv, ((uint32_t)(t0 + 16 * tt + l16) * ldkv_u + 16 * dt + 4 * g4) * 2u, 0, 0));
+            for (int s = 0; s < 4; ++s)
+                vf[tt][s] = as_bf16x8(__builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rv, ((uint32_t)(t0 + 16 * tt + l16) * ldkv_u + 32 * s + 8 * g4) * 2u, 0, 0)));
         __builtin_amdgcn_sched_barrier(0);            // every load of the tile is in flight before the products
         // Z^T of hidden chunk c: zt[2 ht + tt], started at b1, 16 MFMAs over the keys
         auto zchunk = [&](int c, f32x4 (&zt)[4]) {
@@ -244,25 +257,25 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_fwd_kernel(FitParams p) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = mfma(wf, kf[tt][s], acc[dt][tt]);
             }
+        // E^T = V_hat^T - V^T: d tile dt meets the k-step dt / 2 of V
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) acc[dt][tt] = mfma(neg_eye[dt & 1], vf[tt][dt >> 1], acc[dt][tt]);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int t = t0 + 16 * tt + l16;
             const bool valid = t < T;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                const float vt[4] = {bf16_lo(vv[tt][dt][0]), bf16_hi(vv[tt][dt][0]), bf16_lo(vv[tt][dt][1]),
-                                     bf16_hi(vv[tt][dt][1])};
-                float g[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = acc[dt][tt][i] - vt[i];
-                    if (valid) loss = fmaf(e, e, loss);
-                    g[i] = gscale * e;
-                }
-                if (WRITE_G)      // rows past T fall outside the descriptor and are dropped
+                for (int i = 0; i < 4; ++i)
+                    if (valid) loss = fmaf(acc[dt][tt][i], acc[dt][tt][i], loss);
+                if (WRITE_E)      // rows past T fall outside the descriptor and are dropped
                     __builtin_amdgcn_raw_buffer_store_b64(
                         __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
-                                           u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])}),
+                                           u32x2{pack_bf16x2(acc[dt][tt][0], acc[dt][tt][1]),
+                                                 pack_bf16x2(acc[dt][tt][2], acc[dt][tt][3])}),
                         rgo, (uint32_t)((t * d + 16 * dt + 4 * g4) * 2), 0, 0);
             }
         }
@@ -289,7 +302,7 @@ __device__ __forceinline__ uint32_t tslot(int row, int piece) {
     return (uint32_t)(row * kTRowB + ((piece ^ (row & 7)) << 4));
 }
 
-template <bool WRITE_G>
+template <bool WRITE_E>
 __global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams p, int n_per_xcd) {
     __shared__ __attribute__((aligned(16))) unsigned char kt[2 * kTHalf];   // keys of the tile
     __shared__ __attribute__((aligned(16))) unsigned char ht[2 * kTHalf];   // H_u
@@ -362,7 +375,6 @@ __global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams
         const int hf = n >> 6, nn = n & 63;
         *reinterpret_cast<u32x2*>(tile + hf * kTHalf + tslot(r, nn >> 3) + (nn & 7) * 2) = v;
     };
-    const float gscale = 2.0f / (float)T;
     const __bf16* w1b = p.w1b + (int64_t)q * H * d;
     const __bf16* w2b = p.w2b + (int64_t)q * d * H;
     const __bf16* wl = p.w_lin + (int64_t)q * d * d;
@@ -400,9 +412,9 @@ __global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams
             for (int v = 0; v < 4; ++v) {
                 const float e = accv[a][v] + b2[n + v] - vt[v];
                 loss = fmaf(e, e, loss);
-                g[v] = gscale * e;
+                g[v] = e;
             }
-            if (WRITE_G)
+            if (WRITE_E)
                 *reinterpret_cast<u32x2*>(p.gb + ((int64_t)q * T + t) * d + n) =
                     u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
         }
@@ -420,21 +432,22 @@ __global__ __launch_bounds__(kFitThreads, 2) void fit_fwd_tiled_kernel(FitParams
 // ------------------------------------------------------------ backward
 // One workgroup per (problem, 128-unit hidden slice, token range), 64 tokens
 // per iteration. Wave w takes hidden units u0 = 128 slice + 32 (w & 3) .. + 31
-// and the 32-token half w >> 2 of each tile, and keeps its dW1 and dW2^T rows
-// (32 x 128 each) in registers for the whole range. Resident: the slice's W1
-// rows in LDS (B operand of Z), the wave's W2^T rows as register fragments
-// (B operand of G W2). The keys and G of each tile arrive by direct
-// global -> LDS copies into a four-tile ring, three tiles ahead. Per tile:
+// and the 32-token half w >> 2 of each tile, and keeps its rows of the two
+// weight-gradient sums, H^T E and dZ^T K (32 x 128 each, up to the factor
+// 2 / T), in registers for the whole range. Resident in LDS: the slice's W1
+// rows (B operand of Z) and W2^T rows (B operand of E W2). The keys and E of
+// each tile arrive by direct global -> LDS copies into two alternating
+// buffers, one tile ahead. Per tile:
 //   Z  [tok][u] = K W1^T + b1           A = K rows (LDS)        16 MFMAs
-//   dH [tok][u] = G W2                  A = G rows (LDS)        16 MFMAs
+//   dH [tok][u] = E W2                  A = E rows (LDS)        16 MFMAs
 //   H = gelu(Z), dZ = dH gelu'(Z); lane (unit j, g4) holds tokens 4 g4 + i
 //     and 16 + 4 g4 + i of its unit, the k-slots of one A fragment of the
 //     token contractions below
-//   dW2^T[u][o] += H^T G                B = G^T by transposing LDS reads
-//   dW1  [u][i] += dZ^T K               B = K^T likewise        32 MFMAs
-//   db2 (slice 0; wave w sums d tiles 2 (w & 3), + 1) from the same G^T
-//   fragments by bf16 dot products with ones, db1 from dZ, both in fp32.
-// Tokens past T read as zeros: their G and dH vanish, so they add nothing.
+//   (H^T E)[u][o] += ...                B = E^T by transposing LDS reads
+//   (dZ^T K)[u][i] += ...               B = K^T likewise        32 MFMAs
+//   sum_t E (slice 0; wave w sums d tiles 2 (w & 3), + 1) from E^T
+//   fragments by bf16 dot products with ones, sum_t dZ from dZ, both in fp32.
+// Tokens past T read as zeros: their E and dH vanish, so they add nothing.
 // The two token halves write separate partials; the update sums them.
 constexpr int kBwdTok = 64;
 constexpr int kBwdRing = 2;
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
     const int n_sl = H / 128;
     // blockIdx -> (problem, slice, range): XCD x = blockIdx % 8 takes
     // problems x, x + 8, ..., each problem's slices and ranges back to back,
-    // so they share the keys and G of a tile in that XCD's L2.
+    // so they share the keys and E of a tile in that XCD's L2.
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int per_q = n_sl * p.bwd_ranges;
     const int q = (j / per_q) * 8 + xcd, sr = j - (j / per_q) * per_q;
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
     const int ib = rg * per, n_it = max(0, min(n_all, ib + per) - ib);
     const __bf16* const kq = p.keys + (int64_t)l * T * ldkv + hh * d;
     const __bf16* const gq = p.gb + (int64_t)q * T * d;
-    // Tile i's keys and G rows: wave w copies rows 8 w .. 8 w + 7 of each
+    // Tile i's keys and E rows: wave w copies rows 8 w .. 8 w + 7 of each
     // (two copies of 4 rows; lane L fills row 4 c' + L / 16, slot L % 16 with
     // the piece that the swizzle puts there). Rows past T read as zeros.
     auto issue = [&](int i, unsigned char* const kt) {
@@ -589,10 +602,10 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float zz = z[tt][ht][i];
-                    const float qq = normal_tail(fabsf(zz));
-                    hv[tt][i] = gelu_q(zz, qq);
-                    dv[tt][i] = dh[tt][ht][i] * gelu_grad_q(zz, qq);
+                    float hz, gz;
+                    gelu_and_grad(z[tt][ht][i], hz, gz);
+                    hv[tt][i] = hz;
+                    dv[tt][i] = dh[tt][ht][i] * gz;
                     sdz += dv[tt][i];
                 }
             db1a[ht] += sdz;
@@ -687,7 +700,7 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
     }
     if (mode == 0) return;
     if (mode == 1) {
-        const float lr = p.lr;
+        const float lr = p.lr * (2.0f / (float)p.ctx_len);   // the sums are over E = (T / 2) G
         const int np = p.n_parts;
         const float* pw1 = p.pw1 + (int64_t)q * np * H * d;   // [part][u][i]
         const float* pw2 = p.pw2 + (int64_t)q * np * H * d;   // [part][u][o]

@@ -109,12 +109,12 @@ struct FitParams {
     float* w1; float* b1; float* w2; float* b2;   // [P, h, d], [P, h], [P, d, h], [P, d]
     float* losses;                // [P, n_steps + 1] or null
     // workspace, per problem
-    __bf16* gb;                   // [P, T, d]  (2 / T)(v_hat - v)
+    __bf16* gb;                   // [P, T, d]  E = v_hat - v (the loss gradient is (2 / T) E)
     __bf16* w1b; __bf16* w2b; __bf16* w2tb;       // bf16 copies: [P, h, d], [P, d, h], [P, h, d]
-    float* pw1;                   // [P, n_parts, h, d]  partial dW1
-    float* pw2;                   // [P, n_parts, h, d]  partial dW2, stored transposed ([u][o])
-    float* pb1;                   // [P, n_parts, h]     partial db1
-    float* pb2;                   // [P, n_parts, d]     partial db2
+    float* pw1;                   // [P, n_parts, h, d]  partial dZ^T K
+    float* pw2;                   // [P, n_parts, h, d]  partial H^T E ([u][o], dW2 transposed)
+    float* pb1;                   // [P, n_parts, h]     partial sum_t dZ
+    float* pb2;                   // [P, n_parts, d]     partial sum_t E
     float* loss_p;                // [P, n_loss_parts]   sums of squared errors
 };
 hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStream_t s);
