@@ -427,7 +427,8 @@ size_t lowram_pinv_workspace_size(const lowram_pinv_args *args);
  * W1, b1, W2, b2 (W_lin fixed), for every (layer, KV head) at once. Products
  * in bf16 with float32 sums (keys, values, the bf16 copies of the weights and
  * the intermediate activations and gradients are bf16); the parameters are
- * float32 masters updated in place. gelu is the exact erf form.
+ * float32 masters updated in place. gelu is the exact erf form (the kernels
+ * evaluate it, and its derivative, from a fitted normal tail to within 6e-5).
  * losses[l, h, i] is L before step i and losses[l, h, n_steps] after the
  * last step.
  * Shapes (L layers, T tokens, Hkv heads, d = 128, h = mlp_hidden, a multiple
