@@ -13,7 +13,8 @@
 //   xkv_gram_kernel        bf16 MFMA: partial 256 x 256 Gram tiles per token chunk
 //   xkv_gram_reduce_kernel fp64 sum of the chunk partials into symmetric M
 //   xkv_gemm_f64_kernel    fp64 products of the iteration (M X, Y^T Y)
-//   xkv_chol_kernel        Cholesky of the r x r Gram of the block (one workgroup)
+//   xkv_chol_panel_kernel  Cholesky of the r x r Gram, one 64-column panel (one workgroup)
+//   xkv_chol_update_kernel the trailing update after a panel (many workgroups)
 //   xkv_trsm_kernel        X = Y L^-T, rows in parallel (CholeskyQR)
 //   xkv_emit_kernel        bf16 B_l and the transposed basis
 //   xkv_a_kernel           bf16 MFMA: A = C X
@@ -398,66 +399,85 @@ __global__ __launch_bounds__(256) void xkv_sum_splits_kernel(const double* parts
 constexpr int kCholPw = 16;
 
 // In-place lower Cholesky factor of the r x r Gram g (row-major; the strict
-// upper triangle is left as it was), one workgroup: 16-column panels factored
-// in LDS, trailing lower triangle updated in 4 x 4 blocks. A pivot at or below
-// r * 2^-52 * max diag marks the column dead: its L column is zero and the
+// upper triangle is left as it was), blocked by 64-column panels: for panel
+// j0 one workgroup per problem factors columns j0 .. j0+63 (16-column steps
+// in LDS, each step's update kept inside the panel), then
+// xkv_chol_update_kernel subtracts L21 L21^T from the trailing lower
+// triangle on many workgroups. A pivot at or below r * 2^-52 * max diag (of
+// the Gram as given) marks the column dead: its L column is zero and the
 // solve gives that basis column zero (the block is rank deficient there).
-// One workgroup per problem (grid x).
-__global__ __launch_bounds__(1024) void xkv_chol_kernel(double* g, int r, int32_t* dead) {
+constexpr int kCholNb = 64;                 // columns per panel; the rank is a multiple of it
+
+__global__ __launch_bounds__(1024) void xkv_chol_panel_kernel(double* g, int r, int32_t* dead, double* taus, int j0) {
     __shared__ double pan[kXMaxRank * kCholPw];
-    __shared__ double red[16];
+    __shared__ double red[16], pivs[kCholPw], invs[kCholPw];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     g += (int64_t)blockIdx.x * r * r;
     dead += (int64_t)blockIdx.x * r;
-    double dm = 0.0;
-    for (int i = tid; i < r; i += 1024) dm = fmax(dm, g[(int64_t)i * r + i]);
-    for (int off = 32; off > 0; off >>= 1) dm = fmax(dm, __shfl_xor(dm, off, kWave));
-    if (lane == 0) red[w] = dm;
-    __syncthreads();
-    dm = red[0];
-    for (int i = 1; i < 16; ++i) dm = fmax(dm, red[i]);
-    const double tau = (double)r * 0x1p-52 * dm;
+    double tau;
+    if (j0 == 0) {                          // the threshold comes from the diagonal before any update
+        double dm = 0.0;
+        for (int i = tid; i < r; i += 1024) dm = fmax(dm, g[(int64_t)i * r + i]);
+        for (int off = 32; off > 0; off >>= 1) dm = fmax(dm, __shfl_xor(dm, off, kWave));
+        if (lane == 0) red[w] = dm;
+        __syncthreads();
+        dm = red[0];
+        for (int i = 1; i < 16; ++i) dm = fmax(dm, red[i]);
+        tau = (double)r * 0x1p-52 * dm;
+        if (tid == 0) taus[blockIdx.x] = tau;
+    } else {
+        tau = taus[blockIdx.x];
+    }
+    const int jend = j0 + kCholNb;          // r is a multiple of kCholNb
 
-    for (int j0 = 0; j0 < r; j0 += kCholPw) {
-        const int rows = r - j0;
+    for (int c0 = j0; c0 < jend; c0 += kCholPw) {
+        const int rows = r - c0;
         for (int e = tid; e < rows * kCholPw; e += 1024) {
             const int i = e / kCholPw, c = e % kCholPw;
-            pan[e] = g[(int64_t)(j0 + i) * r + j0 + c];
+            pan[e] = g[(int64_t)(c0 + i) * r + c0 + c];
         }
         __syncthreads();
+        // Column c stays unscaled until the end of the 16 steps: every thread
+        // forms the two scaled factors of its update itself (the same rounded
+        // products a scaled column would hold), so a step needs one barrier.
         for (int c = 0; c < kCholPw; ++c) {
             const double d = pan[c * kCholPw + c];
             const bool dd = !(d > tau);
             const double piv = dd ? 0.0 : sqrt(d);
             const double inv = dd ? 0.0 : 1.0 / piv;
-            __syncthreads();
-            for (int i = c + tid; i < rows; i += 1024) pan[i * kCholPw + c] = i == c ? piv : pan[i * kCholPw + c] * inv;
-            if (tid == 0) dead[j0 + c] = dd ? 1 : 0;
-            __syncthreads();
+            if (tid == 0) {
+                dead[c0 + c] = dd ? 1 : 0;
+                pivs[c] = piv;
+                invs[c] = inv;
+            }
             const int nc = kCholPw - 1 - c;
             for (int e = tid; e < (rows - c - 1) * nc; e += 1024) {
                 const int i = c + 1 + e / nc, cc = c + 1 + e % nc;
-                if (cc <= i) pan[i * kCholPw + cc] -= pan[i * kCholPw + c] * pan[cc * kCholPw + c];
+                if (cc <= i) pan[i * kCholPw + cc] -= (pan[i * kCholPw + c] * inv) * (pan[cc * kCholPw + c] * inv);
             }
             __syncthreads();
         }
         for (int e = tid; e < rows * kCholPw; e += 1024) {
             const int i = e / kCholPw, c = e % kCholPw;
-            if (c <= i) g[(int64_t)(j0 + i) * r + j0 + c] = pan[e];
+            if (c <= i) {
+                const double v = i == c ? pivs[c] : pan[e] * invs[c];
+                pan[e] = v;
+                g[(int64_t)(c0 + i) * r + c0 + c] = v;
+            }
         }
-        const int nb = (rows - kCholPw) / 4;
-        const int64_t nblk = (int64_t)nb * (nb + 1) / 2;
-        for (int64_t e = tid; e < nblk; e += 1024) {
-            int bi = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
-            while ((int64_t)bi * (bi + 1) / 2 > e) --bi;
-            while ((int64_t)(bi + 1) * (bi + 2) / 2 <= e) ++bi;
-            const int bk = (int)(e - (int64_t)bi * (bi + 1) / 2);
+        __syncthreads();
+        // The rest of this panel: columns c0+16 .. jend-1, every row below,
+        // in 4 x 4 blocks (block column bk, block row bi >= bk).
+        const int nbi = (rows - kCholPw) / 4, nbk = (jend - c0 - kCholPw) / 4;
+        for (int e = tid; e < nbi * nbk; e += 1024) {
+            const int bi = e / nbk, bk = e % nbk;
+            if (bk > bi) continue;
             const int i0 = kCholPw + bi * 4, k0 = kCholPw + bk * 4;
-            double s[4][4];
+            double sacc[4][4];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) s[a][b] = 0.0;
+                for (int b = 0; b < 4; ++b) sacc[a][b] = 0.0;
 #pragma unroll 4
             for (int c = 0; c < kCholPw; ++c) {
                 double li[4], lk[4];
@@ -469,15 +489,77 @@ __global__ __launch_bounds__(1024) void xkv_chol_kernel(double* g, int r, int32_
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) s[a][b] = fma(li[a], lk[b], s[a][b]);
+                    for (int b = 0; b < 4; ++b) sacc[a][b] = fma(li[a], lk[b], sacc[a][b]);
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    if (k0 + b <= i0 + a) g[(int64_t)(j0 + i0 + a) * r + j0 + k0 + b] -= s[a][b];
+                    if (k0 + b <= i0 + a) g[(int64_t)(c0 + i0 + a) * r + c0 + k0 + b] -= sacc[a][b];
         }
         __syncthreads();
+    }
+}
+
+// Trailing update after panel j0: G[i][k] -= sum_c L[i][c] L[k][c] over the
+// panel's columns c, for i >= k >= j0 + 64. One workgroup per 64 x 64 tile
+// of the lower block triangle (grid x: tile, grid y: problem); each thread a
+// 4 x 4 block, the tile's two row sets of L staged in LDS.
+__global__ __launch_bounds__(256) void xkv_chol_update_kernel(double* g, int r, int j0) {
+    __shared__ double li[kCholNb][kCholNb + 1], lk[kCholNb][kCholNb + 1];
+    const int tid = threadIdx.x;
+    g += (int64_t)blockIdx.y * r * r;
+    const int base = j0 + kCholNb;
+    // tile index -> (ti, tk), tk <= ti
+    const int e = blockIdx.x;
+    int ti = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+    while (ti * (ti + 1) / 2 > e) --ti;
+    while ((ti + 1) * (ti + 2) / 2 <= e) ++ti;
+    const int tk = e - ti * (ti + 1) / 2;
+    const int r0 = base + ti * kCholNb, k0 = base + tk * kCholNb;      // both < r: r - base is a multiple of 64
+    for (int x = tid; x < kCholNb * kCholNb; x += 256) {
+        const int row = x / kCholNb, c = x % kCholNb;
+        li[row][c] = g[(int64_t)(r0 + row) * r + j0 + c];
+        lk[row][c] = g[(int64_t)(k0 + row) * r + j0 + c];
+    }
+    __syncthreads();
+    const int a0 = (tid >> 4) * 4, b0 = (tid & 15) * 4;
+    double sacc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sacc[a][b] = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < kCholNb; ++c) {
+        double x[4], y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[q] = li[a0 + q][c];
+            y[q] = lk[b0 + q][c];
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) sacc[a][b] = fma(x[a], y[b], sacc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = r0 + a0 + a, k = k0 + b0 + b;
+            if (k <= i) g[(int64_t)i * r + k] -= sacc[a][b];
+        }
+}
+
+// Blocked Cholesky of n_prob r x r Grams (r a multiple of 64); taus holds
+// n_prob doubles of scratch.
+static void launch_chol(double* g, int r, int32_t* dead, double* taus, int n_prob, hipStream_t s) {
+    for (int j0 = 0; j0 < r; j0 += kCholNb) {
+        hipLaunchKernelGGL(xkv_chol_panel_kernel, dim3((unsigned)n_prob), dim3(1024), 0, s, g, r, dead, taus, j0);
+        const int nt = (r - j0 - kCholNb) / kCholNb;
+        if (nt > 0)
+            hipLaunchKernelGGL(xkv_chol_update_kernel, dim3((unsigned)(nt * (nt + 1) / 2), (unsigned)n_prob), dim3(256), 0,
+                               s, g, r, j0);
     }
 }
 
@@ -674,7 +756,7 @@ static void gram_tn(const XkvParams& p, const double* y, hipStream_t s) {
 static void cholqr(const XkvParams& p, const double* in, double* out, hipStream_t s) {
     const int r = p.rank;
     gram_tn(p, in, s);
-    hipLaunchKernelGGL(xkv_chol_kernel, dim3((unsigned)p.n_batch), dim3(1024), 0, s, p.g, r, p.dead);
+    launch_chol(p.g, r, p.dead, p.g_parts, p.n_batch, s);     // g_parts is free until the next Gram
     hipLaunchKernelGGL(xkv_trsm_kernel, dim3((unsigned)((r + kTrRows - 1) / kTrRows), (unsigned)p.n_batch), dim3(256), 0,
                        s, (const double*)nullptr, p.rinv, p.g, p.dead, r, r);
     gemm_nn(p, p.n, r, in, (int64_t)p.n * r, r, p.rinv, (int64_t)r * r, out, false, s);
@@ -751,7 +833,7 @@ hipError_t launch_pinv(const PinvParams& p, hipStream_t s) {
     };
     gram(p.wk64, p.g);
     gram(p.wv64, p.bm);
-    hipLaunchKernelGGL(xkv_chol_kernel, dim3((unsigned)P), dim3(1024), 0, s, p.g, d, p.dead);
+    launch_chol(p.g, d, p.dead, p.g_parts, P, s);             // g_parts is free: both Grams are summed
     hipLaunchKernelGGL(xkv_trsm_kernel, dim3((unsigned)((d + kTrRows - 1) / kTrRows), (unsigned)P), dim3(256), 0, s,
                        (const double*)nullptr, p.rinv, p.g, p.dead, d, d);
     auto small = [&](bool ta, const double* a, const double* b, double* out) {
