@@ -593,10 +593,20 @@ __global__ __launch_bounds__(256) void xkv_trsm_kernel(const double* y, double* 
         double v = xs[row][j] - (s0 + s1);
         const double ljj = lj[j];
         const bool dj = dead[j] != 0;
+        // L[j][jb .. jb+15] in registers before the sweep, so no step of it
+        // waits for memory.
+        double lb[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double2 t = *reinterpret_cast<const double2*>(lj + jb + 2 * i);
+            lb[2 * i] = t.x;
+            lb[2 * i + 1] = t.y;
+        }
+#pragma unroll
         for (int cc = 0; cc < 16; ++cc) {
             double xv = (dj || !(ljj != 0.0)) ? 0.0 : v / ljj;
             xv = __shfl(xv, (lane & ~15) | cc, kWave);
-            if (c > cc) v = fma(-lj[jb + cc], xv, v);
+            if (c > cc) v = fma(-lb[cc], xv, v);
             if (c == cc) xs[row][j] = xv;
         }
     }
