@@ -394,6 +394,7 @@ XKV_CONFIGS = {c.name: c for c in (
     XkvConfig("x_small_ragged", 2, 1000, 256, 64, 384, 40.0),
     XkvConfig("x_short", 2, 40, 256, 64, 64, 10.0),          # fewer tokens than the rank
     XkvConfig("x_mid", 4, 8192, 1024, 512, 1536, 200.0),
+    XkvConfig("x_rank_max", 2, 3000, 1024, 1024, 1536, 300.0),  # the largest rank, ragged tokens
     # one group of four Llama-3.1-8B layers (8 KV heads x 128) at 131072 tokens, r = 512
     XkvConfig("x_llama_131k", 4, 131072, 1024, 512, 1536, 200.0),
 )}

@@ -103,6 +103,14 @@ def test_mid_four_layers():
     _check(xc, x, out, optimum=True)
 
 
+def test_max_rank():
+    """r = 1024, the largest supported rank (sixteen 64-column Cholesky
+    panels with a trailing update after each), on a ragged token count."""
+    xc = synth.XKV_CONFIGS["x_rank_max"]
+    x, out = _run(xc)
+    _check(xc, x, out, optimum=True)
+
+
 def test_full_shape():
     xc = synth.XKV_CONFIGS["x_llama_131k"]                # 4 Llama-3.1-8B layers, T = 131072, r = 512
     x, out = _run(xc)
