@@ -430,7 +430,8 @@ size_t lowram_pinv_workspace_size(const lowram_pinv_args *args);
  * float32 masters updated in place. gelu is the exact erf form (the kernels
  * evaluate it, and its derivative, from a fitted normal tail to within 6e-5).
  * losses[l, h, i] is L before step i and losses[l, h, n_steps] after the
- * last step.
+ * last step; with losses NULL no loss is written and the loss-only forward
+ * pass after the last step is skipped (the parameters are the same).
  * Shapes (L layers, T tokens, Hkv heads, d = 128, h = mlp_hidden, a multiple
  * of 128 in [128, 1024]): keys [L, T, Hkv*d] bf16 (e.g. A B_l), v [L, T, Hkv,
  * d] bf16, w_lin [L, Hkv, d, d] bf16 output-major; w1 [L, Hkv, h, d], b1

@@ -652,12 +652,13 @@ def fit_launch(args, stream=None):
         raise LowramError(rc, last_error())
 
 
-def fit_predictor(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, *, workspace=None, stream=None):
+def fit_predictor(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, *, want_losses=True, workspace=None, stream=None):
     """n_steps of gradient descent on the nonlinear branch of every (layer, KV
     head) predictor; updates w1, b1, w2, b2 in place and returns the losses
-    [L, Hkv, n_steps + 1]."""
+    [L, Hkv, n_steps + 1] (None with want_losses=False, which also skips the
+    loss-only pass after the last step)."""
     Lr, T, hkv, d = v.shape
-    losses = torch.empty(Lr, hkv, n_steps + 1, dtype=torch.float32, device=v.device)
+    losses = torch.empty(Lr, hkv, n_steps + 1, dtype=torch.float32, device=v.device) if want_losses else None
     args = make_fit_args(keys, v, w_lin, w1, b1, w2, b2, n_steps, lr, losses=losses)
     L = lib()
     _run(L.lowram_fit_predictor, args, L.lowram_fit_workspace_size, v.device, workspace, stream)

@@ -759,10 +759,12 @@ hipError_t launch_fit(const FitParams& p, void* ev_begin, void* ev_end, hipStrea
         hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, it, 1);
     }
     if (ev_end && (e = hipEventRecord(static_cast<hipEvent_t>(ev_end), s)) != hipSuccess) return e;
-    if (resident && wide) hipLaunchKernelGGL((fit_fwd_kernel<false, 8>), gf, dim3(kFitThreads), 0, s, p);
-    else if (resident) hipLaunchKernelGGL((fit_fwd_kernel<false, 4>), gf, dim3(kFitThreads), 0, s, p);
-    else hipLaunchKernelGGL((fit_fwd_tiled_kernel<false>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
-    hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, p.n_steps, 0);
+    if (p.losses) {     // the loss after the last step: a forward pass that only sums squared errors
+        if (resident && wide) hipLaunchKernelGGL((fit_fwd_kernel<false, 8>), gf, dim3(kFitThreads), 0, s, p);
+        else if (resident) hipLaunchKernelGGL((fit_fwd_kernel<false, 4>), gf, dim3(kFitThreads), 0, s, p);
+        else hipLaunchKernelGGL((fit_fwd_tiled_kernel<false>), gt, dim3(kFitThreads), 0, s, p, per_xcd);
+        hipLaunchKernelGGL(fit_update_kernel, dim3(P, kUpdSlices), dim3(256), 0, s, p, p.n_steps, 0);
+    }
     return hipGetLastError();
 }
 

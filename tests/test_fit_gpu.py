@@ -101,6 +101,21 @@ def test_mid_sampled():
         print(f"f_mid ({l},{h}): update rel err {rel:.2e}, losses {ls}", flush=True)
 
 
+def test_without_losses_same_parameters():
+    """With no loss buffer the loss-only pass after the last step is skipped;
+    the parameters are bit-identical to a run that reports the losses."""
+    fc = synth.FIT_CONFIGS["f_small_ragged"]
+    xa = synth.gen_fit_inputs(fc, "cuda")
+    xb = {n: t.clone() for n, t in xa.items()}
+    la = L.fit_predictor(xa["keys"], xa["v"], xa["w_lin"], xa["w1"], xa["b1"], xa["w2"], xa["b2"], fc.n_steps, fc.lr)
+    lb = L.fit_predictor(xb["keys"], xb["v"], xb["w_lin"], xb["w1"], xb["b1"], xb["w2"], xb["b2"], fc.n_steps, fc.lr,
+                         want_losses=False)
+    torch.cuda.synchronize()
+    assert lb is None and la.shape[-1] == fc.n_steps + 1
+    for n in ("w1", "b1", "w2", "b2"):
+        assert torch.equal(xa[n], xb[n]), n
+
+
 def test_zero_steps_reports_the_start_loss():
     fc = synth.FIT_CONFIGS["f_small_ragged"]
     x = synth.gen_fit_inputs(fc, "cuda")
