@@ -336,46 +336,59 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
         return *reinterpret_cast<const u32x2*>(sv_w + r * 256 + ((pc ^ (r & 15)) << 4) + 8 * (g4 & 1));
     };
     if (MODE == 0) {
-        // d^2 in binary64 by every lane for its 32 values, into this wave's
-        // 16 KB LDS tile [16 tokens][128] (32-byte column c = 4ot + g of row
-        // l16 stored at c ^ l16), then lanes 0..15 add their token's 128
-        // terms in index order.
+        // d^2 in binary64, in four 32-feature chunks: every lane forms the
+        // squares of its 32 values of the chunk into this wave's 16 KB LDS
+        // tile [64 tokens][32] (16-byte pair cp of row r at slot cp ^ (r & 15),
+        // so a 16-lane group's row reads hit distinct banks); then lane r adds
+        // token r's 32 terms in index order, its sum running across the
+        // chunks. All 64 lanes carry a token's chain at once.
         unsigned char* const et = w == 0 ? buf0 : (w == 1 ? buf1 : (w == 2 ? buf2 : buf3));
+        if (p.v_hat != nullptr) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int t = __shfl(my_tok, tt * 16 + l16, kWave);
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = __shfl(my_tok, tt * 16 + l16, kWave);
+                if (t >= 0) {
 #pragma unroll
-            for (int ot = 0; ot < 8; ++ot) {
-                const u32x2 vv = v4(tt * 16 + l16, ot);
-                double d2[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t word = vv[i >> 1];
-                    const float vf = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
-                    const double dl = (double)vf - (double)vacc[ot][tt][i];
-                    d2[i] = dl * dl;
-                }
-                double* dst = reinterpret_cast<double*>(et + l16 * 1024 + (((ot * 4 + g4) ^ l16) * 32));
-                dst[0] = d2[0]; dst[1] = d2[1]; dst[2] = d2[2]; dst[3] = d2[3];
-                if (p.v_hat != nullptr && t >= 0) {
-                    float* vh = p.v_hat + (((int64_t)l * T + t) * p.n_kv + h) * kHeadDim + ot * 16 + 4 * g4;
-                    *reinterpret_cast<f32x4*>(vh) = vacc[ot][tt];
+                    for (int ot = 0; ot < 8; ++ot) {
+                        float* vh = p.v_hat + (((int64_t)l * T + t) * p.n_kv + h) * kHeadDim + ot * 16 + 4 * g4;
+                        *reinterpret_cast<f32x4*>(vh) = vacc[ot][tt];
+                    }
                 }
             }
-            wait_lgkmcnt0();
-            if (g4 == 0 && t >= 0) {
-                double e = 0.0;
-                for (int c = 0; c < 32; ++c) {
-                    const double* src = reinterpret_cast<const double*>(et + l16 * 1024 + ((c ^ l16) * 32));
-                    e = e + src[0];
-                    e = e + src[1];
-                    e = e + src[2];
-                    e = e + src[3];
-                }
-                p.err[lh * T + t] = e;
-            }
-            wait_lgkmcnt0();
         }
+        double e = 0.0;
+#pragma unroll
+        for (int fc = 0; fc < 4; ++fc) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int r = tt * 16 + l16;
+#pragma unroll
+                for (int oo = 0; oo < 2; ++oo) {
+                    const int ot = 2 * fc + oo;
+                    const u32x2 vv = v4(r, ot);
+                    double d2[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t word = vv[i >> 1];
+                        const float vf = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+                        const double dl = (double)vf - (double)vacc[ot][tt][i];
+                        d2[i] = dl * dl;
+                    }
+                    const int cp = 8 * oo + 2 * g4;      // pairs of columns 16 oo + 4 g4 .. + 3
+                    *reinterpret_cast<double2*>(et + r * 256 + ((cp ^ (r & 15)) << 4)) = double2{d2[0], d2[1]};
+                    *reinterpret_cast<double2*>(et + r * 256 + (((cp + 1) ^ (r & 15)) << 4)) = double2{d2[2], d2[3]};
+                }
+            }
+            wait_lgkmcnt0();                          // the wave's LDS operations complete in order
+#pragma unroll
+            for (int cp = 0; cp < 16; ++cp) {
+                const double2 pr = *reinterpret_cast<const double2*>(et + lane * 256 + ((cp ^ (lane & 15)) << 4));
+                e = e + pr.x;
+                e = e + pr.y;
+            }
+            wait_lgkmcnt0();                          // before the next chunk overwrites the tile
+        }
+        if (my_tok >= 0) p.err[lh * T + my_tok] = e;
     } else {
         // R = V - V_hat in binary64, encoded like the ranking's gather.
 #pragma unroll
