@@ -678,11 +678,16 @@ __global__ __launch_bounds__(kFitThreads, 1) void fit_bwd_kernel(FitParams p) {
 // Grid (problem, slice of kUpdSlices). mode 0: loss only (slot `step`, slice
 // 0); mode 1: gradient step `step`: each weight's partials summed in a fixed
 // order by the one thread that owns it, which updates the fp32 master and
-// writes its bf16 copies; mode 2: bf16 copies only. Threads walk the weights
-// along the partials' contiguous axis.
+// writes its bf16 copies; mode 2: bf16 copies only. W1, b1 and b2 are walked
+// along the partials' contiguous axis; W2 ([o][u]) goes in tiles of 32 units
+// x 128 outputs through LDS, so that its partials ([part][u][o]) and its
+// transposed copy ([u][o]) are walked along o and W2 and its copy along u.
 constexpr int kUpdSlices = 8;
+constexpr int kUt = 32;                          // hidden units per W2 tile
 
 __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, int mode) {
+    __shared__ float gt[kUt][kHeadDim + 1];      // a tile's W2 gradient, [u][o]
+    __shared__ uint16_t nt[kUt][kHeadDim + 2];   // its bf16 values, [u][o]
     const int q = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
     const int d = kHeadDim, H = p.hidden;
     const int e0 = slice * 256 + tid, es = 256 * kUpdSlices;
@@ -699,26 +704,16 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
         p.losses[(int64_t)q * (p.n_steps + 1) + step] = (float)(s / (double)p.ctx_len);
     }
     if (mode == 0) return;
+    const float lr = p.lr * (2.0f / (float)p.ctx_len);   // the sums are over E = (T / 2) G
+    const int np = p.n_parts;
     if (mode == 1) {
-        const float lr = p.lr * (2.0f / (float)p.ctx_len);   // the sums are over E = (T / 2) G
-        const int np = p.n_parts;
         const float* pw1 = p.pw1 + (int64_t)q * np * H * d;   // [part][u][i]
-        const float* pw2 = p.pw2 + (int64_t)q * np * H * d;   // [part][u][o]
         for (int e = e0; e < H * d; e += es) {
-            float g1 = 0.f, g2 = 0.f;
-            for (int c = 0; c < np; ++c) {
-                g1 += pw1[(int64_t)c * H * d + e];
-                g2 += pw2[(int64_t)c * H * d + e];
-            }
+            float g1 = 0.f;
+            for (int c = 0; c < np; ++c) g1 += pw1[(int64_t)c * H * d + e];
             const float x1 = w1[e] - lr * g1;         // w1[u][i], e = u d + i
             w1[e] = x1;
             w1b[e] = f32_to_bf16_bits(x1);
-            const int u = e / d, o = e - u * d;       // w2[o][u]
-            const float x2 = w2[(int64_t)o * H + u] - lr * g2;
-            w2[(int64_t)o * H + u] = x2;
-            const uint16_t v = f32_to_bf16_bits(x2);
-            w2b[(int64_t)o * H + u] = v;
-            w2tb[e] = v;                               // w2tb[u][o]
         }
         for (int u = e0; u < H; u += es) {
             float g = 0.f;
@@ -730,14 +725,42 @@ __global__ __launch_bounds__(256) void fit_update_kernel(FitParams p, int step, 
             for (int c = 0; c < np; ++c) g += p.pb2[((int64_t)q * np + c) * d + o];
             b2[o] -= lr * g;
         }
-        return;
+    } else {
+        for (int e = e0; e < H * d; e += es) w1b[e] = f32_to_bf16_bits(w1[e]);
     }
-    for (int e = e0; e < H * d; e += es) w1b[e] = f32_to_bf16_bits(w1[e]);
-    for (int e = e0; e < d * H; e += es) {
-        const int o = e / H, u = e - o * H;
-        const uint16_t v = f32_to_bf16_bits(w2[e]);
-        w2b[e] = v;
-        w2tb[(int64_t)u * d + o] = v;
+    const float* pw2 = p.pw2 + (int64_t)q * np * H * d;       // [part][u][o]
+    constexpr int kPer = kUt * kHeadDim / 256;                 // tile elements per thread
+    for (int u0 = slice * kUt; u0 < H; u0 += kUt * kUpdSlices) {
+        if (mode == 1) {
+#pragma unroll 4
+            for (int k = 0; k < kPer; ++k) {
+                const int idx = tid + 256 * k, ul = idx / kHeadDim, o = idx % kHeadDim;
+                float g2 = 0.f;
+                for (int c = 0; c < np; ++c) g2 += pw2[(int64_t)c * H * d + (int64_t)(u0 + ul) * d + o];
+                gt[ul][o] = g2;
+            }
+            __syncthreads();
+        }
+#pragma unroll 4
+        for (int k = 0; k < kPer; ++k) {
+            const int idx = tid + 256 * k, o = idx / kUt, ul = idx % kUt;
+            const int64_t wi = (int64_t)o * H + u0 + ul;          // w2[o][u]
+            float x2 = w2[wi];
+            if (mode == 1) {
+                x2 = x2 - lr * gt[ul][o];
+                w2[wi] = x2;
+            }
+            const uint16_t v = f32_to_bf16_bits(x2);
+            w2b[wi] = v;
+            nt[ul][o] = v;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < kPer; ++k) {
+            const int idx = tid + 256 * k, ul = idx / kHeadDim, o = idx % kHeadDim;
+            w2tb[(int64_t)(u0 + ul) * d + o] = nt[ul][o];         // w2tb[u][o]
+        }
+        __syncthreads();
     }
 }
 
