@@ -240,20 +240,35 @@ __global__ __launch_bounds__(kGramThreads, 1) void xkv_gram_kernel(XkvParams p) 
 }
 
 // M[256 J + a][256 I + b] = sum over chunks of P (binary64, chunk order),
-// mirrored off the diagonal. Grid (256 rows a, n_upper tiles, problems), 256 threads (b).
+// mirrored off the diagonal. Grid (16 groups of 16 rows a, n_upper tiles,
+// problems), 256 threads (b).
+constexpr int kRedRows = 16;                    // tile rows per reduction block
+
 __global__ __launch_bounds__(256) void xkv_gram_reduce_kernel(XkvParams p) {
-    const int tile = blockIdx.y, a = blockIdx.x, b = threadIdx.x;
+    // Block: rows a0 .. a0+15 of one upper tile, thread b its column. The
+    // sums go to M directly (coalesced along b) and, for an off-diagonal tile,
+    // to the mirrored block through LDS, so that each thread then writes 16
+    // consecutive doubles of one mirrored row.
+    __shared__ double sub[kRedRows][kXT + 1];
+    const int tile = blockIdx.y, a0 = blockIdx.x * kRedRows, b = threadIdx.x;
     const int64_t prob = blockIdx.z;
     int ti, tj;
     xkv_tile(tile, p.nt, ti, tj);
-    const float* src = p.partials + (prob * p.n_chunks * p.n_upper + tile) * (kXT * kXT) + a * kXT + b;
+    const float* src = p.partials + (prob * p.n_chunks * p.n_upper + tile) * (kXT * kXT) + a0 * kXT + b;
     double* const m = p.m + prob * p.n * (int64_t)p.n;
     const int64_t chunk_stride = (int64_t)p.n_upper * (kXT * kXT);
-    double v = 0.0;
-    for (int c = 0; c < p.n_chunks; ++c) v += (double)src[c * chunk_stride];
-    const int64_t row = (int64_t)tj * kXT + a, col = (int64_t)ti * kXT + b;
-    m[row * p.n + col] = v;
-    if (ti != tj) m[col * p.n + row] = v;
+#pragma unroll 4
+    for (int r = 0; r < kRedRows; ++r) {
+        double v = 0.0;
+        for (int c = 0; c < p.n_chunks; ++c) v += (double)src[c * chunk_stride + r * kXT];
+        m[((int64_t)tj * kXT + a0 + r) * p.n + (int64_t)ti * kXT + b] = v;
+        sub[r][b] = v;
+    }
+    if (ti == tj) return;                          // the whole block takes this branch
+    __syncthreads();
+    double* const dst = m + ((int64_t)ti * kXT + b) * p.n + (int64_t)tj * kXT + a0;
+#pragma unroll
+    for (int r = 0; r < kRedRows; ++r) dst[r] = sub[r][b];
 }
 
 // ------------------------------------------------------- fp64 products
@@ -776,7 +791,7 @@ static void cholqr(const XkvParams& p, const double* in, double* out, hipStream_
 // steps take one CholeskyQR pass (only their span feeds the next product),
 // the last one two (the second restores orthogonality to rounding level).
 hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(xkv_gram_reduce_kernel, dim3(kXT, (unsigned)p.n_upper, (unsigned)p.n_batch), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(xkv_gram_reduce_kernel, dim3(kXT / kRedRows, (unsigned)p.n_upper, (unsigned)p.n_batch), dim3(256), 0, s, p);
     const int64_t nr = (int64_t)p.n * p.rank;
     double* buf[2] = {p.x, p.y};
     const double* in = p.omega;
