@@ -96,9 +96,9 @@ __device__ __forceinline__ void xkv_tile_blocked(int k, int nt, int& ti, int& tj
 //
 // Four waves, one per SIMD, each owning a 128 x 128 quarter of the tile (256
 // accumulator registers). The keys come into LDS untransposed, by direct
-// copies three 32-token steps ahead in a ring of four stages: per stage and
-// operand 32 token rows x 256 columns (512-byte rows of 32 pieces of 16
-// bytes, piece p of row t in slot p ^ gsw(t)). The MFMA fragments are read
+// copies four 32-token steps ahead in a ring of five stages (the whole 160 KB
+// of LDS): per stage and operand 32 token rows x 256 columns (512-byte rows of
+// 32 pieces of 16 bytes, piece p of row t in slot p ^ gsw(t)). The MFMA fragments are read
 // with the transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
 // group, lanes 4r .. 4r+3 name row r's 16 consecutive columns and lane j gets
 // column j of those 4 rows, i.e. 4 consecutive tokens of one column; two such
@@ -120,12 +120,11 @@ __device__ __forceinline__ int gsw(int t) { return 2 * ((t & 3) | (((t >> 3) & 3
 __device__ __forceinline__ bf16x8 tr_frag(const unsigned char* op, uint32_t off) {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(op + off + 4 * kGRowB));
-    u32x4 v;
-    v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-    v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-    v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-    v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-    return as_bf16x8(v);
+    // Concatenated as they are: any repacking would be vector instructions
+    // that wait on both reads.
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // 64 MFMAs of one 32-token step of the wave's 128 x 128 block.
@@ -154,6 +153,7 @@ __global__ __launch_bounds__(kGramThreads, 1) void xkv_gram_kernel(XkvParams p) 
     __shared__ __attribute__((aligned(16))) unsigned char st1[kGStage];
     __shared__ __attribute__((aligned(16))) unsigned char st2[kGStage];
     __shared__ __attribute__((aligned(16))) unsigned char st3[kGStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st4[kGStage];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Blocks go round-robin over the 8 XCDs; XCD x takes the contiguous run
     // of positions x * per .. x * per + per - 1, in an order that walks the
@@ -214,21 +214,24 @@ __global__ __launch_bounds__(kGramThreads, 1) void xkv_gram_kernel(XkvParams p) 
     dma(0, st0);
     if (n_steps > 1) dma(1, st1);
     if (n_steps > 2) dma(2, st2);
-    // Step s: wait for this wave's copies of s (those of s+1 and s+2 may stay
-    // in flight, 8 per step), meet, start s+3 into the stage s-1 used, multiply.
+    if (n_steps > 3) dma(3, st3);
+    // Step s: wait for this wave's copies of s (those of s+1 .. s+3 may stay
+    // in flight, 8 per step), meet, start s+4 into the stage s-1 used, multiply.
     auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-        if (s + 2 < n_steps) wait_vmcnt<16>();
+        if (s + 3 < n_steps) wait_vmcnt<24>();
+        else if (s + 2 < n_steps) wait_vmcnt<16>();
         else if (s + 1 < n_steps) wait_vmcnt<8>();
         else wait_vmcnt<0>();
         barrier_lds();
-        if (s + 3 < n_steps) dma(s + 3, nxt);
+        if (s + 4 < n_steps) dma(s + 4, nxt);
         gram_step(cur, acc, wi, wj, lane_off, lane_sw);
     };
-    for (int s = 0; s < n_steps; s += 4) {
-        step(s, st0, st3);
+    for (int s = 0; s < n_steps; s += 5) {
+        step(s, st0, st4);
         if (s + 1 < n_steps) step(s + 1, st1, st0);
         if (s + 2 < n_steps) step(s + 2, st2, st1);
         if (s + 3 < n_steps) step(s + 3, st3, st2);
+        if (s + 4 < n_steps) step(s + 4, st4, st3);
     }
     float* out = p.partials + ((prob * p.n_chunks + chunk) * p.n_upper + tile) * (kXT * kXT);
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -662,7 +665,14 @@ __global__ __launch_bounds__(kXThreads, 1) void xkv_a_kernel(XkvParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char st1[2 * kXStage];
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_ct = (p.rank + kXT - 1) / kXT;
-    const int ct = blockIdx.x % n_ct, tt = blockIdx.x / n_ct;
+    // Blocks go round-robin over the 8 XCDs. XCD x takes token tiles x, x + 8,
+    // x + 16, ..., each with all its column tiles in consecutive positions, so
+    // the workgroups that read one token tile's keys share them in one L2.
+    // The grid is padded to a multiple of 8 token tiles; padding blocks exit.
+    const int n_tt = (p.ctx_len + kXT - 1) / kXT;
+    const int pos = blockIdx.x >> 3;
+    const int ct = pos % n_ct, tt = (pos / n_ct) * 8 + (blockIdx.x & 7);
+    if (tt >= n_tt) return;
     const int c0 = ct * kXT, t0 = tt * kXT;
     const int n_steps = p.n / kXK;
     const int64_t prob = blockIdx.y;
@@ -812,7 +822,7 @@ hipError_t launch_xkv_factor(const XkvParams& p, hipStream_t s) {
     hipLaunchKernelGGL(xkv_emit_kernel, dim3((unsigned)(p.rank / 64), (unsigned)(p.n / 64), (unsigned)p.n_batch),
                        dim3(256), 0, s, p, (const double*)buf[cur]);
     const int n_ct = (p.rank + kXT - 1) / kXT, n_tt = (p.ctx_len + kXT - 1) / kXT;
-    hipLaunchKernelGGL(xkv_a_kernel, dim3((unsigned)(n_ct * n_tt), (unsigned)p.n_batch), dim3(kXThreads), 0, s, p);
+    hipLaunchKernelGGL(xkv_a_kernel, dim3((unsigned)(n_ct * ((n_tt + 7) / 8) * 8), (unsigned)p.n_batch), dim3(kXThreads), 0, s, p);
     return hipGetLastError();
 }
 
