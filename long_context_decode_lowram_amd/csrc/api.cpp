@@ -72,7 +72,7 @@ int plan_decode(const lowram_decode_args* a, DecodePlan* pl) {
     DecodeParams sm{};
     sm.n_split = pl->n_split; sm.win_len = a->win_len; sm.hidden = a->mlp_hidden;
     const size_t smem = combine_smem_bytes(sm);
-    if (smem > 65536) return fail(LOWRAM_ERR_UNSUPPORTED, "too many splits plus window tokens for the combine");
+    if (smem > 65536) return fail(LOWRAM_ERR_UNSUPPORTED, "mlp_hidden too wide for the combine");
 
     const size_t B = a->batch;
     pl->off_list = 0;

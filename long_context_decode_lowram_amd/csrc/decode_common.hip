@@ -130,17 +130,6 @@ hipError_t launch_window_append(const WindowParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    v = is_max ? wave_max(v) : wave_sum(v);
-    __syncthreads();
-    if (lane == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-    return r;
-}
-
 // One workgroup per (query head j, sequence b). A partial record is
 // (m, l, O[0:hidden], O[hidden:hidden+d]) where m is the running max of the
 // scaled scores, l = sum exp(s - m) over its tokens, O[0:hidden] the
@@ -150,8 +139,60 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 // after rescaling every record to the common max; W2 and b2 are linear and
 // the weights p sum to L, so applying them after the weighted sum gives the
 // predictor's value for every token exactly (up to rounding).
+//
+// The kernel is a short chain of dependent steps, so every load it needs is
+// issued at the start, in one round trip: this thread's W2 pieces, the window
+// rows of its wave's first window batch, then the records. Each wave folds
+// its records and its window tokens into running (max, weight sum, sums)
+// pairs, the window tokens as one more record whose hidden part is zero (their
+// values are exact), and two barriers merge the eight waves.
 constexpr int kCombWaves = 8;
 constexpr int kCombThreads = kCombWaves * 64;
+constexpr int kCombWin = 16;          // window tokens per wave per batch
+
+// Features 2 lane and 2 lane + 1 of a row, as stored (bf16 pair in .x, or two floats).
+template <int ACT> __device__ __forceinline__ uint2 ld_pair_raw(const void* base, int64_t elem) {
+    if constexpr (ACT == DT_F32) return *reinterpret_cast<const uint2*>(static_cast<const float*>(base) + elem);
+    else return make_uint2(*reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + elem), 0u);
+}
+template <int ACT> __device__ __forceinline__ float2 pair_f(uint2 r) {
+    if constexpr (ACT == DT_F32) return make_float2(__uint_as_float(r.x), __uint_as_float(r.y));
+    else return make_float2(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u));
+}
+// Values of lane ^ 1 and lane ^ 2 (DPP quad permutations, no LDS traffic).
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+// One step of a transposing butterfly: a lane carries 2n partial sums and
+// keeps the half that bit `o` of its lane index selects, adding the partner's
+// (lane ^ o) partial of the same values; the partner keeps the other half.
+template <int N>
+__device__ __forceinline__ void fold_half(const float (&in)[2 * N], float (&out)[N], int lane, int o) {
+    const bool hi = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float keep = hi ? in[N + i] : in[i], send = hi ? in[i] : in[N + i];
+        out[i] = keep + __shfl_xor(send, o, kWave);
+    }
+}
+
+// sum_e oc[e] w[e] over the elements of one 16-byte W2 piece.
+template <int ACT> __device__ __forceinline__ float dot_piece(const uint4 u, const float* oc) {
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+    float y = 0.f;
+    if constexpr (ACT == DT_F32) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y += oc[k] * __uint_as_float(wd[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            y += oc[2 * k] * __uint_as_float(wd[k] << 16) + oc[2 * k + 1] * __uint_as_float(wd[k] & 0xffff0000u);
+    }
+    return y;
+}
 
 template <int ACT>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
@@ -159,25 +200,94 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     const int lane = tid & 63, wv = tid >> 6;
     const int h = j / p.group, H = p.hidden, S = p.part_stride, nf = H + kHeadDim;
     const int nsplit = min(p.n_split, (attended_count(p, b) + p.blocks_per_split - 1) / p.blocks_per_split);
-    const int nw = window_len(p);         // at most p.win_len, which sizes sw
+    const int nw = window_len(p);
     const float* P = p.partials + ((int64_t)b * p.n_q + j) * p.n_split * (int64_t)S;
     extern __shared__ float sm[];
-    float* sw = sm;                       // [win_len]
-    float* oc = sw + p.win_len;           // [H + 128]
-    float* red = oc + nf + kHeadDim;      // [8 + 3 * 128]: block reductions, then the W2 quarter sums
-    float* part = red + 8 + 3 * kHeadDim; // [8][H + 128]: the waves' record sums
-    float* wml = part + kCombWaves * nf;  // [8][2]: each wave's max and weight sum
+    float* part = sm;                              // [8][nf]: the waves' record sums
+    float* wpart = part + kCombWaves * nf;         // [8][d]: the waves' window value sums
+    float* oc = wpart + kCombWaves * kHeadDim;     // [nf]: the merged sums
+    float* wml = oc + nf;                          // [8][4]: record max and weight sum, window max and weight sum
 
-    // out[f] takes four threads, a quarter of the W2 row each; the first 256
-    // bytes of that quarter are loaded now, before anything they wait on.
-    const int f_out = tid & (kHeadDim - 1), quarter = tid >> 7;
-    const int64_t w2row = (((int64_t)b * p.n_kv + h) * kHeadDim + f_out) * H;
-    const int i0 = quarter * (H / 4), n_c = (H / 4) / 8;       // 16-byte pieces of the quarter
-    const bool w2_vec = ACT == DT_BF16 && H % 32 == 0;
-    const uint4* w2v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.w2) + w2row + i0);
+    // W2 rows: out[f] takes the 32 lanes of one half-wave, so every load reads
+    // whole rows (coalesced). Pass k covers the rows f = 16 k + tid / 32; lane
+    // l32 of the half takes the 16-byte pieces l32 + 32 m of its row. The
+    // pieces of m = 0 and b2 are loaded now.
+    constexpr int kEpp = ACT == DT_F32 ? 4 : 8;    // W2 elements per 16-byte piece
+    const int n_pc = H / kEpp;                     // pieces per row (H is a multiple of 16)
+    const int l32 = tid & 31, g16 = tid >> 5;
+    const int64_t head = (int64_t)b * p.n_kv + h;
+    const uint4* w2g = reinterpret_cast<const uint4*>(static_cast<const char*>(p.w2) +
+                                                      head * kHeadDim * H * (int64_t)(ACT == DT_F32 ? 4 : 2));
     uint4 w2pre[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) w2pre[c] = (w2_vec && c < n_c) ? w2v[c] : make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < 8; ++k) {
+        const int f = 16 * k + g16;
+        w2pre[k] = l32 < n_pc ? w2g[(int64_t)f * n_pc + l32] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // The row sums end in lane group k_own of the half (see below); b2 of that row.
+    const int k_own = 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
+    const int f_own = 16 * k_own + g16;
+    const float b2_own = p.b2 ? ld<ACT>(p.b2, head * kHeadDim + f_own) : 0.f;
+
+    // Window tokens: batch u0 gives wave wv the tokens u0 + 16 wv + i; lane
+    // holds features 2 lane and 2 lane + 1 of the query and of each row.
+    const int64_t q_row = ((int64_t)b * p.n_q + j) * kHeadDim;
+    const float2 qq = pair_f<ACT>(ld_pair_raw<ACT>(p.q, q_row + 2 * lane));
+    auto win_load = [&](int u0, uint2 (&kr)[kCombWin], uint2 (&vr)[kCombWin]) {
+#pragma unroll
+        for (int i = 0; i < kCombWin; ++i) {
+            const int u = u0 + kCombWin * wv + i;
+            const int64_t row = (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + 2 * lane;
+            kr[i] = u < nw ? ld_pair_raw<ACT>(p.win_k, row) : make_uint2(0u, 0u);
+            vr[i] = u < nw ? ld_pair_raw<ACT>(p.win_v, row) : make_uint2(0u, 0u);
+        }
+    };
+    float wm = -INFINITY, wl = 0.f, wa0 = 0.f, wa1 = 0.f;   // this wave's window max, weight sum, value sums
+    auto win_use = [&](int u0, const uint2 (&kr)[kCombWin], const uint2 (&vr)[kCombWin]) {
+        if (u0 + kCombWin * wv >= nw) return;       // no token of this batch is the wave's
+        // q . k of the wave's 16 tokens: the lanes' products, then a
+        // transposing butterfly (17 shuffles in place of 16 wave sums); lane
+        // ends with the sum of token 8 b5 + 4 b4 + 2 b3 + b2 (bits of its
+        // index), which lane 32 b5 + 16 b4 + 8 b3 + 4 b2 then hands out.
+        float v16[16], v8[8], v4[4], v2[2], v1[1];
+#pragma unroll
+        for (int i = 0; i < kCombWin; ++i) {
+            const float2 kk = pair_f<ACT>(kr[i]);
+            v16[i] = qq.x * kk.x + qq.y * kk.y;
+        }
+        fold_half<8>(v16, v8, lane, 32);
+        fold_half<4>(v8, v4, lane, 16);
+        fold_half<2>(v4, v2, lane, 8);
+        fold_half<1>(v2, v1, lane, 4);
+        float tsum = v1[0] + quad_xor2(v1[0]);
+        tsum += quad_xor1(tsum);
+        float sc[kCombWin];
+        float mnew = wm;
+#pragma unroll
+        for (int i = 0; i < kCombWin; ++i) {
+            const int src = 32 * ((i >> 3) & 1) + 16 * ((i >> 2) & 1) + 8 * ((i >> 1) & 1) + 4 * (i & 1);
+            sc[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tsum), src)) * p.scale;
+            if (u0 + kCombWin * wv + i < nw) mnew = fmaxf(mnew, sc[i]);
+        }
+        if (mnew == -INFINITY) return;             // no token of this batch is the wave's
+        const float r = wm == -INFINITY ? 0.f : expf(wm - mnew);
+        wl *= r;
+        wa0 *= r;
+        wa1 *= r;
+#pragma unroll
+        for (int i = 0; i < kCombWin; ++i) {
+            if (u0 + kCombWin * wv + i < nw) {
+                const float e = expf(sc[i] - mnew);
+                const float2 vv = pair_f<ACT>(vr[i]);
+                wl += e;
+                wa0 += e * vv.x;
+                wa1 += e * vv.y;
+            }
+        }
+        wm = mnew;
+    };
+    uint2 kr[kCombWin], vr[kCombWin];
+    win_load(0, kr, vr);
 
     // Records: wave wv merges the splits wv, wv+8, ... eight at a time, with
     // a running max (every sum is rescaled to it as it grows), so the loads of
@@ -224,128 +334,97 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
             if (fi < nf) part[wv * nf + fi] = acc[i];
         }
         if (lane == 0 && f0 == 0) {
-            wml[2 * wv] = mrun;
-            wml[2 * wv + 1] = lrun;
+            wml[4 * wv] = mrun;
+            wml[4 * wv + 1] = lrun;
         }
     }
 
-    // Window tokens: exact keys and values, scored here. Wave wv scores the
-    // tokens wv, wv + 8, ..., two at a time: lane l holds features 2l and
-    // 2l + 1 of the query and reads the same two of each key row (the wave
-    // reads a row's 128 features in one coalesced pass), then the wave sums.
-    const int64_t q_row = ((int64_t)b * p.n_q + j) * kHeadDim;
-    const float q0 = ld<ACT>(p.q, q_row + 2 * lane), q1 = ld<ACT>(p.q, q_row + 2 * lane + 1);
-    // Eight tokens per batch: their sixteen loads are issued before any sum,
-    // so the batch waits for memory once.
-    float mx = -INFINITY;
-    constexpr int kWinBatch = 8;
-    for (int u0 = wv; u0 < nw; u0 += kWinBatch * kCombWaves) {
-        float k0[kWinBatch], k1[kWinBatch];
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-            const int u = u0 + i * kCombWaves;
-            const int64_t row = (((int64_t)b * p.win_cap + (u < nw ? u : u0)) * p.n_kv + h) * kHeadDim + 2 * lane;
-            k0[i] = ld<ACT>(p.win_k, row);
-            k1[i] = ld<ACT>(p.win_k, row + 1);
-        }
-#pragma unroll
-        for (int i = 0; i < kWinBatch; ++i) {
-            const int u = u0 + i * kCombWaves;
-            const float sc = wave_sum(q0 * k0[i] + q1 * k1[i]) * p.scale;
-            if (u < nw) {
-                if (lane == 0) sw[u] = sc;
-                mx = fmaxf(mx, sc);
-            }
-        }
+    // The window batches: the first was loaded with the records; the others
+    // (windows above 128 tokens) load and fold one at a time.
+    win_use(0, kr, vr);
+    for (int u0 = kCombWin * kCombWaves; u0 < nw; u0 += kCombWin * kCombWaves) {
+        win_load(u0, kr, vr);
+        win_use(u0, kr, vr);
     }
-    float M = block_reduce(mx, red, true);     // its barriers also publish part, wml and sw
-    for (int w8 = 0; w8 < kCombWaves; ++w8) M = fmaxf(M, wml[2 * w8]);
+    wpart[wv * kHeadDim + 2 * lane] = wa0;
+    wpart[wv * kHeadDim + 2 * lane + 1] = wa1;
+    if (lane == 0) {
+        wml[4 * wv + 2] = wm;
+        wml[4 * wv + 3] = wl;
+    }
+    __syncthreads();
 
+    // Merge the waves at the common max: oc = the rescaled record sums, and
+    // on the value part the rescaled window sums.
+    float M = -INFINITY;
+#pragma unroll
+    for (int w8 = 0; w8 < kCombWaves; ++w8) M = fmaxf(M, fmaxf(wml[4 * w8], wml[4 * w8 + 2]));
     const int64_t out_row = ((int64_t)b * p.n_q + j) * kHeadDim;
-    if (M == -INFINITY) {   // nothing attended for this sequence
+    if (M == -INFINITY) {   // nothing attended for this sequence (uniform branch)
         for (int f = tid; f < kHeadDim; f += blockDim.x) st<ACT>(p.out, out_row + f, 0.f);
     } else {
-        float scl[kCombWaves], Lt = 0.f;
+        float sr[kCombWaves], sw[kCombWaves], Lt = 0.f, Lw = 0.f;
 #pragma unroll
         for (int w8 = 0; w8 < kCombWaves; ++w8) {
-            scl[w8] = wml[2 * w8] == -INFINITY ? 0.f : expf(wml[2 * w8] - M);
-            Lt += scl[w8] * wml[2 * w8 + 1];
+            sr[w8] = wml[4 * w8] == -INFINITY ? 0.f : expf(wml[4 * w8] - M);
+            sw[w8] = wml[4 * w8 + 2] == -INFINITY ? 0.f : expf(wml[4 * w8 + 2] - M);
+            Lt += sr[w8] * wml[4 * w8 + 1];
+            Lw += sw[w8] * wml[4 * w8 + 3];
         }
-        float lw = 0.f;
-        for (int u = tid; u < nw; u += blockDim.x) {
-            const float e = expf(sw[u] - M);
-            sw[u] = e;
-            lw += e;
-        }
-        const float Lw = block_reduce(lw, red, false);
         for (int f = tid; f < nf; f += blockDim.x) {
             float v = 0.f;
 #pragma unroll
-            for (int w8 = 0; w8 < kCombWaves; ++w8) v += scl[w8] * part[w8 * nf + f];
+            for (int w8 = 0; w8 < kCombWaves; ++w8) v += sr[w8] * part[w8 * nf + f];
+            if (f >= H) {
+#pragma unroll
+                for (int w8 = 0; w8 < kCombWaves; ++w8) v += sw[w8] * wpart[w8 * kHeadDim + (f - H)];
+            }
             oc[f] = v;
         }
         __syncthreads();
-        // out[f] = (sum_i O_G[i] W2[f][i] + O_V[f] + L b2[f] + window) / (L + L_w).
+        // out[f] = (sum_i O_G[i] W2[f][i] + O_V[f] + window + L b2[f]) / (L + L_w)
         const float inv = 1.0f / (Lt + Lw);
-        const int f = f_out;
-        float y = 0.f;
-        if (w2_vec) {
-            auto piece = [&](int c, const uint4 u) {
-                const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        float y8[8], y4[4], y2[2], y1[1];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int i = i0 + 8 * c + 2 * k;
-                    y += oc[i] * __uint_as_float(wd[k] << 16) + oc[i + 1] * __uint_as_float(wd[k] & 0xffff0000u);
-                }
-            };
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (c < n_c) piece(c, w2pre[c]);
-            for (int c = 8; c < n_c; ++c) piece(c, w2v[c]);
-        } else {
-            const int i1 = quarter == 3 ? H : i0 + H / 4;
-            for (int i = i0; i < i1; ++i) y += oc[i] * ld<ACT>(p.w2, w2row + i);
+        for (int k = 0; k < 8; ++k) {
+            const int f = 16 * k + g16;
+            float y = l32 < n_pc ? dot_piece<ACT>(w2pre[k], oc + l32 * kEpp) : 0.f;
+            for (int pc = l32 + 32; pc < n_pc; pc += 32) y += dot_piece<ACT>(w2g[(int64_t)f * n_pc + pc], oc + pc * kEpp);
+            y8[k] = y;
         }
-        // Window values: quarter q takes the tokens u = q (mod 4); each token's
-        // row is read by 128 threads, coalesced; eight rows' loads in flight
-        // together.
-        for (int u0 = quarter; u0 < nw; u0 += 4 * kWinBatch) {
-            float vv[kWinBatch];
-#pragma unroll
-            for (int i = 0; i < kWinBatch; ++i) {
-                const int u = u0 + 4 * i;
-                vv[i] = u < nw ? ld<ACT>(p.win_v, (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + f) : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < kWinBatch; ++i) {
-                const int u = u0 + 4 * i;
-                if (u < nw) y += sw[u] * vv[i];
-            }
-        }
-        if (quarter == 3) {
-            y += oc[H + f];
-            if (p.b2) y += Lt * ld<ACT>(p.b2, ((int64_t)b * p.n_kv + h) * kHeadDim + f);
-        }
-        if (quarter > 0) red[8 + (quarter - 1) * kHeadDim + f] = y;
-        __syncthreads();
-        if (quarter == 0)
-            st<ACT>(p.out, out_row + f, (((y + red[8 + f]) + red[8 + kHeadDim + f]) + red[8 + 2 * kHeadDim + f]) * inv);
+        // Row sums over the 32 lanes of the half, transposed as they fold:
+        // lane group (b4, b3, b2) ends with pass k_own's full sum.
+        fold_half<4>(y8, y4, lane, 16);
+        fold_half<2>(y4, y2, lane, 8);
+        fold_half<1>(y2, y1, lane, 4);
+        float y = y1[0] + quad_xor2(y1[0]);
+        y += quad_xor1(y);
+        if ((lane & 3) == 0) st<ACT>(p.out, out_row + f_own, (y + oc[H + f_own] + Lt * b2_own) * inv);
     }
-    if (p.stats != nullptr && j % p.group == 0 && tid == 0) {
+    // Exact stats: the first wave sums the per-split counts, a split per lane
+    // (every load in flight at once; integer sums, so the order is free).
+    if (p.stats != nullptr && j % p.group == 0 && wv == 0) {
         int tok = 0, res = 0;
         const int32_t* c = p.counts + ((int64_t)b * p.n_kv + h) * p.n_split * 2;
-        for (int s = 0; s < nsplit; ++s) {
+        for (int s = lane; s < nsplit; s += kWave) {
             tok += c[2 * s];
             res += c[2 * s + 1];
         }
-        p.stats[((int64_t)b * p.n_kv + h) * 2 + 0] = tok + nw;
-        p.stats[((int64_t)b * p.n_kv + h) * 2 + 1] = res;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            tok += __shfl_xor(tok, o, kWave);
+            res += __shfl_xor(res, o, kWave);
+        }
+        if (lane == 0) {
+            p.stats[((int64_t)b * p.n_kv + h) * 2 + 0] = tok + nw;
+            p.stats[((int64_t)b * p.n_kv + h) * 2 + 1] = res;
+        }
     }
 }
 
 size_t combine_smem_bytes(const DecodeParams& p) {
-    return sizeof(float) * ((size_t)p.win_len + (kCombWaves + 1) * ((size_t)p.hidden + kHeadDim) + 4 * kHeadDim + 8 +
-                            2 * kCombWaves);
+    const size_t nf = (size_t)p.hidden + kHeadDim;
+    return sizeof(float) * ((kCombWaves + 1) * nf + (size_t)kCombWaves * kHeadDim + 4 * kCombWaves);
 }
 
 hipError_t launch_combine(const DecodeParams& p, int act, hipStream_t s) {

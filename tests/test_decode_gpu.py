@@ -154,6 +154,19 @@ def test_window_lengths(generic):
         check(case, cfg, generic=generic)
 
 
+@pytest.mark.parametrize("name,act_cfg", [("bf16", C4.replace(ctx_len=64 * 20 + 3, batch=2, win_cap=1024)),
+                                          ("f32", C1.replace(ctx_len=64 * 12 + 5, batch=2, win_cap=1024))])
+def test_long_windows(name, act_cfg):
+    """Windows that cross the combine's 128-token batches (eight waves of 16
+    tokens each, later batches loaded and folded in turn), up to the full
+    1024-token capacity; dominant window scores (query scaled up) so that an
+    unmerged or misscaled batch shows in the output."""
+    case = make_case(act_cfg, layer=2, q_scale=4.0)
+    for w in (127, 128, 129, 300, 1024):
+        case["win_len"] = w
+        check(case, act_cfg, generic=False)
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
 def test_sequence_with_everything_evicted(generic):
     cfg = SMALL["i8_keep"]
