@@ -141,8 +141,9 @@ hipError_t launch_window_append(const WindowParams& p, hipStream_t s) {
 // predictor's value for every token exactly (up to rounding).
 //
 // The kernel is a short chain of dependent steps, so every load it needs is
-// issued at the start, in one round trip: this thread's W2 pieces, the window
-// rows of its wave's first window batch, then the records. Each wave folds
+// issued at the start, in one round trip: the records of its wave's first
+// batch, the window rows of its first window batch, then this thread's W2
+// pieces (needed last, so the records merge while they land). Each wave folds
 // its records and its window tokens into running (max, weight sum, sums)
 // pairs, the window tokens as one more record whose hidden part is zero (their
 // values are exact), and two barriers merge the eight waves.
@@ -197,7 +198,7 @@ template <int ACT> __device__ __forceinline__ float dot_piece(const uint4 u, con
 template <int ACT>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = j / p.group, H = p.hidden, S = p.part_stride, nf = H + kHeadDim;
     const int nsplit = min(p.n_split, (attended_count(p, b) + p.blocks_per_split - 1) / p.blocks_per_split);
     const int nw = window_len(p);
@@ -208,10 +209,90 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
     float* oc = wpart + kCombWaves * kHeadDim;     // [nf]: the merged sums
     float* wml = oc + nf;                          // [8][4]: record max and weight sum, window max and weight sum
 
+    // Issue order: the first record batch, the first window batch, then the
+    // W2 pieces, b2 and the query. Loads complete in issue order, so the
+    // records merge while the W2 rows (cold in every cache) are still in
+    // flight; W2 is first needed after both barriers.
+    //
+    // Records: wave wv merges the splits wv, wv+8, ... eight at a time, with
+    // a running max (every sum is rescaled to it as it grows), so the loads of
+    // a batch's maxima, weight sums and O rows are in flight together. Lane
+    // takes the features f0 + lane + 64 i, six at a time: each load of the
+    // wave reads 256 consecutive bytes of one record.
+    // rec_load issues plain loads only: a split past the last reads split 0
+    // (written by this call whenever nsplit >= 1) and a feature past the
+    // record reads its last one, and rec_use gives those entries weight
+    // zero. Loads feeding a select under the split test made the compiler
+    // wait for each record before issuing the next one's.
+    auto rec_load = [&](int f0, int s0, float2 (&ml)[8], float (&v)[8][6]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sp = s0 + kCombWaves * u;
+            const float* rec = P + (int64_t)(sp < nsplit ? sp : 0) * S;
+            ml[u] = *reinterpret_cast<const float2*>(rec);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) v[u][i] = rec[2 + min(f0 + lane + 64 * i, nf - 1)];
+        }
+    };
+    auto rec_use = [&](int s0, const float2 (&ml)[8], const float (&v)[8][6], float& mrun, float& lrun, float (&acc)[6]) {
+        float mb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mb[u] = s0 + kCombWaves * u < nsplit ? ml[u].x : -INFINITY;
+        float mnew = mrun;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mnew = fmaxf(mnew, mb[u]);
+        const float r = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
+        lrun *= r;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) acc[i] *= r;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float e = mb[u] == -INFINITY ? 0.f : __expf(mb[u] - mnew);
+            lrun += e * ml[u].y;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) acc[i] += e * v[u][i];
+        }
+        mrun = mnew;
+    };
+    auto rec_store = [&](int f0, const float (&acc)[6], float mrun, float lrun) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const int fi = f0 + lane + 64 * i;
+            if (fi < nf) part[wv * nf + fi] = acc[i];
+        }
+        if (lane == 0 && f0 == 0) {
+            wml[4 * wv] = mrun;
+            wml[4 * wv + 1] = lrun;
+        }
+    };
+    float2 ml0[8];
+    float v0[8][6];
+    if (nsplit > 0) rec_load(0, wv, ml0, v0);     // none: split 0 may hold stale data
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Window tokens: batch u0 gives wave wv the tokens u0 + 16 wv + i; lane
+    // holds features 2 lane and 2 lane + 1 of the query and of each row.
+    // A wave with no token in the batch loads nothing (the buffers may be
+    // absent when the window is empty); otherwise every row load is
+    // unconditional, tokens past the window reading the last one (win_use
+    // ignores them).
+    auto win_load = [&](int u0, uint2 (&kr)[kCombWin], uint2 (&vr)[kCombWin]) {
+        if (u0 + kCombWin * wv >= nw) return;
+#pragma unroll
+        for (int i = 0; i < kCombWin; ++i) {
+            const int u = min(u0 + kCombWin * wv + i, nw - 1);
+            const int64_t row = (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + 2 * lane;
+            kr[i] = ld_pair_raw<ACT>(p.win_k, row);
+            vr[i] = ld_pair_raw<ACT>(p.win_v, row);
+        }
+    };
+    uint2 kr[kCombWin], vr[kCombWin];
+    win_load(0, kr, vr);
+
     // W2 rows: out[f] takes the 32 lanes of one half-wave, so every load reads
     // whole rows (coalesced). Pass k covers the rows f = 16 k + tid / 32; lane
-    // l32 of the half takes the 16-byte pieces l32 + 32 m of its row. The
-    // pieces of m = 0 and b2 are loaded now.
+    // l32 of the half takes the 16-byte pieces l32 + 32 m of its row; the
+    // pieces of m = 0 are loaded here.
     constexpr int kEpp = ACT == DT_F32 ? 4 : 8;    // W2 elements per 16-byte piece
     const int n_pc = H / kEpp;                     // pieces per row (H is a multiple of 16)
     const int l32 = tid & 31, g16 = tid >> 5;
@@ -222,26 +303,25 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int f = 16 * k + g16;
-        w2pre[k] = l32 < n_pc ? w2g[(int64_t)f * n_pc + l32] : make_uint4(0u, 0u, 0u, 0u);
+        w2pre[k] = w2g[(int64_t)f * n_pc + min(l32, n_pc - 1)];   // lanes past the row: unused duplicate
     }
-    // The row sums end in lane group k_own of the half (see below); b2 of that row.
+    // The row sums end in lane group k_own of the half (see below); b2 of that
+    // row, kept as stored and converted where it is used.
     const int k_own = 4 * ((lane >> 4) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1);
     const int f_own = 16 * k_own + g16;
-    const float b2_own = p.b2 ? ld<ACT>(p.b2, head * kHeadDim + f_own) : 0.f;
-
-    // Window tokens: batch u0 gives wave wv the tokens u0 + 16 wv + i; lane
-    // holds features 2 lane and 2 lane + 1 of the query and of each row.
+    // Without b2 the load reads the query instead (no branch, whose join
+    // would make the compiler wait for every load issued so far) and the
+    // value is dropped where it is used.
+    const bool has_b2 = p.b2 != nullptr;
+    const void* const b2src = has_b2 ? p.b2 : p.q;
+    const int64_t b2i = has_b2 ? head * kHeadDim + f_own : 0;
+    uint32_t b2_raw;
+    if constexpr (ACT == DT_F32) b2_raw = static_cast<const uint32_t*>(b2src)[b2i];
+    else b2_raw = static_cast<const uint16_t*>(b2src)[b2i];
     const int64_t q_row = ((int64_t)b * p.n_q + j) * kHeadDim;
     const float2 qq = pair_f<ACT>(ld_pair_raw<ACT>(p.q, q_row + 2 * lane));
-    auto win_load = [&](int u0, uint2 (&kr)[kCombWin], uint2 (&vr)[kCombWin]) {
-#pragma unroll
-        for (int i = 0; i < kCombWin; ++i) {
-            const int u = u0 + kCombWin * wv + i;
-            const int64_t row = (((int64_t)b * p.win_cap + u) * p.n_kv + h) * kHeadDim + 2 * lane;
-            kr[i] = u < nw ? ld_pair_raw<ACT>(p.win_k, row) : make_uint2(0u, 0u);
-            vr[i] = u < nw ? ld_pair_raw<ACT>(p.win_v, row) : make_uint2(0u, 0u);
-        }
-    };
+    __builtin_amdgcn_sched_barrier(0);
+
     float wm = -INFINITY, wl = 0.f, wa0 = 0.f, wa1 = 0.f;   // this wave's window max, weight sum, value sums
     auto win_use = [&](int u0, const uint2 (&kr)[kCombWin], const uint2 (&vr)[kCombWin]) {
         if (u0 + kCombWin * wv >= nw) return;       // no token of this batch is the wave's
@@ -270,14 +350,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
             if (u0 + kCombWin * wv + i < nw) mnew = fmaxf(mnew, sc[i]);
         }
         if (mnew == -INFINITY) return;             // no token of this batch is the wave's
-        const float r = wm == -INFINITY ? 0.f : expf(wm - mnew);
+        const float r = wm == -INFINITY ? 0.f : __expf(wm - mnew);
         wl *= r;
         wa0 *= r;
         wa1 *= r;
 #pragma unroll
         for (int i = 0; i < kCombWin; ++i) {
             if (u0 + kCombWin * wv + i < nw) {
-                const float e = expf(sc[i] - mnew);
+                const float e = __expf(sc[i] - mnew);
                 const float2 vv = pair_f<ACT>(vr[i]);
                 wl += e;
                 wa0 += e * vv.x;
@@ -286,57 +366,28 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
         }
         wm = mnew;
     };
-    uint2 kr[kCombWin], vr[kCombWin];
-    win_load(0, kr, vr);
 
-    // Records: wave wv merges the splits wv, wv+8, ... eight at a time, with
-    // a running max (every sum is rescaled to it as it grows), so the loads of
-    // a batch's maxima, weight sums and O rows are in flight together. Lane
-    // takes the features lane + 64 i, six at a time: each load of the wave
-    // reads 256 consecutive bytes of one record.
-    for (int f0 = 0; f0 < nf; f0 += 64 * 6) {
+    // Features 0 .. 383 with the first batch already loaded (straight-line,
+    // so its wait covers only the loads issued before the window and W2),
+    // then any further feature slices.
+    {
+        float mrun = -INFINITY, lrun = 0.f;
+        float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (nsplit > 0) rec_use(wv, ml0, v0, mrun, lrun, acc);
+        for (int s0 = wv + kCombWaves * 8; s0 < nsplit; s0 += kCombWaves * 8) {
+            rec_load(0, s0, ml0, v0);
+            rec_use(s0, ml0, v0, mrun, lrun, acc);
+        }
+        rec_store(0, acc, mrun, lrun);
+    }
+    for (int f0 = 64 * 6; f0 < nf; f0 += 64 * 6) {
         float mrun = -INFINITY, lrun = 0.f;
         float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int s0 = wv; s0 < nsplit; s0 += kCombWaves * 8) {
-            float mb[8], lb[8], v[8][6];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int sp = s0 + kCombWaves * u;
-                const bool ok = sp < nsplit;
-                const float* rec = P + (int64_t)(ok ? sp : 0) * S;
-                mb[u] = ok ? rec[0] : -INFINITY;
-                lb[u] = ok ? rec[1] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 6; ++i) {
-                    const int fi = f0 + lane + 64 * i;
-                    v[u][i] = (ok && fi < nf) ? rec[2 + fi] : 0.f;
-                }
-            }
-            float mnew = mrun;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) mnew = fmaxf(mnew, mb[u]);
-            const float r = mrun == -INFINITY ? 0.f : expf(mrun - mnew);
-            lrun *= r;
-#pragma unroll
-            for (int i = 0; i < 6; ++i) acc[i] *= r;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float e = mb[u] == -INFINITY ? 0.f : expf(mb[u] - mnew);
-                lrun += e * lb[u];
-#pragma unroll
-                for (int i = 0; i < 6; ++i) acc[i] += e * v[u][i];
-            }
-            mrun = mnew;
+            rec_load(f0, s0, ml0, v0);
+            rec_use(s0, ml0, v0, mrun, lrun, acc);
         }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int fi = f0 + lane + 64 * i;
-            if (fi < nf) part[wv * nf + fi] = acc[i];
-        }
-        if (lane == 0 && f0 == 0) {
-            wml[4 * wv] = mrun;
-            wml[4 * wv + 1] = lrun;
-        }
+        rec_store(f0, acc, mrun, lrun);
     }
 
     // The window batches: the first was loaded with the records; the others
@@ -366,8 +417,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
         float sr[kCombWaves], sw[kCombWaves], Lt = 0.f, Lw = 0.f;
 #pragma unroll
         for (int w8 = 0; w8 < kCombWaves; ++w8) {
-            sr[w8] = wml[4 * w8] == -INFINITY ? 0.f : expf(wml[4 * w8] - M);
-            sw[w8] = wml[4 * w8 + 2] == -INFINITY ? 0.f : expf(wml[4 * w8 + 2] - M);
+            sr[w8] = wml[4 * w8] == -INFINITY ? 0.f : __expf(wml[4 * w8] - M);
+            sw[w8] = wml[4 * w8 + 2] == -INFINITY ? 0.f : __expf(wml[4 * w8 + 2] - M);
             Lt += sr[w8] * wml[4 * w8 + 1];
             Lw += sw[w8] * wml[4 * w8 + 3];
         }
@@ -399,6 +450,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(DecodeParams p) {
         fold_half<1>(y2, y1, lane, 4);
         float y = y1[0] + quad_xor2(y1[0]);
         y += quad_xor1(y);
+        const float b2_own = has_b2 ? __uint_as_float(ACT == DT_F32 ? b2_raw : b2_raw << 16) : 0.f;
         if ((lane & 3) == 0) st<ACT>(p.out, out_row + f_own, (y + oc[H + f_own] + Lt * b2_own) * inv);
     }
     // Exact stats: the first wave sums the per-split counts, a split per lane

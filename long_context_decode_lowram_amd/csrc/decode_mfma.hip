@@ -51,6 +51,7 @@ constexpr int kRowBytes = kKc * 2;        // one bf16 row of a rank chunk: 128 b
 constexpr int kStage = kFc * kHeadDim;    // elements per stage buffer: a weight chunk (= a B_l chunk)
 constexpr int kQRow = kHeadDim + 8;
 constexpr int kMaxG = 8;
+constexpr int kMaxHidden = 1024;             // the largest hidden width the library takes
 constexpr int kXcd = 8;                   // XCDs on MI355X; workgroups go round-robin over them
 constexpr int kABytes = kBlock * kRowBytes;   // one wave's A rows of a rank chunk: 8 KB
 static_assert(128 * kRowBytes == kStage * 2, "a stage buffer holds one B_l chunk or one weight chunk");
@@ -122,12 +123,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // and pl, which are dead by the feature loop
     float (*const oslot0)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa);
     float (*const oslot1)[kMaxG][kFc] = reinterpret_cast<float (*)[kMaxG][kFc]>(sa + 8192);
-    float* const b1s = reinterpret_cast<float*>(sa + 20736);                           // [1024] hidden bias
+    float* const b1s = reinterpret_cast<float*>(sa + 20736);                           // [kMaxHidden] hidden bias
     float (*const mw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(sa + 24832);         // per-wave score max
     float (*const lw)[kMaxG] = reinterpret_cast<float (*)[kMaxG]>(sa + 24960);         // per-wave weight sum
     int* const cnt_tok = reinterpret_cast<int*>(sa + 25088);
     int* const cnt_res = reinterpret_cast<int*>(sa + 25104);
-    static_assert(25120 <= kWaves * kABytes && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736 &&
+    static_assert(25120 <= kWaves * kABytes && 20736 + 4 * kMaxHidden <= 24832 && 16 * kQRow * 2 <= 4352 && 2 * 8192 <= 20736 &&
                       4352 + kWaves * kMaxG * (kBlock + 1) * 4 <= 20736,
                   "epilogue arrays overflow sa");
 
@@ -183,17 +184,49 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             dma16<kNonTemporal>(rr, rs_w + q * 1024, src, 0u);
         }
     };
-    // Token (relative to the block) and int8 scale of residual row q0 + lane.
+    // Token and int8 scale of residual row q0 + lane.
+    // Lanes past the batch read its last row: every use of tok and scl checks
+    // the row against the batch size. The loads carry no lane test and their
+    // values stay as stored (the caller takes t0 off where it uses them):
+    // a lane test, or arithmetic right after the load, made the compiler wait
+    // for it, and for every copy issued before it, on the spot.
     auto res_meta = [&](int q0, int& tok, float& scl) {
-        const int n = min(kResRows, hi - q0);
-        tok = lane < n ? p.res_idx[res_row + q0 + lane] - t0 : -1;
-        scl = (res_scaled(RDT) && lane < n) ? p.res_scale[res_row + q0 + lane] : 1.f;
+        const int n = min(kResRows, hi - q0);            // >= 1: q0 < hi
+        const int64_t r = res_row + q0 + min(lane, n - 1);
+        tok = p.res_idx[r];
+        scl = res_scaled(RDT) ? p.res_scale[r] : 1.f;
     };
     int tok0 = -1;
     float scl0 = 1.f;
     if (lo < hi) {
         dma_res(lo);
         res_meta(lo, tok0, scl0);
+    }
+
+    // Epilogue operands that do not depend on the keys, loaded now so that
+    // they arrive with the first chunk's copies instead of costing a round
+    // trip after the key loop: this thread's 8 query elements (rows >= G
+    // read row G - 1 and are zeroed where staged), its hidden-bias values
+    // (without b1 the query is read instead and dropped), and for int8 A the
+    // row scales of its token columns (columns past the block read the
+    // block's first row; those keys are zero).
+    const int qj = tid >> 4, qc = (tid & 15) * 8;
+    const u32x4 qv_raw = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) +
+                                                        ((int64_t)b * p.n_q + h * G + min(qj, G - 1)) * kHeadDim + qc);
+    const bool has_b1 = p.b1 != nullptr;
+    const uint16_t* const b1src = has_b1 ? static_cast<const uint16_t*>(p.b1) + ((int64_t)b * p.n_kv + h) * H
+                                         : static_cast<const uint16_t*>(p.q);
+    uint16_t b1_raw[kMaxHidden / kThreads];
+#pragma unroll
+    for (int k = 0; k < kMaxHidden / kThreads; ++k) b1_raw[k] = b1src[has_b1 ? min(tid + kThreads * k, H - 1) : 0];
+    float ascl[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (ADT == DT_I8) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int tl = tt * 16 + l16;
+            const float sv = p.a_scale[(int64_t)b * p.ctx_len + t0 + (tl < nt ? tl : 0)];
+            ascl[tt] = tl < nt ? sv : 1.f;
+        }
     }
 
     // ---- 1. K^T = B_l(head)^T . A_blk^T
@@ -386,17 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // A region and the stage buffers, which the epilogue reuses.
     wait_vmcnt<0>();
 
-    // This thread's 8 query elements and, for int8 A, the row scales.
-    const int qj = tid >> 4, qc = (tid & 15) * 8;
-    u32x4 qv = {0u, 0u, 0u, 0u};
-    if (qj < G) qv = *reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.q) +
-                                                     ((int64_t)b * p.n_q + h * G + qj) * kHeadDim + qc);
-    float ascl[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int tl = tt * 16 + l16;
-        ascl[tt] = ADT == DT_I8 && tl < nt ? p.a_scale[a_row0 + tl] : 1.f;
-    }
+    const u32x4 qv = qj < G ? qv_raw : u32x4{0u, 0u, 0u, 0u};
 
     // Tokens past the block's end contribute nothing: their factor rows were
     // read through a resource that ends at the block, as zeros, so their K
@@ -474,7 +497,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     const int n_fchunks = H / kFc;
     const __bf16* w1 = static_cast<const __bf16*>(p.w1) + ((int64_t)b * p.n_kv + h) * H * (int64_t)kHeadDim;
     const __bf16* wl = static_cast<const __bf16*>(p.w_lin) + ((int64_t)b * p.n_kv + h) * kHeadDim * (int64_t)kHeadDim;
-    const __bf16* b1 = p.b1 ? static_cast<const __bf16*>(p.b1) + ((int64_t)b * p.n_kv + h) * H : nullptr;
     float* rec0 = p.partials + (((int64_t)b * p.n_q + h * G) * p.n_split + split) * (int64_t)p.part_stride;
     const int64_t rec_step = (int64_t)p.n_split * p.part_stride;
 
@@ -530,6 +552,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             int tok = tok0;
             float scl_unused = 1.f;
             if (q0 != lo) res_meta(q0, tok, scl_unused);
+            tok -= t0;
             applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
             s16x4 pa;
 #pragma unroll
@@ -564,6 +587,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             int tok = tok0;
             float scl = scl0;
             if (q0 != lo) res_meta(q0, tok, scl);
+            tok -= t0;
             applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
             bf16x8 pa;
 #pragma unroll
@@ -608,6 +632,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             int tok = tok0;
             float scl = scl0;
             if (q0 != lo) res_meta(q0, tok, scl);
+            tok -= t0;
             applied += __popcll(__ballot(lane < n && tok >= 0 && tok < nt));
             wait_vmcnt<0>();
             for (int ks = 0; ks * 32 < n; ++ks) {
@@ -655,6 +680,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
             int tok = tok0;
             float scl = scl0;
             if (q0 != lo) res_meta(q0, tok, scl);
+            tok -= t0;
             wait_vmcnt<0>();
             // Four rows per step, all their LDS reads first. Rows past n read the
             // zeros the copy left there; rows outside the block get weight zero.
@@ -816,7 +842,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeParams p
     // Past the value part's barrier every wave is done with the query rows and
     // softmax weights; their space holds the two per-wave O buffers of the
     // feature loop.
-    for (int e = tid; e < H; e += kThreads) b1s[e] = b1 ? (float)b1[e] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxHidden / kThreads; ++k) {
+        const int e = tid + kThreads * k;
+        if (e < H) b1s[e] = has_b1 ? __uint_as_float((uint32_t)b1_raw[k] << 16) : 0.f;
+    }
     barrier_lds();               // every wave has read the P K sums in the stage buffers
     store_w(0, preA);
     stage_w(min(1, n_fchunks - 1), preA);
