@@ -45,6 +45,7 @@ constexpr int kPKc = 64;                     // rank columns per B_l / A chunk
 constexpr int kPRow = kPKc * 2;              // bytes of one row of a rank chunk
 constexpr int kBuf = 16384;                  // bytes of one LDS buffer
 constexpr int kXcds = 8;
+constexpr int kPMaxHidden = 4096;           // the largest hidden width the prefill takes
 constexpr uint32_t kOob = 0x80000000u;       // buffer offset past every valid range: reads zero
 
 // LDS row r of a 32-row group holds row perm(r) of the source: accumulator
@@ -94,10 +95,25 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     }
 
     __shared__ __attribute__((aligned(16))) unsigned char buf0[kBuf], buf1[kBuf], buf2[kBuf], buf3[kBuf];
+    // The head's biases as float (zero when absent), for the predictor steps.
+    __shared__ __attribute__((aligned(16))) float sb1[kPMaxHidden], sb2[kHeadDim];
     // This wave's 64 rows of V (256-byte rows; 16-byte piece p of row r at
     // slot p ^ (r & 15)), copied after the keys so they land during the
     // predictor steps. 128 KB of LDS in all: one workgroup per CU.
     __shared__ __attribute__((aligned(16))) unsigned char sv[kPw * kBlock * 256];
+
+    // The biases are loaded now, with no branch and no arithmetic on them until
+    // they are staged after the key loop (a missing bias reads the W_lin row
+    // instead and is dropped): loaded where the predictor steps use them, each
+    // load made the compiler wait for it, and for the next step's copies in
+    // flight, on the spot.
+    const bool has_b1 = p.b1 != nullptr, has_b2 = p.b2 != nullptr;
+    const uint16_t* const b1src = has_b1 ? static_cast<const uint16_t*>(p.b1) + lh * H : static_cast<const uint16_t*>(p.w_lin);
+    const uint16_t* const b2src = has_b2 ? static_cast<const uint16_t*>(p.b2) + lh * kHeadDim : static_cast<const uint16_t*>(p.w_lin);
+    uint16_t b1raw[kPMaxHidden / kPThreads];
+#pragma unroll
+    for (int k = 0; k < kPMaxHidden / kPThreads; ++k) b1raw[k] = b1src[has_b1 ? min(tid + kPThreads * k, H - 1) : 0];
+    const uint16_t b2raw = b2src[has_b2 ? (tid & (kHeadDim - 1)) : 0];
 
     // ---- 1. K^T = B_l(head)^T . A^T over the rank, 64 columns per chunk
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(
@@ -192,6 +208,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     }
     wait_vmcnt<0>();
 
+    // Stage the biases (the first predictor step's barrier publishes them).
+#pragma unroll
+    for (int k = 0; k < kPMaxHidden / kPThreads; ++k) {
+        const int e = tid + kPThreads * k;
+        if (e < H) sb1[e] = has_b1 ? __uint_as_float((uint32_t)b1raw[k] << 16) : 0.f;
+    }
+    if (tid < kHeadDim) sb2[tid] = has_b2 ? __uint_as_float((uint32_t)b2raw << 16) : 0.f;
+
     // K as the B operand: kf[tt][s] holds features 32s + 8g + (0..7) of token 16tt + l16.
     bf16x8 kf[4][4];
 #pragma unroll
@@ -245,8 +269,6 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
     // V_hat^T accumulators: vacc[ot][tt] holds outputs 16ot + 4g + (0..3) of
     // token 16tt + l16; step 0 starts them at b2.
     f32x4 vacc[8][4];
-    const __bf16* b2 = p.b2 ? static_cast<const __bf16*>(p.b2) + lh * kHeadDim : nullptr;
-    const __bf16* b1 = p.b1 ? static_cast<const __bf16*>(p.b1) + lh * H : nullptr;
 
     // One step: wait for its copies, compute from (s0, s1), then, once every
     // wave is done with them, start the copies of step j + 2 into them.
@@ -261,11 +283,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
                 bf16x8 wf[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) wf[s] = lds16(src, (uint32_t)(row * 256 + (((4 * s + g4) ^ (row & 15)) * 16)));
-                f32x4 bb = {0.f, 0.f, 0.f, 0.f};
-                if (b2) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bb[i] = (float)b2[ot * 16 + 4 * g4 + i];
-                }
+                const f32x4 bb = *reinterpret_cast<const f32x4*>(sb2 + ot * 16 + 4 * g4);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     vacc[ot][tt] = bb;
@@ -275,11 +293,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_mfma_kernel(PrefillParam
             }
         } else {
             const int hc = j - 1;
-            f32x4 zb[4];             // hidden bias of LDS rows 16ht + 4g + (0..3)
+            f32x4 zb[4];             // hidden bias of LDS rows 16ht + 4g + (0..3): four consecutive units
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zb[ht][i] = b1 ? (float)b1[hc * 64 + perm32(ht * 16 + 4 * g4 + i)] : 0.f;
+            for (int ht = 0; ht < 4; ++ht) zb[ht] = *reinterpret_cast<const f32x4*>(sb1 + hc * 64 + perm32(ht * 16 + 4 * g4));
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 z[4];
