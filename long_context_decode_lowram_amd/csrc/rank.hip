@@ -348,23 +348,36 @@ hipError_t launch_rank_compact(const RankParams& p, hipStream_t s) {
 // Sixteen lanes per stored residual: lane j of a group owns elements
 // 8j .. 8j+7 of the row (16-byte loads of bf16, 32 of f32). R = V - V_hat at
 // the chosen token, exact in binary64, then encoded. A wave holds four
-// groups and takes two slots per group per iteration (eight rows' loads in
-// flight), walking the slots with a grid stride.
+// groups and takes four slots per group per iteration, walking the slots
+// with a grid stride: the iteration loads its 16 token indices, then the
+// 16 rows of V and of V_hat, then encodes, so it costs two memory round
+// trips. Slots past the end read the last slot (nothing is stored for
+// them): loads under a slot test made the compiler wait for each slot's
+// index and rows in turn.
+template <int IDT> struct RowRaw { uint4 v[IDT == DT_F32 ? 2 : 1], h[IDT == DT_F32 ? 2 : 1]; };
 template <int IDT>
-__device__ __forceinline__ void load_row8(const void* base, int64_t e0, double (&d)[8], const void* base_h) {
-    if (IDT == DT_BF16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
-        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base_h) + e0);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) d[k] = piece_elem<DT_BF16>(u, k) - piece_elem<DT_BF16>(w, k);
+__device__ __forceinline__ RowRaw<IDT> load_row8_raw(const void* base, int64_t e0, const void* base_h) {
+    RowRaw<IDT> r;
+    if constexpr (IDT == DT_BF16) {
+        r.v[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e0);
+        r.h[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base_h) + e0);
     } else {
         const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + e0);
         const uint4* ph = reinterpret_cast<const uint4*>(static_cast<const float*>(base_h) + e0);
-        const uint4 u0 = pv[0], u1 = pv[1], w0 = ph[0], w1 = ph[1];
+        r.v[0] = pv[0]; r.v[1] = pv[1]; r.h[0] = ph[0]; r.h[1] = ph[1];
+    }
+    return r;
+}
+template <int IDT>
+__device__ __forceinline__ void row8_diff(const RowRaw<IDT>& r, double (&d)[8]) {
+    if constexpr (IDT == DT_BF16) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d[k] = piece_elem<DT_BF16>(r.v[0], k) - piece_elem<DT_BF16>(r.h[0], k);
+    } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            d[k] = piece_elem<DT_F32>(u0, k) - piece_elem<DT_F32>(w0, k);
-            d[4 + k] = piece_elem<DT_F32>(u1, k) - piece_elem<DT_F32>(w1, k);
+            d[k] = piece_elem<DT_F32>(r.v[0], k) - piece_elem<DT_F32>(r.h[0], k);
+            d[4 + k] = piece_elem<DT_F32>(r.v[1], k) - piece_elem<DT_F32>(r.h[1], k);
         }
     }
 }
@@ -428,30 +441,59 @@ __device__ __forceinline__ void store_res8(const RankParams& p, int64_t gid, int
 
 template <int IDT, int RDT>
 __global__ __launch_bounds__(256) void rank_gather_kernel(RankParams p, int64_t n_slots) {
+    constexpr int U = 4;                                        // slots per group per iteration
     const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
     const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-    const int64_t stride = (int64_t)gridDim.x * 4 * 8;     // slots per grid step
-    auto row_of = [&](int64_t gid) {
-        const int64_t seg = gid / p.n_res;
-        const int64_t sl = seg / p.n_kv, h = seg % p.n_kv;
-        int t = p.res_idx[gid];
-        t = t < 0 ? 0 : (t >= p.ctx_len ? p.ctx_len - 1 : t);
-        return ((sl * p.ctx_len + t) * p.n_kv + h) * kHeadDim + 8 * j;
+    const int64_t stride = (int64_t)gridDim.x * 4 * 4 * U;     // slots per grid step
+    const bool small = n_slots <= 0x7fffffff;                   // 32-bit divisions suffice
+    const int64_t tok_stride = (int64_t)p.n_kv * kHeadDim;     // elements between tokens of a slice
+    // Element offset of token 0 of slot g's (slice, head), plus this lane's 8 elements.
+    auto seg_base = [&](int64_t g) {
+        int64_t sl, h;
+        if (small) {
+            const uint32_t seg = (uint32_t)g / (uint32_t)p.n_res;
+            sl = seg / (uint32_t)p.n_kv;
+            h = seg % (uint32_t)p.n_kv;
+        } else {
+            const int64_t seg = g / p.n_res;
+            sl = seg / p.n_kv;
+            h = seg % p.n_kv;
+        }
+        return (sl * p.ctx_len * p.n_kv + h) * kHeadDim + 8 * j;
     };
-    for (int64_t base = wave * 8; base < n_slots; base += stride) {
-        const int64_t g0 = base + grp, g1 = base + 4 + grp;    // a group's two slots (uniform per group)
-        double d0[8], d1[8];
-        if (g0 < n_slots) load_row8<IDT>(p.v, row_of(g0), d0, p.v_hat);
-        if (g1 < n_slots) load_row8<IDT>(p.v, row_of(g1), d1, p.v_hat);
-        if (g0 < n_slots) store_res8<RDT>(p, g0, j, d0);
-        if (g1 < n_slots) store_res8<RDT>(p, g1, j, d1);
+    for (int64_t base = wave * (4 * U); base < n_slots; base += stride) {
+        int64_t gid[U], rb[U];
+        int tk[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            gid[u] = base + grp + 4 * u;                        // uniform per group
+            rb[u] = seg_base(gid[u] < n_slots ? gid[u] : n_slots - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) tk[u] = p.res_idx[gid[u] < n_slots ? gid[u] : n_slots - 1];
+        __builtin_amdgcn_sched_barrier(0);
+        RowRaw<IDT> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tk[u] < 0 ? 0 : (tk[u] >= p.ctx_len ? p.ctx_len - 1 : tk[u]);
+            raw[u] = load_row8_raw<IDT>(p.v, rb[u] + (int64_t)t * tok_stride, p.v_hat);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (gid[u] < n_slots) {
+                double d[8];
+                row8_diff<IDT>(raw[u], d);
+                store_res8<RDT>(p, gid[u], j, d);
+            }
+        }
     }
 }
 
 hipError_t launch_rank_gather(const RankParams& p, hipStream_t s) {
     const int64_t n_slots = (int64_t)p.n_slices * p.n_kv * p.n_res;
     if (n_slots == 0) return hipSuccess;
-    const int64_t want = (n_slots + 31) / 32;                 // one step per workgroup covers 32 slots
+    const int64_t want = (n_slots + 63) / 64;                 // one step per workgroup covers 64 slots
     const dim3 grid((unsigned)(want < 8192 ? want : 8192));
     if (p.in_dtype == DT_F32) {
         if (p.res_dtype == DT_F32) hipLaunchKernelGGL((rank_gather_kernel<DT_F32, DT_F32>), grid, dim3(256), 0, s, p, n_slots);
