@@ -450,9 +450,20 @@ __global__ __launch_bounds__(1024) void xkv_chol_panel_kernel(double* g, int r, 
 
     for (int c0 = j0; c0 < jend; c0 += kCholPw) {
         const int rows = r - c0;
-        for (int e = tid; e < rows * kCholPw; e += 1024) {
-            const int i = e / kCholPw, c = e % kCholPw;
-            pan[e] = g[(int64_t)(c0 + i) * r + c0 + c];
+        // Eight loads per thread in flight before any LDS store (a load and
+        // its store per iteration made each iteration a memory round trip);
+        // entries past the panel read its last one and are not stored.
+        const int n_pan = rows * kCholPw;
+        for (int e0 = tid; e0 < n_pan; e0 += 1024 * 8) {
+            double v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = min(e0 + 1024 * k, n_pan - 1);
+                v[k] = g[(int64_t)(c0 + e / kCholPw) * r + c0 + e % kCholPw];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (e0 + 1024 * k < n_pan) pan[e0 + 1024 * k] = v[k];
         }
         __syncthreads();
         // Column c stays unscaled until the end of the 16 steps: every thread
@@ -491,6 +502,15 @@ __global__ __launch_bounds__(1024) void xkv_chol_panel_kernel(double* g, int r, 
             const int bi = e / nbk, bk = e % nbk;
             if (bk > bi) continue;
             const int i0 = kCholPw + bi * 4, k0 = kCholPw + bk * 4;
+            // The block's 16 entries of G (all inside the matrix, the upper
+            // ones too) are loaded before the products and written back under
+            // the triangle test: a load under that test made each entry a
+            // memory round trip of its own.
+            double gv[4][4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) gv[a][b] = g[(int64_t)(c0 + i0 + a) * r + c0 + k0 + b];
             double sacc[4][4];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
@@ -513,7 +533,7 @@ __global__ __launch_bounds__(1024) void xkv_chol_panel_kernel(double* g, int r, 
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    if (k0 + b <= i0 + a) g[(int64_t)(c0 + i0 + a) * r + c0 + k0 + b] -= sacc[a][b];
+                    if (k0 + b <= i0 + a) g[(int64_t)(c0 + i0 + a) * r + c0 + k0 + b] = gv[a][b] - sacc[a][b];
         }
         __syncthreads();
     }
@@ -535,13 +555,30 @@ __global__ __launch_bounds__(256) void xkv_chol_update_kernel(double* g, int r, 
     while ((ti + 1) * (ti + 2) / 2 <= e) ++ti;
     const int tk = e - ti * (ti + 1) / 2;
     const int r0 = base + ti * kCholNb, k0 = base + tk * kCholNb;      // both < r: r - base is a multiple of 64
-    for (int x = tid; x < kCholNb * kCholNb; x += 256) {
-        const int row = x / kCholNb, c = x % kCholNb;
-        li[row][c] = g[(int64_t)(r0 + row) * r + j0 + c];
-        lk[row][c] = g[(int64_t)(k0 + row) * r + j0 + c];
+    // All 32 loads of a thread in flight before its LDS stores.
+    static_assert(kCholNb * kCholNb % 256 == 0, "whole tiles per thread");
+    double vi[kCholNb * kCholNb / 256], vk[kCholNb * kCholNb / 256];
+#pragma unroll
+    for (int q = 0; q < kCholNb * kCholNb / 256; ++q) {
+        const int x = tid + 256 * q, row = x / kCholNb, c = x % kCholNb;
+        vi[q] = g[(int64_t)(r0 + row) * r + j0 + c];
+        vk[q] = g[(int64_t)(k0 + row) * r + j0 + c];
+    }
+#pragma unroll
+    for (int q = 0; q < kCholNb * kCholNb / 256; ++q) {
+        const int x = tid + 256 * q, row = x / kCholNb, c = x % kCholNb;
+        li[row][c] = vi[q];
+        lk[row][c] = vk[q];
     }
     __syncthreads();
     const int a0 = (tid >> 4) * 4, b0 = (tid & 15) * 4;
+    // This thread's 16 entries of G, loaded before the products (all inside
+    // the matrix; the triangle test applies to the write-back only).
+    double gv[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) gv[a][b] = g[(int64_t)(r0 + a0 + a) * r + k0 + b0 + b];
     double sacc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -565,7 +602,7 @@ __global__ __launch_bounds__(256) void xkv_chol_update_kernel(double* g, int r, 
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int i = r0 + a0 + a, k = k0 + b0 + b;
-            if (k <= i) g[(int64_t)i * r + k] -= sacc[a][b];
+            if (k <= i) g[(int64_t)i * r + k] = gv[a][b] - sacc[a][b];
         }
 }
 
