@@ -632,9 +632,28 @@ __global__ __launch_bounds__(256) void xkv_trsm_kernel(const double* y, double* 
     dead += q * r;
     x += q * nrows * r;
     if (y) y += q * nrows * r;
-    for (int e = tid; e < kTrRows * r; e += 256) {
-        const int i = e / r, j = e % r;
-        xs[i][j] = r0 + i >= nrows ? 0.0 : (y ? y[(int64_t)(r0 + i) * r + j] : (r0 + i == j ? 1.0 : 0.0));
+    const int n_x = kTrRows * r;
+    if (y) {
+        // Eight loads per thread in flight before its LDS stores; rows past
+        // the end read the last row and store zero.
+        for (int e0 = tid; e0 < n_x; e0 += 256 * 8) {
+            double v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = min(e0 + 256 * k, n_x - 1), i = e / r, j = e % r;
+                v[k] = y[(int64_t)min(r0 + i, nrows - 1) * r + j];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = e0 + 256 * k;
+                if (e < n_x) xs[e / r][e % r] = r0 + e / r >= nrows ? 0.0 : v[k];
+            }
+        }
+    } else {
+        for (int e = tid; e < n_x; e += 256) {
+            const int i = e / r, j = e % r;
+            xs[i][j] = r0 + i < nrows && r0 + i == j ? 1.0 : 0.0;
+        }
     }
     __syncthreads();
     for (int jb = 0; jb < r; jb += 16) {
