@@ -168,6 +168,21 @@ def test_long_windows(name, act_cfg):
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
+def test_window_only_sequence(generic):
+    """Sequence 1 has every block evicted but 40 window tokens: the combine
+    has no partial record for it (and must not read a stale one) and attends
+    the window alone; sequence 0 keeps its blocks."""
+    cfg = SMALL["bf16_r1024_sel"]
+    case = make_case(cfg, layer=3)
+    nb = -(-cfg.ctx_len // 64)
+    case["keep"] = torch.ones(2, nb, dtype=torch.uint8)
+    case["keep"][1] = 0
+    case["win_len"] = 40
+    out, stats = check(case, cfg, generic=generic)
+    assert stats[1, :, 1].abs().sum().item() == 0 and (stats[1, :, 0] == 40).all()
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "auto"])
 def test_sequence_with_everything_evicted(generic):
     cfg = SMALL["i8_keep"]
     case = make_case(cfg, layer=5)
